@@ -1,0 +1,18 @@
+"""fp64 CPU oracle for paged attention: test infrastructure only.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s ``cpu_baseline`` leg may
+import this package.  It holds no C sources, so there is nothing to compile for it.
+"""
+
+from .paged_attention import (  # noqa: F401
+    allowed_mask,
+    attention_probs,
+    attention_rows,
+    copy_blocks,
+    decode,
+    gather_kv,
+    key_range,
+    kv_head_of,
+    prefill_varlen,
+    store_kv,
+)

@@ -1,0 +1,255 @@
+"""Plain, slow, fp64 CPU oracle for attention over a paged, block-structured KV cache.
+
+TEST INFRASTRUCTURE, NOT PRODUCT CODE.  Only ``tests/``, ``__graft_entry__.smoke()`` and
+the ``cpu_baseline`` leg of ``bench.py`` may import or call anything in this package.  It
+shares no code with the HIP library (``paged_attention_block_amd``) and imports nothing
+from it; both sides only consume the seeded inputs made by ``workloads``.
+
+Every function takes numpy arrays and follows the pages' statement of the problem:
+
+* Cache layout ``kv_cache[2, num_blocks, block_size, num_kv_heads, head_size]``; plane 0
+  holds keys, plane 1 values (vLLM learning book, "05. Attention Backends",
+  section 3 FlashAttentionBackend.get_kv_cache_shape; section 5 ``kv_cache.unbind(0)``).
+* Store: a token whose slot is negative is skipped; otherwise the slot splits into
+  ``block = slot // block_size`` and ``offset = slot % block_size`` (MinivLLM API docs,
+  "Attention", section store_kvcache, parameter slot_mapping and its example).
+* Block addressing: logical key ``j`` of sequence ``s`` lives in physical block
+  ``block_table[s, j // block_size]`` at offset ``j % block_size`` (vLLM learning book,
+  section 10 question 2, the slot_mapping / block_table formula; MinivLLM API docs,
+  section paged_attention_decode, parameter block_tables).
+* Mask: query row ``i`` of a sequence with ``seqlen_q`` queries and ``seqlen_k`` keys sits
+  at absolute position ``p = seqlen_k - seqlen_q + i`` (bottom-right aligned causal
+  diagonal of HF transformers continuous_batching ``input_ouputs.py``,
+  ``build_attention_mask``); it may attend keys ``j <= p`` and, with a sliding window of
+  ``W >= 1`` keys, only ``j >= p - W + 1`` (the window counts the query's own key; same
+  function, and the vllm-npu 0.4.2 diff, ``torch_sdpa.py`` ``_make_sliding_window_bias``).
+  ``W <= 0`` means no window.
+* GQA: query head ``h`` reads KV head ``h // (num_heads // num_kv_heads)`` (vllm-npu 0.4.2
+  diff, ``torch_sdpa.py`` forward, ``repeat_interleave(num_queries_per_kv, dim=1)``).
+* Attention: ``out = softmax(scale * q K^T) V`` over the allowed keys; a row with no
+  allowed key is written as zeros (vLLM learning book, section 5, the profile-run
+  ``output.fill_(0)``; the pages leave the empty row otherwise undefined).
+
+Decode is the same definition with one query per sequence and ``seqlen_k = seq_lens[s]``
+(MinivLLM API docs, section paged_attention_decode: one query, ``context_lens`` valid
+keys).  All floating-point work is fp64.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "store_kv",
+    "copy_blocks",
+    "key_range",
+    "allowed_mask",
+    "kv_head_of",
+    "gather_kv",
+    "attention_probs",
+    "attention_rows",
+    "prefill_varlen",
+    "decode",
+]
+
+
+# ----------------------------------------------------------------------------- store / copy
+
+
+def store_kv(kv_cache: np.ndarray, key: np.ndarray, value: np.ndarray,
+             slot_mapping: np.ndarray) -> np.ndarray:
+    """Return a copy of ``kv_cache`` with token ``t``'s key/value rows written to its slot.
+
+    MinivLLM API docs, "Attention", section store_kvcache: ``slot // block_size`` picks
+    the block, ``slot % block_size`` the offset, and a slot of -1 skips the token (any
+    negative slot is skipped here).  The copy is bitwise: the arrays keep their dtype.
+    ``key``/``value`` are ``[num_tokens, num_kv_heads, head_size]``.
+    """
+    out = kv_cache.copy()
+    block_size = kv_cache.shape[2]
+    for t in range(len(slot_mapping)):
+        slot = int(slot_mapping[t])
+        if slot < 0:
+            continue
+        block, offset = divmod(slot, block_size)
+        out[0, block, offset] = key[t]
+        out[1, block, offset] = value[t]
+    return out
+
+
+def copy_blocks(kv_cache: np.ndarray, block_pairs) -> np.ndarray:
+    """Return a copy of ``kv_cache`` in which block ``dst`` of both planes holds block ``src``.
+
+    vllm-npu 0.4.2 diff, ``torch_sdpa.py`` / ``xformers.py``, ``copy_blocks(kv_caches,
+    src_to_dists)`` (signature only on the pages).  Reading: every copy reads the cache
+    as it was before the call.
+    """
+    before = kv_cache.copy()
+    out = kv_cache.copy()
+    for src, dst in block_pairs:
+        out[:, int(dst)] = before[:, int(src)]
+    return out
+
+
+# ----------------------------------------------------------------------------- the mask
+
+
+def key_range(row: int, seqlen_q: int, seqlen_k: int, sliding_window: int):
+    """Inclusive key range ``(lo, hi)`` that query ``row`` may attend; empty when ``hi < lo``.
+
+    HF transformers ``input_ouputs.py``, ``build_attention_mask``: the causal diagonal is
+    offset by ``seqlen_k - seqlen_q`` so the last query sees every key; the sliding window
+    keeps the ``W`` keys ending at the query's own position.
+    """
+    p = seqlen_k - seqlen_q + row
+    hi = min(p, seqlen_k - 1)
+    lo = max(0, p - sliding_window + 1) if sliding_window > 0 else 0
+    return lo, hi
+
+
+def allowed_mask(seqlen_q: int, seqlen_k: int, sliding_window: int) -> np.ndarray:
+    """Boolean ``[seqlen_q, seqlen_k]`` matrix, True where query row ``i`` may attend key ``j``."""
+    mask = np.zeros((seqlen_q, seqlen_k), dtype=bool)
+    for i in range(seqlen_q):
+        lo, hi = key_range(i, seqlen_q, seqlen_k, sliding_window)
+        if hi >= lo:
+            mask[i, lo:hi + 1] = True
+    return mask
+
+
+# ----------------------------------------------------------------------------- attention
+
+
+def kv_head_of(head: int, num_heads: int, num_kv_heads: int) -> int:
+    """KV head read by query head ``head``: consecutive query heads share one KV head
+    (vllm-npu 0.4.2 diff, ``torch_sdpa.py`` forward, ``repeat_interleave`` on dim 1)."""
+    return head // (num_heads // num_kv_heads)
+
+
+def gather_kv(kv_cache: np.ndarray, table_row: np.ndarray, positions, kv_head: int):
+    """Key and value rows (fp64, ``[len(positions), head_size]``) of logical keys ``positions``.
+
+    vLLM learning book, section 10 question 2: physical block ``table_row[j // block_size]``,
+    offset ``j % block_size``.
+    """
+    block_size = kv_cache.shape[2]
+    n = len(positions)
+    head_size = kv_cache.shape[4]
+    k = np.empty((n, head_size), dtype=np.float64)
+    v = np.empty((n, head_size), dtype=np.float64)
+    for r, j in enumerate(positions):
+        block = int(table_row[j // block_size])
+        offset = j % block_size
+        k[r] = kv_cache[0, block, offset, kv_head]
+        v[r] = kv_cache[1, block, offset, kv_head]
+    return k, v
+
+
+def _locate(cu_seqlens_q: np.ndarray, token: int) -> int:
+    """Sequence that owns packed query ``token`` (zero-length sequences own nothing)."""
+    s = int(np.searchsorted(cu_seqlens_q, token, side="right")) - 1
+    assert cu_seqlens_q[s] <= token < cu_seqlens_q[s + 1]
+    return s
+
+
+def attention_probs(query, kv_cache, block_table, cu_seqlens_q, cu_seqlens_k, scale,
+                    num_kv_heads, sliding_window, token, head):
+    """Softmax weights of packed query ``token``, head ``head`` over keys ``[0, seqlen_k)``.
+
+    Masked keys get weight exactly 0.  Returns ``(probs, seq)``; ``probs`` is all zeros
+    for a row with no allowed key.
+    """
+    s = _locate(cu_seqlens_q, token)
+    seqlen_q = int(cu_seqlens_q[s + 1] - cu_seqlens_q[s])
+    seqlen_k = int(cu_seqlens_k[s + 1] - cu_seqlens_k[s])
+    row = token - int(cu_seqlens_q[s])
+    g = kv_head_of(head, query.shape[1], num_kv_heads)
+    probs = np.zeros(seqlen_k, dtype=np.float64)
+    lo, hi = key_range(row, seqlen_q, seqlen_k, sliding_window)
+    if hi < lo:
+        return probs, s
+    k, _ = gather_kv(kv_cache, block_table[s], range(lo, hi + 1), g)
+    z = float(scale) * (k @ np.asarray(query[token, head], dtype=np.float64))
+    w = np.exp(z - z.max())
+    probs[lo:hi + 1] = w / w.sum()
+    return probs, s
+
+
+def attention_rows(query, kv_cache, block_table, cu_seqlens_q, cu_seqlens_k, scale,
+                   num_kv_heads, sliding_window, picks) -> np.ndarray:
+    """Output rows ``out[token, head, :]`` (fp64) for each ``(token, head)`` in ``picks``.
+
+    The definition, one row at a time: softmax weights from ``attention_probs`` times the
+    value rows gathered through the block table.  Used at sizes where computing every
+    row would take too long.
+    """
+    rows = []
+    num_heads = query.shape[1]
+    for token, head in picks:
+        probs, s = attention_probs(query, kv_cache, block_table, cu_seqlens_q, cu_seqlens_k,
+                                   scale, num_kv_heads, sliding_window, int(token), int(head))
+        nz = np.nonzero(probs)[0]
+        if len(nz) == 0:
+            rows.append(np.zeros(query.shape[2], dtype=np.float64))
+            continue
+        lo, hi = int(nz.min()), int(nz.max())
+        g = kv_head_of(int(head), num_heads, num_kv_heads)
+        _, v = gather_kv(kv_cache, block_table[s], range(lo, hi + 1), g)
+        rows.append(probs[lo:hi + 1] @ v)
+    return np.stack(rows) if rows else np.zeros((0, query.shape[2]))
+
+
+def prefill_varlen(query, kv_cache, block_table, cu_seqlens_q, cu_seqlens_k, scale,
+                   num_kv_heads, sliding_window=0) -> np.ndarray:
+    """Every output row of varlen paged attention, ``[total_q, num_heads, head_size]`` fp64.
+
+    Same definition as ``attention_rows``, evaluated per (sequence, KV head) over the
+    union of the rows' key ranges with the element mask of ``allowed_mask``: only
+    numpy's summation order differs.  Covers prefill (``seqlen_q == seqlen_k``) and
+    chunked prefill (``seqlen_q < seqlen_k``, MinivLLM API docs, section
+    flash_attention_prefill; HF ``build_attention_mask``).
+    """
+    q = np.asarray(query, dtype=np.float64)
+    total_q, num_heads, head_size = q.shape
+    out = np.zeros((total_q, num_heads, head_size), dtype=np.float64)
+    num_seqs = len(cu_seqlens_q) - 1
+    for s in range(num_seqs):
+        q0 = int(cu_seqlens_q[s])
+        seqlen_q = int(cu_seqlens_q[s + 1]) - q0
+        seqlen_k = int(cu_seqlens_k[s + 1] - cu_seqlens_k[s])
+        if seqlen_q <= 0 or seqlen_k <= 0:
+            continue
+        mask = allowed_mask(seqlen_q, seqlen_k, sliding_window)
+        cols = np.nonzero(mask.any(axis=0))[0]
+        if len(cols) == 0:
+            continue
+        lo, hi = int(cols.min()), int(cols.max())
+        mask = mask[:, lo:hi + 1]
+        live_rows = mask.any(axis=1)
+        for g in range(num_kv_heads):
+            k, v = gather_kv(kv_cache, block_table[s], range(lo, hi + 1), g)
+            heads = [h for h in range(num_heads) if kv_head_of(h, num_heads, num_kv_heads) == g]
+            qg = q[q0:q0 + seqlen_q, heads, :].transpose(1, 0, 2)   # [group, seqlen_q, D]
+            z = float(scale) * (qg @ k.T)                           # [group, seqlen_q, n]
+            z = np.where(mask[None], z, -np.inf)
+            zmax = np.where(live_rows[None, :, None], z.max(axis=2, keepdims=True), 0.0)
+            w = np.where(mask[None], np.exp(z - zmax), 0.0)
+            denom = w.sum(axis=2, keepdims=True)
+            p = np.divide(w, denom, out=np.zeros_like(w), where=denom > 0)
+            out[q0:q0 + seqlen_q, heads, :] = (p @ v).transpose(1, 0, 2)
+    return out
+
+
+def decode(query, kv_cache, block_table, seq_lens, scale, num_kv_heads,
+           sliding_window=0) -> np.ndarray:
+    """Paged decode, ``[num_seqs, num_heads, head_size]`` fp64: one query per sequence.
+
+    MinivLLM API docs, section paged_attention_decode: sequence ``s`` attends its
+    ``seq_lens[s]`` cached keys; this is ``prefill_varlen`` with ``seqlen_q = 1``, so the
+    sliding window applies to the single query too.
+    """
+    seq_lens = np.asarray(seq_lens, dtype=np.int64)
+    cu_q = np.arange(len(seq_lens) + 1, dtype=np.int64)
+    cu_k = np.concatenate([[0], np.cumsum(seq_lens)])
+    return prefill_varlen(query, kv_cache, block_table, cu_q, cu_k, scale, num_kv_heads,
+                          sliding_window)

@@ -1,0 +1,98 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that the pins catch each.
+
+Every mutation replaces one oracle helper for the duration of a test; the pins from
+``test_oracle.py`` are then run and at least one of them must fail.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle.paged_attention as pa
+from tests import test_oracle as pins
+
+PIN_FUNCS = [
+    lambda gd: pins.test_mask_worked_examples(gd, "mask_sk8_sq4_w6.txt"),
+    lambda gd: pins.test_mask_worked_examples(gd, "mask_sk5_sq3_w2.txt"),
+    lambda gd: pins.test_matches_dense_sdpa_on_contiguous_kv(4, 2, 3),
+    lambda gd: pins.test_matches_dense_sdpa_on_contiguous_kv(6, 2, 0),
+    lambda gd: pins.test_square_causal_matches_sdpa_is_causal(),
+    lambda gd: pins.test_closed_forms(),
+    lambda gd: pins.test_chunked_prefill_equals_one_shot(),
+    lambda gd: pins.test_decode_equals_last_row_of_prefill(),
+    lambda gd: pins.test_block_size_invariance(),
+    lambda gd: pins.test_gqa_equals_explicitly_duplicated_kv_heads(),
+    lambda gd: pins.test_store_worked_example(gd),
+]
+
+
+def _window_off_by_one(row, sq, sk, w):
+    p = sk - sq + row
+    return (max(0, p - w) if w > 0 else 0), min(p, sk - 1)
+
+
+def _causal_exclusive(row, sq, sk, w):
+    p = sk - sq + row
+    return (max(0, p - w + 1) if w > 0 else 0), min(p - 1, sk - 1)
+
+
+def _top_left_aligned(row, sq, sk, w):
+    p = row
+    return (max(0, p - w + 1) if w > 0 else 0), min(p, sk - 1)
+
+
+def _gqa_modulo(head, num_heads, num_kv_heads):
+    return head % num_kv_heads
+
+
+def _gather_swapped_planes(kv_cache, table_row, positions, kv_head):
+    k, v = _orig_gather(kv_cache, table_row, positions, kv_head)
+    return v, k
+
+
+def _gather_wrong_offset(kv_cache, table_row, positions, kv_head):
+    bs = kv_cache.shape[2]
+    k = np.stack([kv_cache[0, int(table_row[j // bs]), (bs - 1 - j % bs), kv_head] for j in positions])
+    v = np.stack([kv_cache[1, int(table_row[j // bs]), (bs - 1 - j % bs), kv_head] for j in positions])
+    return k.astype(np.float64), v.astype(np.float64)
+
+
+def _store_offset_swapped(kv_cache, key, value, slot_mapping):
+    out = kv_cache.copy()
+    bs = kv_cache.shape[2]
+    for t, slot in enumerate(slot_mapping):
+        if slot < 0:
+            continue
+        out[0, slot % bs, slot // bs] = key[t]
+        out[1, slot % bs, slot // bs] = value[t]
+    return out
+
+
+_orig_gather = pa.gather_kv
+
+MUTATIONS = {
+    "window_off_by_one": ("key_range", _window_off_by_one),
+    "causal_excludes_self": ("key_range", _causal_exclusive),
+    "top_left_alignment": ("key_range", _top_left_aligned),
+    "gqa_modulo_mapping": ("kv_head_of", _gqa_modulo),
+    "k_v_planes_swapped": ("gather_kv", _gather_swapped_planes),
+    "block_offset_reversed": ("gather_kv", _gather_wrong_offset),
+    "store_block_offset_swapped": ("store_kv", _store_offset_swapped),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_pins_catch_planted_mistake(name, monkeypatch, golden_dir):
+    attr, fn = MUTATIONS[name]
+    monkeypatch.setattr(pa, attr, fn)
+    import oracle
+    if hasattr(oracle, attr):
+        monkeypatch.setattr(oracle, attr, fn)
+    failures = 0
+    for pin in PIN_FUNCS:
+        try:
+            pin(golden_dir)
+        except (AssertionError, IndexError, ValueError):
+            failures += 1
+    assert failures > 0, f"no pin caught mutation {name}"
