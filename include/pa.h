@@ -1,0 +1,171 @@
+/*
+ * pa.h — C ABI of the paged-attention library (libpa.so) for AMD Instinct MI355X (gfx950).
+ *
+ * Three operations on a paged, block-structured KV cache, plus block copies:
+ *   pa_store_kv        scatter new keys/values into cache slots (slot_mapping)
+ *   pa_copy_blocks     duplicate physical blocks of both cache planes
+ *   pa_prefill_varlen  varlen causal attention (chunked, optional sliding window)
+ *   pa_decode          grouped-query decode, one query per sequence, split-K
+ *
+ * Conventions shared by every entry point
+ *   - All tensor arguments are DEVICE pointers, caller-allocated and caller-owned; the
+ *     library never allocates, frees or keeps them.  Index arrays are int32.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Calls only
+ *     enqueue work on it and never synchronise; the result is ready when the stream is.
+ *   - Scalars are checked on the host before any HIP call; a failed check returns a
+ *     non-zero pa_status and pa_last_error() names the argument.  Device contents (slot
+ *     values, table entries, lengths) are preconditions that are not checked.
+ *   - Zero work (no tokens, no sequences, zero-length sequences) is PA_OK and a no-op.
+ *
+ * Cache layout (vLLM learning book, "05. Attention Backends", section 3, FlashAttention
+ * backend get_kv_cache_shape): one contiguous buffer
+ *     kv_cache[2][num_blocks][block_size][num_kv_heads][head_size]
+ * plane 0 holds keys, plane 1 values; element (p, b, o, g, d) is at linear index
+ * (((p*num_blocks + b)*block_size + o)*num_kv_heads + g)*head_size + d.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+    PA_OK = 0,
+    PA_ERR_INVALID_ARG = 1,   /* null pointer with work to do, bad size or count        */
+    PA_ERR_UNSUPPORTED = 2,   /* head size, block size, dtype or group size not built     */
+    PA_ERR_WORKSPACE = 3,     /* decode workspace missing or smaller than required        */
+    PA_ERR_LAUNCH = 4         /* the HIP runtime reported an error at launch              */
+} pa_status;
+
+typedef enum pa_dtype {
+    PA_F32 = 0,               /* float32 cache, q/k/v and output                          */
+    PA_BF16 = 1               /* bfloat16 cache, q/k/v and output; fp32 accumulation      */
+} pa_dtype;
+
+/* Description of the caller's cache.  head_size in {64, 128}; block_size a power of two in
+ * [1, 256] for PA_F32 and in [16, 256] for PA_BF16; num_blocks*block_size < 2^31. */
+typedef struct pa_cache_desc {
+    void*   kv_cache;
+    int32_t num_blocks;
+    int32_t block_size;
+    int32_t num_kv_heads;
+    int32_t head_size;
+    int32_t dtype;            /* a pa_dtype value */
+} pa_cache_desc;
+
+/*
+ * pa_store_kv — write token t's key and value rows into its cache slot.
+ *
+ * MinivLLM API docs, "Attention" page, section store_kvcache (and its example); vLLM
+ * learning book, section 10 question 2: slot = physical_block * block_size + offset, so
+ * cache[0][slot / block_size][slot % block_size][:][:] = key[t] and plane 1 = value[t].
+ * A negative slot (-1 padding) skips the token.  The copy is bitwise.
+ *
+ *   key, value    [num_tokens][num_kv_heads][head_size], contiguous, cache dtype
+ *   slot_mapping  [num_tokens] int32
+ * Preconditions: every non-negative slot < num_blocks*block_size and no slot repeats
+ * (a repeated slot is a write race).
+ */
+int pa_store_kv(const pa_cache_desc* cache, const void* key, const void* value,
+                const int32_t* slot_mapping, int32_t num_tokens, void* stream);
+
+/*
+ * pa_copy_blocks — for each pair (src, dst): cache[:, dst] = cache[:, src], both planes.
+ *
+ * vllm-npu 0.4.2 diff, torch_sdpa.py / xformers.py backend, copy_blocks(kv_caches,
+ * src_to_dists) (copy-on-write forks; the pages give the signature only).
+ *   block_pairs  [num_pairs][2] int32 (src, dst)
+ * Preconditions: ids in [0, num_blocks); dst values unique and not among the src values,
+ * so every copy reads the pre-call contents.
+ */
+int pa_copy_blocks(const pa_cache_desc* cache, const int32_t* block_pairs, int32_t num_pairs,
+                   void* stream);
+
+/*
+ * pa_prefill_varlen — attention for packed query chunks over keys already in the cache.
+ *
+ * MinivLLM API docs, section flash_attention_prefill (packed varlen queries, cu_seqlens,
+ * online softmax, GQA); HF transformers continuous_batching input_ouputs.py,
+ * build_attention_mask (bottom-right causal diagonal when seqlen_q < seqlen_k, sliding
+ * window); vLLM learning book section 5 (varlen call with block_table).
+ *
+ * Sequence s owns query rows [cu_seqlens_q[s], cu_seqlens_q[s+1]) and has
+ * seqlen_k = cu_seqlens_k[s+1] - cu_seqlens_k[s] keys, logical key j at
+ * block_table[s*max_blocks_per_seq + j/block_size], offset j % block_size.  Row i sits at
+ * position p = seqlen_k - seqlen_q + i and attends keys j in [lo, p] with
+ * lo = max(0, p - sliding_window + 1) when sliding_window > 0, else 0.  Query head h reads
+ * KV head h / (num_heads / num_kv_heads).  out = softmax(scale * q.K^T) V per row and head;
+ * a row with no key (p < 0) is written as zeros.
+ *
+ *   out, query    [cu_seqlens_q[num_seqs]][num_heads][head_size], contiguous, cache dtype
+ *   block_table   [num_seqs][max_blocks_per_seq] int32 (entries outside a sequence's live
+ *                 key range are never read and may be -1)
+ *   cu_seqlens_q, cu_seqlens_k  [num_seqs + 1] int32, non-decreasing, starting at 0
+ *   max_seqlen_q  >= every seqlen_q (sizes the grid); max_seqlen_k >= every seqlen_k
+ *   scale         final multiplier of q.K^T (e.g. 1/sqrt(head_size))
+ * Keys must already be stored (pa_store_kv first).  The K/V tiles are read only inside
+ * each row's live range, so cache slots outside it may hold anything, NaN included.
+ */
+int pa_prefill_varlen(const pa_cache_desc* cache, void* out, const void* query,
+                      const int32_t* block_table, int32_t max_blocks_per_seq,
+                      const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                      int32_t num_seqs, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                      int32_t num_heads, float scale, int32_t sliding_window, void* stream);
+
+/*
+ * pa_decode_partition_size — the split-K partition (keys per work item) pa_decode uses for
+ * these sizes when called with partition_size = 0.  Always a multiple of 64.
+ */
+int32_t pa_decode_partition_size(const pa_cache_desc* cache, int32_t num_seqs,
+                                 int32_t num_heads, int32_t max_seq_len,
+                                 int32_t sliding_window);
+
+/*
+ * pa_decode_workspace_size — bytes of device workspace pa_decode needs (0 when every
+ * sequence fits one partition).  partition_size 0 = the automatic choice.
+ */
+size_t pa_decode_workspace_size(const pa_cache_desc* cache, int32_t num_seqs,
+                                int32_t num_heads, int32_t max_seq_len,
+                                int32_t sliding_window, int32_t partition_size);
+
+/*
+ * pa_decode — one query token per sequence over its cached keys (split-K + merge).
+ *
+ * MinivLLM API docs, section paged_attention_decode (query [batch][heads][dim],
+ * block_tables, context_lens valid keys per sequence); vLLM learning book section 7
+ * (split-KV for long-context decode).  Sequence s attends keys [lo, n) with
+ * n = seq_lens[s] (the keys stored so far, the new token's included) and
+ * lo = max(0, n - sliding_window) when sliding_window > 0, else 0: the seqlen_q = 1 case
+ * of pa_prefill_varlen.  The key range is cut into partitions of partition_size keys
+ * (0 = automatic; otherwise a multiple of 64), each reduced to a partial softmax state in
+ * the workspace and merged with a log-sum-exp rescale.
+ *
+ *   out, query   [num_seqs][num_heads][head_size], contiguous, cache dtype
+ *   block_table  [num_seqs][max_blocks_per_seq] int32
+ *   seq_lens     [num_seqs] int32, each in [0, max_seq_len]
+ *   workspace    device buffer of >= pa_decode_workspace_size(...) bytes (may be NULL when
+ *                that is 0); its contents need no initialisation
+ * A sequence with seq_lens[s] == 0 gets a zero output row.
+ */
+int pa_decode(const pa_cache_desc* cache, void* out, const void* query,
+              const int32_t* block_table, int32_t max_blocks_per_seq,
+              const int32_t* seq_lens, int32_t num_seqs, int32_t max_seq_len,
+              int32_t num_heads, float scale, int32_t sliding_window,
+              int32_t partition_size, void* workspace, size_t workspace_bytes,
+              void* stream);
+
+/* Fixed text for a status code. */
+const char* pa_status_string(int status);
+
+/* Detail of the most recent non-OK return on the calling thread ("" if none). */
+const char* pa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

@@ -1,0 +1,258 @@
+// C ABI of libpa: host-side argument checks, launch planning and dispatch.
+//
+// Every scalar is validated before the first HIP call, so a rejected call touches no
+// device state.  The library never allocates memory and never synchronises: calls only
+// enqueue kernels on the caller's stream.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/pa.h"
+#include "pa_internal.hpp"
+
+namespace pa {
+hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);
+hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s);
+hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t s);
+}  // namespace pa
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+bool is_pow2(int32_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int log2i(int32_t x) {
+    int r = 0;
+    while ((1 << r) < x) ++r;
+    return r;
+}
+
+// Checks the cache description; fills `c`.
+int check_cache(const pa_cache_desc* d, pa::CacheArgs* c) {
+    if (!d) return fail(PA_ERR_INVALID_ARG, "cache descriptor is NULL");
+    if (!d->kv_cache) return fail(PA_ERR_INVALID_ARG, "kv_cache is NULL");
+    if (d->num_blocks <= 0) return fail(PA_ERR_INVALID_ARG, "num_blocks must be > 0 (got %d)", d->num_blocks);
+    if (d->num_kv_heads <= 0) return fail(PA_ERR_INVALID_ARG, "num_kv_heads must be > 0 (got %d)", d->num_kv_heads);
+    if (d->dtype != PA_F32 && d->dtype != PA_BF16) return fail(PA_ERR_UNSUPPORTED, "dtype %d not supported", d->dtype);
+    if (d->head_size != 64 && d->head_size != 128)
+        return fail(PA_ERR_UNSUPPORTED, "head_size %d not supported (64 or 128)", d->head_size);
+    if (!is_pow2(d->block_size) || d->block_size > 256)
+        return fail(PA_ERR_UNSUPPORTED, "block_size %d must be a power of two <= 256", d->block_size);
+    if ((int64_t)d->num_blocks * d->block_size >= (int64_t(1) << 31))
+        return fail(PA_ERR_INVALID_ARG, "num_blocks * block_size must be < 2^31");
+    if ((int64_t)d->num_kv_heads * d->head_size > (int64_t(1) << 20))
+        return fail(PA_ERR_INVALID_ARG, "num_kv_heads * head_size too large");
+    c->kv = d->kv_cache;
+    c->num_blocks = d->num_blocks;
+    c->block_size = d->block_size;
+    c->block_shift = log2i(d->block_size);
+    c->num_kv_heads = d->num_kv_heads;
+    c->head_size = d->head_size;
+    c->dtype = d->dtype;
+    c->plane_elems = (int64_t)d->num_blocks * d->block_size * d->num_kv_heads * d->head_size;
+    return PA_OK;
+}
+
+int check_heads(const pa::CacheArgs& c, int32_t num_heads) {
+    if (num_heads <= 0) return fail(PA_ERR_INVALID_ARG, "num_heads must be > 0 (got %d)", num_heads);
+    if (num_heads % c.num_kv_heads != 0)
+        return fail(PA_ERR_INVALID_ARG, "num_heads %d is not a multiple of num_kv_heads %d", num_heads,
+                    c.num_kv_heads);
+    const int group = num_heads / c.num_kv_heads;
+    if (c.dtype == PA_BF16 && group > 16)
+        return fail(PA_ERR_UNSUPPORTED, "bf16 decode supports up to 16 query heads per KV head (got %d)", group);
+    if (c.dtype == PA_BF16 && c.block_size < 16)
+        return fail(PA_ERR_UNSUPPORTED, "bf16 kernels need block_size >= 16 (got %d)", c.block_size);
+    if (num_heads > 65535) return fail(PA_ERR_INVALID_ARG, "num_heads too large");
+    return PA_OK;
+}
+
+int launch_status(hipError_t e) {
+    if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "HIP launch failed: %s", hipGetErrorString(e));
+    g_last_error[0] = 0;
+    return PA_OK;
+}
+
+// Split-K partition size: aim for ~8 work items per SIMD (4 per CU x 256 CUs x 8) with at
+// least 128 keys per item, and keep the partial states small against the KV bytes.
+int32_t auto_part(int32_t num_seqs, int32_t num_kv_heads, int32_t max_keys) {
+    const int64_t items_target = 8192;
+    const int64_t total = (int64_t)num_seqs * num_kv_heads * max_keys;
+    int64_t part = 128;
+    while (part < 8192 && total / part > items_target) part *= 2;
+    return (int32_t)part;
+}
+
+// Largest key span a partitioned sequence covers: its live keys [lo, n) plus the < 32 keys
+// between lo and the 32-aligned start of its first partition.
+int32_t max_keys_of(int32_t max_seq_len, int32_t window) {
+    if (window > 0 && max_seq_len > window) return max_seq_len < window + 31 ? max_seq_len : window + 31;
+    return max_seq_len;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_string(int status) {
+    switch (status) {
+        case PA_OK: return "ok";
+        case PA_ERR_INVALID_ARG: return "invalid argument";
+        case PA_ERR_UNSUPPORTED: return "unsupported configuration";
+        case PA_ERR_WORKSPACE: return "workspace too small";
+        case PA_ERR_LAUNCH: return "kernel launch failed";
+        default: return "unknown status";
+    }
+}
+
+const char* pa_last_error(void) { return g_last_error; }
+
+int pa_store_kv(const pa_cache_desc* cache, const void* key, const void* value,
+                const int32_t* slot_mapping, int32_t num_tokens, void* stream) {
+    pa::StoreArgs a;
+    int st = check_cache(cache, &a.c);
+    if (st) return st;
+    if (num_tokens < 0) return fail(PA_ERR_INVALID_ARG, "num_tokens must be >= 0 (got %d)", num_tokens);
+    if (num_tokens == 0) { g_last_error[0] = 0; return PA_OK; }
+    if (!key || !value || !slot_mapping) return fail(PA_ERR_INVALID_ARG, "key, value and slot_mapping must be non-NULL");
+    a.key = key;
+    a.value = value;
+    a.slots = slot_mapping;
+    a.num_tokens = num_tokens;
+    return launch_status(pa::launch_store(a, (hipStream_t)stream));
+}
+
+int pa_copy_blocks(const pa_cache_desc* cache, const int32_t* block_pairs, int32_t num_pairs,
+                   void* stream) {
+    pa::CopyArgs a;
+    int st = check_cache(cache, &a.c);
+    if (st) return st;
+    if (num_pairs < 0 || num_pairs > (1 << 29)) return fail(PA_ERR_INVALID_ARG, "num_pairs out of range (got %d)", num_pairs);
+    if (num_pairs == 0) { g_last_error[0] = 0; return PA_OK; }
+    if (!block_pairs) return fail(PA_ERR_INVALID_ARG, "block_pairs is NULL");
+    a.pairs = block_pairs;
+    a.num_pairs = num_pairs;
+    return launch_status(pa::launch_copy_blocks(a, (hipStream_t)stream));
+}
+
+int pa_prefill_varlen(const pa_cache_desc* cache, void* out, const void* query,
+                      const int32_t* block_table, int32_t max_blocks_per_seq,
+                      const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                      int32_t num_seqs, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                      int32_t num_heads, float scale, int32_t sliding_window, void* stream) {
+    pa::PrefillArgs a;
+    int st = check_cache(cache, &a.c);
+    if (st) return st;
+    if ((st = check_heads(a.c, num_heads))) return st;
+    if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs must be >= 0 (got %d)", num_seqs);
+    if (max_seqlen_q < 0 || max_seqlen_k < 0) return fail(PA_ERR_INVALID_ARG, "max_seqlen_q/k must be >= 0");
+    if (num_seqs == 0 || max_seqlen_q == 0) { g_last_error[0] = 0; return PA_OK; }
+    if (!out || !query || !block_table || !cu_seqlens_q || !cu_seqlens_k)
+        return fail(PA_ERR_INVALID_ARG, "out, query, block_table, cu_seqlens_q and cu_seqlens_k must be non-NULL");
+    if (max_blocks_per_seq < 1) return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq must be >= 1");
+    if ((int64_t)max_seqlen_k > (int64_t)max_blocks_per_seq * a.c.block_size)
+        return fail(PA_ERR_INVALID_ARG, "max_seqlen_k %d exceeds max_blocks_per_seq * block_size", max_seqlen_k);
+    if (!(scale == scale)) return fail(PA_ERR_INVALID_ARG, "scale is NaN");
+    if (a.c.dtype == PA_F32 && (int64_t)num_seqs * max_seqlen_q >= (int64_t(1) << 31))
+        return fail(PA_ERR_INVALID_ARG, "num_seqs * max_seqlen_q too large");
+    if ((int64_t)num_seqs * num_heads * ((max_seqlen_q + 31) / 32) >= (int64_t(1) << 30))
+        return fail(PA_ERR_INVALID_ARG, "grid too large");
+    a.out = out;
+    a.q = query;
+    a.table = block_table;
+    a.max_blocks = max_blocks_per_seq;
+    a.cu_q = cu_seqlens_q;
+    a.cu_k = cu_seqlens_k;
+    a.num_seqs = num_seqs;
+    a.max_seqlen_q = max_seqlen_q;
+    a.num_heads = num_heads;
+    a.group = num_heads / a.c.num_kv_heads;
+    a.scale = scale;
+    a.window = sliding_window > 0 ? sliding_window : 0;
+    hipStream_t s = (hipStream_t)stream;
+    return launch_status(a.c.dtype == PA_BF16 ? pa::launch_prefill_bf16(a, s) : pa::launch_prefill_f32(a, s));
+}
+
+int32_t pa_decode_partition_size(const pa_cache_desc* cache, int32_t num_seqs, int32_t num_heads,
+                                 int32_t max_seq_len, int32_t sliding_window) {
+    (void)num_heads;
+    const int32_t hkv = (cache && cache->num_kv_heads > 0) ? cache->num_kv_heads : 1;
+    return auto_part(num_seqs > 0 ? num_seqs : 1, hkv,
+                     max_keys_of(max_seq_len > 0 ? max_seq_len : 1, sliding_window));
+}
+
+size_t pa_decode_workspace_size(const pa_cache_desc* cache, int32_t num_seqs, int32_t num_heads,
+                                int32_t max_seq_len, int32_t sliding_window, int32_t partition_size) {
+    if (!cache || num_seqs <= 0 || num_heads <= 0 || max_seq_len <= 0) return 0;
+    if (cache->dtype != PA_BF16) return 0;  // the float32 path needs no workspace
+    const int32_t part = partition_size > 0
+                             ? partition_size
+                             : pa_decode_partition_size(cache, num_seqs, num_heads, max_seq_len, sliding_window);
+    const int32_t parts = (max_keys_of(max_seq_len, sliding_window) + part - 1) / part;
+    if (parts <= 1) return 0;
+    return (size_t)num_seqs * num_heads * parts * ((size_t)cache->head_size + 2) * sizeof(float);
+}
+
+int pa_decode(const pa_cache_desc* cache, void* out, const void* query, const int32_t* block_table,
+              int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t num_seqs,
+              int32_t max_seq_len, int32_t num_heads, float scale, int32_t sliding_window,
+              int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream) {
+    pa::DecodeArgs a;
+    int st = check_cache(cache, &a.c);
+    if (st) return st;
+    if ((st = check_heads(a.c, num_heads))) return st;
+    if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs must be >= 0 (got %d)", num_seqs);
+    if (max_seq_len < 0) return fail(PA_ERR_INVALID_ARG, "max_seq_len must be >= 0");
+    if (num_seqs == 0) { g_last_error[0] = 0; return PA_OK; }
+    if (!out || !query || !block_table || !seq_lens)
+        return fail(PA_ERR_INVALID_ARG, "out, query, block_table and seq_lens must be non-NULL");
+    if (max_blocks_per_seq < 1) return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq must be >= 1");
+    if ((int64_t)max_seq_len > (int64_t)max_blocks_per_seq * a.c.block_size)
+        return fail(PA_ERR_INVALID_ARG, "max_seq_len %d exceeds max_blocks_per_seq * block_size", max_seq_len);
+    if (partition_size < 0 || partition_size % 64 != 0)
+        return fail(PA_ERR_INVALID_ARG, "partition_size must be 0 or a positive multiple of 64 (got %d)", partition_size);
+    if (!(scale == scale)) return fail(PA_ERR_INVALID_ARG, "scale is NaN");
+    if (num_seqs > 0x7fffffff / 64) return fail(PA_ERR_INVALID_ARG, "num_seqs too large");
+    a.out = out;
+    a.q = query;
+    a.table = block_table;
+    a.max_blocks = max_blocks_per_seq;
+    a.seq_lens = seq_lens;
+    a.num_seqs = num_seqs;
+    a.num_heads = num_heads;
+    a.group = num_heads / a.c.num_kv_heads;
+    a.scale = scale;
+    a.window = sliding_window > 0 ? sliding_window : 0;
+    hipStream_t s = (hipStream_t)stream;
+    if (a.c.dtype == PA_F32) {
+        a.part = 0;
+        a.max_parts = 1;
+        a.ws_o = nullptr;
+        a.ws_ml = nullptr;
+        return launch_status(pa::launch_decode_f32(a, s));
+    }
+    const int32_t mkeys = max_keys_of(max_seq_len > 0 ? max_seq_len : 1, a.window);
+    a.part = partition_size > 0 ? partition_size : auto_part(num_seqs, a.c.num_kv_heads, mkeys);
+    a.max_parts = (mkeys + a.part - 1) / a.part;
+    if (a.max_parts < 1) a.max_parts = 1;
+    if (a.max_parts > 65535) return fail(PA_ERR_INVALID_ARG, "too many partitions; raise partition_size");
+    if (a.c.num_kv_heads > 65535) return fail(PA_ERR_INVALID_ARG, "num_kv_heads too large");
+    const size_t need = pa_decode_workspace_size(cache, num_seqs, num_heads, max_seq_len, sliding_window, a.part);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(PA_ERR_WORKSPACE, "decode needs %zu workspace bytes, got %zu", need, workspace ? workspace_bytes : 0);
+    a.ws_o = (float*)workspace;
+    a.ws_ml = need > 0 ? (float*)workspace + (size_t)num_seqs * num_heads * a.max_parts * a.c.head_size : nullptr;
+    return launch_status(pa::launch_decode_bf16(a, s));
+}
+
+}  // extern "C"

@@ -1,0 +1,121 @@
+"""C ABI on the CPU: the library loads, exports every function include/pa.h declares, and
+rejects bad arguments on the host before any HIP call (no kernel ever runs here)."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_attention_block_amd as pa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000  # never dereferenced: every call below fails validation or has zero work
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "pa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(pa.lib_path()):
+        pytest.skip("libpa.so not built")
+    return pa.load()
+
+
+def desc(nb=64, bs=16, hkv=2, d=128, dtype=1, ptr=FAKE):
+    return ctypes.byref(pa._CacheDesc(ptr, nb, bs, hkv, d, dtype))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared()
+    assert {"pa_store_kv", "pa_copy_blocks", "pa_prefill_varlen", "pa_decode"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    assert lib.pa_status_string(0) == b"ok"
+    assert b"argument" in lib.pa_status_string(1)
+    assert b"unknown" in lib.pa_status_string(99)
+
+
+def test_zero_work_is_ok_without_launch(lib):
+    assert lib.pa_store_kv(desc(), None, None, None, 0, None) == 0
+    assert lib.pa_copy_blocks(desc(), None, 0, None) == 0
+    assert lib.pa_prefill_varlen(desc(), None, None, None, 1, None, None, 0, 0, 0, 8, 1.0, 0, None) == 0
+    assert lib.pa_decode(desc(), None, None, None, 1, None, 0, 0, 8, 1.0, 0, 0, None, 0, None) == 0
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(d=96), 2, b"head_size"),
+    (dict(bs=12), 2, b"block_size"),
+    (dict(bs=512), 2, b"block_size"),
+    (dict(dtype=7), 2, b"dtype"),
+    (dict(nb=0), 1, b"num_blocks"),
+    (dict(hkv=0), 1, b"num_kv_heads"),
+    (dict(ptr=0), 1, b"kv_cache"),
+    (dict(nb=1 << 28, bs=16), 1, b"2^31"),
+])
+def test_cache_descriptor_checks(lib, kw, status, needle):
+    assert lib.pa_store_kv(desc(**kw), FAKE, FAKE, FAKE, 4, None) == status
+    assert needle in lib.pa_last_error()
+
+
+def test_null_cache_descriptor(lib):
+    assert lib.pa_store_kv(None, FAKE, FAKE, FAKE, 4, None) == 1
+
+
+def test_store_and_copy_argument_checks(lib):
+    assert lib.pa_store_kv(desc(), None, FAKE, FAKE, 4, None) == 1
+    assert lib.pa_store_kv(desc(), FAKE, FAKE, FAKE, -1, None) == 1
+    assert lib.pa_copy_blocks(desc(), None, 3, None) == 1
+    assert lib.pa_copy_blocks(desc(), FAKE, -2, None) == 1
+
+
+def test_prefill_argument_checks(lib):
+    args = lambda **k: dict(dict(out=FAKE, q=FAKE, tab=FAKE, mb=4, cuq=FAKE, cuk=FAKE, b=2, msq=10, msk=60, h=8,  # noqa: E731
+                                  scale=0.1, w=0), **k)
+
+    def call(d=None, **k):
+        a = args(**k)
+        return lib.pa_prefill_varlen(d or desc(), a["out"], a["q"], a["tab"], a["mb"], a["cuq"], a["cuk"],
+                                     a["b"], a["msq"], a["msk"], a["h"], a["scale"], a["w"], None)
+    assert call(h=7) == 1 and b"multiple" in lib.pa_last_error()
+    assert call(h=0) == 1
+    assert call(h=2 * 17) == 2 and b"16" in lib.pa_last_error()          # group 17 > 16 for bf16
+    assert call(out=None) == 1
+    assert call(mb=0) == 1
+    assert call(msk=65) == 1 and b"max_blocks_per_seq" in lib.pa_last_error()
+    assert call(scale=float("nan")) == 1
+    assert call(d=desc(bs=8)) == 2                                      # bf16 needs block_size >= 16
+    assert call(b=-1) == 1
+
+
+def test_decode_argument_and_workspace_checks(lib):
+    d = desc(nb=1000, bs=16, hkv=8, d=128)
+    need = lib.pa_decode_workspace_size(d, 64, 32, 4097, 0, 128)
+    parts = -(-4097 // 128)
+    assert need == 64 * 32 * parts * (128 + 2) * 4
+    # too small a workspace is rejected before any launch
+    assert lib.pa_decode(d, FAKE, FAKE, FAKE, 300, FAKE, 64, 4097, 32, 0.1, 0, 128, FAKE, need - 1, None) == 3
+    assert lib.pa_decode(d, FAKE, FAKE, FAKE, 300, FAKE, 64, 4097, 32, 0.1, 0, 128, None, need, None) == 3
+    assert lib.pa_decode(d, FAKE, FAKE, FAKE, 300, FAKE, 64, 4097, 32, 0.1, 0, 96, FAKE, need, None) == 1
+    assert lib.pa_decode(d, FAKE, FAKE, FAKE, 200, FAKE, 64, 4097, 32, 0.1, 0, 128, FAKE, need, None) == 1
+    assert lib.pa_decode(d, None, FAKE, FAKE, 300, FAKE, 64, 4097, 32, 0.1, 0, 128, FAKE, need, None) == 1
+    # one partition: no workspace needed; float32 never needs one
+    assert lib.pa_decode_workspace_size(d, 64, 32, 100, 0, 128) == 0
+    assert lib.pa_decode_workspace_size(desc(dtype=0), 64, 32, 4097, 0, 128) == 0
+    # a window bounds the key span
+    assert lib.pa_decode_workspace_size(d, 8, 40, 33281, 4096, 128) == 8 * 40 * (-(-(4096 + 31) // 128)) * 130 * 4
+
+
+def test_auto_partition_is_multiple_of_64(lib):
+    for b, n in ((1, 100), (64, 4097), (8, 33281), (252, 8193), (1024, 100000)):
+        p = lib.pa_decode_partition_size(desc(hkv=8), b, 32, n, 0)
+        assert p >= 128 and p % 64 == 0
