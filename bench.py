@@ -1,0 +1,355 @@
+"""Benchmark of the paged-attention hot path on one MI355X.
+
+Default run (one JSON line on stdout):
+  * headline, ``value``: GQA paged decode, B 64, contexts U[512, 4096], H 32 / Hkv 8,
+    D 128, block 16, bf16.  One step = store the 64 new tokens through slot_mapping, then
+    decode.  ``value`` = algorithmic bytes of the step / wall time of the step (GB/s).
+  * ``prefill``: varlen causal prefill, 16 prompts of U[128, 2048] tokens, same heads;
+    one step = store every prompt token, then prefill.  TFLOP/s of algorithmic FLOPs.
+  * ``roofline`` per op: algorithmic bytes (decode) or FLOPs (prefill) of one launch over
+    its mean duration, timed with HIP events on the stream the library launches on.
+  * ``cpu_baseline``: the fp64 numpy oracle on the host, on a bounded sample of the same
+    workload, in the same unit.
+
+Algorithmic work (not the work the kernels actually do):
+  decode bytes  = sum_s keys(s) * Hkv * D * 2 (K and V) * 2 B + q + out + 4 B per block-table
+                  entry read and per seq_len
+  prefill FLOPs = sum over (query row, allowed key, head) of 4 * D
+  store bytes   = 2 * T * Hkv * D * 2 B read + the same written + 4 B per slot
+
+Usage: python bench.py [--steps K] [--warmup W] [--workload decode|prefill|chunked|mixed]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CU x 4096 FLOP/clk x 2.4 GHz)
+METRIC = "paged decode HBM GB/s (% peak); varlen prefill bf16 TFLOP/s (% MFMA peak)"
+
+WORKLOAD_CONFIG = {"decode": 2, "prefill": 3, "chunked": 4, "mixed": 5}
+
+
+# ----------------------------------------------------------------------------- algorithmic work
+
+
+def key_span(sq, sk, i, window):
+    p = sk - sq + i
+    hi = min(p, sk - 1)
+    lo = max(0, p - window + 1) if window > 0 else 0
+    return lo, hi
+
+
+def decode_bytes(op, wl) -> float:
+    import numpy as np
+    elt = 2 if wl.dtype.itemsize == 2 else 4
+    row = wl.num_kv_heads * wl.head_size * elt
+    total = 0
+    for n in op.seq_lens.astype(np.int64):
+        lo = max(0, int(n) - wl.sliding_window) if wl.sliding_window > 0 else 0
+        keys = int(n) - lo
+        total += 2 * keys * row
+        if keys > 0:
+            total += 4 * ((int(n) - 1) // wl.block_size - lo // wl.block_size + 1)
+    b = len(op.seq_lens)
+    total += 2 * b * wl.num_heads * wl.head_size * elt + 4 * b
+    return float(total)
+
+
+def prefill_flops(op, wl) -> float:
+    import numpy as np
+    cu_q, cu_k = op.cu_seqlens_q.astype(np.int64), op.cu_seqlens_k.astype(np.int64)
+    total = 0
+    for s in range(len(cu_q) - 1):
+        sq, sk = int(cu_q[s + 1] - cu_q[s]), int(cu_k[s + 1] - cu_k[s])
+        i = np.arange(sq)
+        p = sk - sq + i
+        hi = np.minimum(p, sk - 1)
+        lo = np.maximum(0, p - wl.sliding_window + 1) if wl.sliding_window > 0 else np.zeros_like(p)
+        total += int(np.maximum(0, hi - lo + 1).sum())
+    return float(total) * wl.num_heads * 4 * wl.head_size
+
+
+def store_bytes(op, wl) -> float:
+    elt = 2 if wl.dtype.itemsize == 2 else 4
+    t = len(op.slot_mapping)
+    return float(2 * 2 * t * wl.num_kv_heads * wl.head_size * elt + 4 * t)
+
+
+def copy_bytes(op, wl) -> float:
+    elt = 2 if wl.dtype.itemsize == 2 else 4
+    return float(2 * len(op.pairs) * 2 * wl.block_size * wl.num_kv_heads * wl.head_size * elt)
+
+
+# ----------------------------------------------------------------------------- GPU timing
+
+
+class Step:
+    """Device-resident inputs of one phase and a callable that runs it."""
+
+    def __init__(self, wl, ops, dev):
+        import numpy as np
+        import torch
+        import paged_attention_block_amd as pa
+        self.pa, self.torch = pa, torch
+        self.wl, self.ops, self.dev = wl, ops, dev
+        i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)  # noqa: E731
+        self.cache = wl.kv_cache.to(dev)
+        self.prepared = []
+        for op in ops:
+            d = {"op": op}
+            name = type(op).__name__
+            if name == "CopyOp":
+                d["pairs"] = i32(op.pairs)
+            elif name == "StoreOp":
+                d.update(k=op.key.to(dev), v=op.value.to(dev), slots=i32(op.slot_mapping))
+            elif name == "PrefillOp":
+                d.update(q=op.query.to(dev), table=i32(op.block_table), cuq=i32(op.cu_seqlens_q),
+                         cuk=i32(op.cu_seqlens_k))
+                d["out"] = torch.empty_like(d["q"])
+            elif name == "DecodeOp":
+                d.update(q=op.query.to(dev), table=i32(op.block_table), lens=i32(op.seq_lens))
+                d["out"] = torch.empty_like(d["q"])
+                need = pa.pa_decode_workspace_size(self.cache, len(op.seq_lens), wl.num_heads,
+                                                   op.max_seq_len, wl.sliding_window)
+                d["ws"] = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+                d["part"] = pa.pa_decode_partition_size(self.cache, len(op.seq_lens), wl.num_heads,
+                                                        op.max_seq_len, wl.sliding_window)
+            self.prepared.append(d)
+        self.names = [type(d["op"]).__name__ for d in self.prepared]
+
+    def run_op(self, d):
+        pa, wl, op = self.pa, self.wl, d["op"]
+        name = type(op).__name__
+        if name == "CopyOp":
+            pa.pa_copy_blocks(self.cache, d["pairs"])
+        elif name == "StoreOp":
+            pa.pa_store_kv(d["k"], d["v"], self.cache, d["slots"])
+        elif name == "PrefillOp":
+            pa.pa_prefill_varlen(d["q"], self.cache, d["table"], d["cuq"], d["cuk"], op.max_seqlen_q,
+                                 op.max_seqlen_k, wl.scale, wl.num_kv_heads, wl.sliding_window, out=d["out"])
+        elif name == "DecodeOp":
+            pa.pa_decode(d["q"], self.cache, d["table"], d["lens"], op.max_seq_len, wl.scale,
+                         wl.num_kv_heads, wl.sliding_window, out=d["out"], workspace=d["ws"])
+
+    def time(self, steps: int, warmup: int):
+        """Wall time per step and mean HIP-event duration of every op over the timed steps."""
+        torch = self.torch
+        for _ in range(warmup):
+            for d in self.prepared:
+                self.run_op(d)
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream(self.dev)
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(self.prepared) + 1)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(steps):
+            evs[k][0].record(stream)
+            for i, d in enumerate(self.prepared):
+                self.run_op(d)
+                evs[k][i + 1].record(stream)
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) / steps
+        per_op = [sum(evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(steps)) / steps / 1e3
+                  for i in range(len(self.prepared))]
+        return wall, per_op
+
+
+# ----------------------------------------------------------------------------- CPU baseline
+
+
+def cpu_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        n = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+        return int(n)
+    except Exception:
+        return 1
+
+
+def cpu_baseline_decode(wl, op, budget_s: float = 20.0):
+    """Oracle decode of as many sequences as fit ~budget_s (at least 4), in GB/s."""
+    import numpy as np
+    import oracle
+    vals = wl.kv_cache.float().numpy()
+    q = op.query.float().numpy()
+    done, bytes_done, t_used = 0, 0.0, 0.0
+    b = len(op.seq_lens)
+    t_start = time.perf_counter()
+    while done < b and (t_used < budget_s or done < 4):
+        s = done
+        sub = type(op)(query=op.query[s:s + 1], block_table=op.block_table[s:s + 1],
+                       seq_lens=op.seq_lens[s:s + 1], max_seq_len=int(op.seq_lens[s]),
+                       out_rows=op.out_rows, seq_ids=[s])
+        t0 = time.perf_counter()
+        oracle.decode(q[s:s + 1], vals, op.block_table[s:s + 1], op.seq_lens[s:s + 1], wl.scale,
+                      wl.num_kv_heads, wl.sliding_window)
+        t_used += time.perf_counter() - t0
+        bytes_done += decode_bytes(sub, wl)
+        done += 1
+    del t_start
+    return {"value": round(bytes_done / t_used / 1e9, 4), "unit": "GB/s", "cores": cpu_threads(),
+            "kind": "oracle",
+            "sample": f"fp64 numpy oracle decode of the first {done} of {b} sequences "
+                      f"({bytes_done / 1e6:.1f} MB algorithmic, {t_used:.1f} s)"}
+
+
+def cpu_baseline_prefill(wl, op, budget_s: float = 20.0):
+    """Oracle prefill of whole sequences, shortest first, until ~budget_s; TFLOP/s."""
+    import numpy as np
+    import oracle
+    vals = wl.kv_cache.float().numpy()
+    q = op.query.float().numpy()
+    lens = np.diff(op.cu_seqlens_q)
+    order = np.argsort(lens)
+    flops, t_used, n = 0.0, 0.0, 0
+    for s in order:
+        if t_used >= budget_s and n >= 1:
+            break
+        a, b = int(op.cu_seqlens_q[s]), int(op.cu_seqlens_q[s + 1])
+        cu_q = np.array([0, b - a]); cu_k = np.array([0, int(op.cu_seqlens_k[s + 1] - op.cu_seqlens_k[s])])
+        t0 = time.perf_counter()
+        oracle.prefill_varlen(q[a:b], vals, op.block_table[s:s + 1], cu_q, cu_k, wl.scale,
+                              wl.num_kv_heads, wl.sliding_window)
+        t_used += time.perf_counter() - t0
+        sub = type(op)(query=op.query[a:b], block_table=op.block_table[s:s + 1], cu_seqlens_q=cu_q,
+                       cu_seqlens_k=cu_k, max_seqlen_q=b - a, max_seqlen_k=int(cu_k[1]),
+                       out_rows=op.out_rows, seq_ids=[int(s)])
+        flops += prefill_flops(sub, wl)
+        n += 1
+    return {"value": round(flops / t_used / 1e12, 6), "unit": "TFLOP/s", "cores": cpu_threads(),
+            "kind": "oracle",
+            "sample": f"fp64 numpy oracle prefill of the {n} shortest of {len(lens)} sequences "
+                      f"({flops / 1e9:.1f} GFLOP algorithmic, {t_used:.1f} s)"}
+
+
+# ----------------------------------------------------------------------------- traffic (PMC)
+
+
+def read_traffic(kernel_tag: str):
+    """HBM bytes per launch from a committed counter summary, if it still matches the source."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{kernel_tag}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    src = os.path.join(ROOT, "paged_attention_block_amd", "csrc", kv.get("source", ""))
+    if not os.path.exists(src):
+        return None
+    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    if digest != kv.get("source_sha256_16"):
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ----------------------------------------------------------------------------- main
+
+
+def roofline(achieved, peak, unit, bound, traffic=None):
+    return {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": traffic}
+
+
+def bench_workload(name, steps, warmup, dev, with_cpu):
+    import workloads as W
+    wl = W.config(WORKLOAD_CONFIG[name])
+    phase = wl.phases[-1] if name == "chunked_decode" else wl.phases[0]
+    step = Step(wl, phase, dev)
+    wall, per_op = step.time(steps, warmup)
+    ops = [d["op"] for d in step.prepared]
+    res = {"workload": W.CONFIG_NAMES[WORKLOAD_CONFIG[name]], "ms_per_step": round(wall * 1e3, 4), "ops": {}}
+    total_bytes, total_flops = 0.0, 0.0
+    for op, t in zip(ops, per_op):
+        n = type(op).__name__
+        if n == "DecodeOp":
+            b = decode_bytes(op, wl)
+            total_bytes += b
+            res["ops"]["decode"] = {"ms": round(t * 1e3, 4), "GB/s": round(b / t / 1e9, 1),
+                                    "bytes": b, "tokens_per_s": round(len(op.seq_lens) / t, 1),
+                                    "partition_size": step.prepared[ops.index(op)]["part"],
+                                    "roofline": roofline(b / t / 1e9, HBM_PEAK_GBS, "GB/s", "hbm",
+                                                         read_traffic("decode"))}
+        elif n == "PrefillOp":
+            f = prefill_flops(op, wl)
+            total_flops += f
+            res["ops"]["prefill"] = {"ms": round(t * 1e3, 4), "TFLOP/s": round(f / t / 1e12, 2), "flops": f,
+                                     "roofline": roofline(f / t / 1e12, BF16_PEAK_TFLOPS, "TFLOP/s", "mfma",
+                                                          read_traffic("prefill"))}
+        elif n == "StoreOp":
+            b = store_bytes(op, wl)
+            total_bytes += b
+            res["ops"]["store"] = {"ms": round(t * 1e3, 4), "GB/s": round(b / t / 1e9, 1), "bytes": b}
+        elif n == "CopyOp":
+            b = copy_bytes(op, wl)
+            total_bytes += b
+            res["ops"]["copy_blocks"] = {"ms": round(t * 1e3, 4), "GB/s": round(b / t / 1e9, 1), "bytes": b}
+    res["step_GB/s"] = round(total_bytes / wall / 1e9, 2)
+    res["step_TFLOP/s"] = round(total_flops / wall / 1e12, 3)
+    if with_cpu:
+        for op in ops:
+            if type(op).__name__ == "DecodeOp" and name == "decode":
+                res["cpu_baseline"] = cpu_baseline_decode(wl, op)
+            if type(op).__name__ == "PrefillOp" and name == "prefill":
+                res["cpu_baseline"] = cpu_baseline_prefill(wl, op)
+    return res
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode", choices=sorted(WORKLOAD_CONFIG))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the secondary prefill measurement")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the library has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    dev = torch.device("cuda:0")
+    with_cpu = not args.no_cpu_baseline
+    main_res = bench_workload(args.workload, args.steps, args.warmup, dev, with_cpu)
+    line = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": main_res["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1) bf16, seeded lengths and block tables)"}
+    if args.workload in ("decode", "mixed", "chunked") and "decode" in main_res["ops"]:
+        line.update(value=main_res["step_GB/s"], unit="GB/s")
+        line["roofline"] = main_res["ops"]["decode"]["roofline"]
+    else:
+        line.update(value=main_res["step_TFLOP/s"], unit="TFLOP/s")
+        line["roofline"] = main_res["ops"]["prefill"]["roofline"]
+    wl_cfg = WORKLOAD_CONFIG[args.workload]
+    line["config"] = {"workload": main_res["workload"], "config_index": wl_cfg, "ops": main_res["ops"]}
+    line["cpu_baseline"] = main_res.get("cpu_baseline")
+    if args.workload == "decode" and not args.no_prefill:
+        pre = bench_workload("prefill", max(10, args.steps // 2), max(3, args.warmup // 2), dev, with_cpu)
+        line["prefill"] = {"workload": pre["workload"], "value": pre["step_TFLOP/s"], "unit": "TFLOP/s",
+                           "ms_per_step": pre["ms_per_step"], "ops": pre["ops"],
+                           "roofline": pre["ops"]["prefill"]["roofline"],
+                           "cpu_baseline": pre.get("cpu_baseline")}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
