@@ -97,7 +97,7 @@ def copy_bytes(op, wl) -> float:
 class Step:
     """Device-resident inputs of one phase and a callable that runs it."""
 
-    def __init__(self, wl, ops, dev):
+    def __init__(self, wl, ops, dev, partition_size=0):
         import numpy as np
         import torch
         import paged_attention_block_amd as pa
@@ -120,11 +120,11 @@ class Step:
             elif name == "DecodeOp":
                 d.update(q=op.query.to(dev), table=i32(op.block_table), lens=i32(op.seq_lens))
                 d["out"] = torch.empty_like(d["q"])
+                d["part"] = partition_size or pa.pa_decode_partition_size(
+                    self.cache, len(op.seq_lens), wl.num_heads, op.max_seq_len, wl.sliding_window)
                 need = pa.pa_decode_workspace_size(self.cache, len(op.seq_lens), wl.num_heads,
-                                                   op.max_seq_len, wl.sliding_window)
+                                                   op.max_seq_len, wl.sliding_window, d["part"])
                 d["ws"] = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-                d["part"] = pa.pa_decode_partition_size(self.cache, len(op.seq_lens), wl.num_heads,
-                                                        op.max_seq_len, wl.sliding_window)
             self.prepared.append(d)
         self.names = [type(d["op"]).__name__ for d in self.prepared]
 
@@ -140,7 +140,8 @@ class Step:
                                  op.max_seqlen_k, wl.scale, wl.num_kv_heads, wl.sliding_window, out=d["out"])
         elif name == "DecodeOp":
             pa.pa_decode(d["q"], self.cache, d["table"], d["lens"], op.max_seq_len, wl.scale,
-                         wl.num_kv_heads, wl.sliding_window, out=d["out"], workspace=d["ws"])
+                         wl.num_kv_heads, wl.sliding_window, out=d["out"], workspace=d["ws"],
+                         partition_size=d["part"])
 
     def time(self, steps: int, warmup: int):
         """Wall time per step and mean HIP-event duration of every op over the timed steps."""
@@ -267,11 +268,11 @@ def roofline(achieved, peak, unit, bound, traffic=None):
             "frac": round(achieved / peak, 4), "traffic": traffic}
 
 
-def bench_workload(name, steps, warmup, dev, with_cpu):
+def bench_workload(name, steps, warmup, dev, with_cpu, partition_size=0):
     import workloads as W
     wl = W.config(WORKLOAD_CONFIG[name])
     phase = wl.phases[-1] if name == "chunked_decode" else wl.phases[0]
-    step = Step(wl, phase, dev)
+    step = Step(wl, phase, dev, partition_size)
     wall, per_op = step.time(steps, warmup)
     ops = [d["op"] for d in step.prepared]
     res = {"workload": W.CONFIG_NAMES[WORKLOAD_CONFIG[name]], "ms_per_step": round(wall * 1e3, 4), "ops": {}}
@@ -318,6 +319,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode", choices=sorted(WORKLOAD_CONFIG))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--partition-size", type=int, default=0, help="decode split-K keys per item (0 = auto)")
     ap.add_argument("--no-prefill", action="store_true", help="skip the secondary prefill measurement")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -328,7 +330,7 @@ def main() -> int:
     import torch
     dev = torch.device("cuda:0")
     with_cpu = not args.no_cpu_baseline
-    main_res = bench_workload(args.workload, args.steps, args.warmup, dev, with_cpu)
+    main_res = bench_workload(args.workload, args.steps, args.warmup, dev, with_cpu, args.partition_size)
     line = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
             "ms_per_step": main_res["ms_per_step"], "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1) bf16, seeded lengths and block tables)"}

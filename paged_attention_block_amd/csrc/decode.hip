@@ -46,28 +46,134 @@ __device__ inline uint32_t pack_bf16(float lo, float hi) {
 
 // DPL = dims per lane chunk of a V row: 8 (16 B) for D = 128, 4 (8 B) for D = 64.
 template <int D> struct VRow;
-template <> struct VRow<128> { typedef uint4 T; };
-template <> struct VRow<64> { typedef uint2 T; };
-
-__device__ inline uint32_t dw(const uint4& v, int i) {
-    return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
-}
-__device__ inline uint32_t dw(const uint2& v, int i) { return i == 0 ? v.x : v.y; }
+template <> struct VRow<128> { typedef u32x4 T; };
+template <> struct VRow<64> { typedef u32x2 T; };
 
 }  // namespace
 
+// Loads of the 32-key step at k0 into registers: K rows (2 groups of 16 keys x KS slices,
+// MFMA A-operand layout) and the V rows one lane needs for the PV MFMAs (8 keys x DPL
+// dims).  Both 16-key groups of a step lie in one physical block each (block_size >= 16,
+// 16-aligned); a group with no live key is never looked up and its lanes read the other
+// group's rows instead, so every load is in bounds and unconditional.  Keys outside
+// [kb, ke) are masked after the load.
 template <int D>
-__global__ __launch_bounds__(64) void decode_bf16_kernel(const DecodeArgs a) {
+__device__ __forceinline__ void load_step(int k0, int kb, int ke, const int32_t* __restrict__ table,
+                                          int shift, int BS, int64_t row_elems, int g,
+                                          const char* __restrict__ kplane,
+                                          const char* __restrict__ vplane, uint32_t k_off,
+                                          uint32_t v_off, uint32_t row_bytes,
+                                          u32x4 (&kr)[2][D / 32], typename VRow<D>::T (&vr)[8]) {
+    typedef typename VRow<D>::T VT;
+    // wave-uniform byte offset of (first key of each 16-key group, KV head g) in a plane
+    int64_t gb[2];
+    bool gv[2];
+#pragma unroll
+    for (int ga = 0; ga < 2; ++ga) {
+        const int j0 = k0 + 16 * ga;
+        gv[ga] = (j0 < ke) && (j0 + 16 > kb);
+        const int blk = gv[ga] ? table[j0 >> shift] : 0;
+        gb[ga] = (((int64_t)blk * BS + (j0 & (BS - 1))) * row_elems + (int64_t)g * D) * 2;
+    }
+    if (!gv[0]) gb[0] = gb[1];
+    if (!gv[1]) gb[1] = gb[0];
+#pragma unroll
+    for (int ga = 0; ga < 2; ++ga) {
+        const char* base = kplane + gb[ga];
+#pragma unroll
+        for (int t = 0; t < D / 32; ++t) kr[ga][t] = *(const u32x4*)(base + k_off + 64 * t);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const char* base = vplane + gb[j >> 2] + (int64_t)(j & 3) * row_bytes;
+        vr[j] = *(const VT*)(base + v_off);
+    }
+}
+
+// Online-softmax update of one 32-key step (scores by MFMA, P packed to bf16, PV by MFMA).
+template <int D>
+__device__ __forceinline__ void compute_step(int k0, int kb, int ke, int grp, float c_log2,
+                                             const bf16x8 (&qf)[D / 32], u32x4 (&kr)[2][D / 32],
+                                             typename VRow<D>::T (&vr)[8], f32x4 (&oacc)[D / 16],
+                                             float& m_run, float& l_run) {
+    constexpr int KS = D / 32;
+    constexpr int DPL = D / 16;
+    typedef typename VRow<D>::T VT;
+    const bool edge = (k0 < kb) || (k0 + 32 > ke);
+    f32x4 sacc[2];
+#pragma unroll
+    for (int ga = 0; ga < 2; ++ga) {
+        sacc[ga] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < KS; ++t)
+            sacc[ga] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[ga][t]),
+                                                               qf[t], sacc[ga], 0, 0, 0);
+    }
+    float sc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sc[j] = sacc[j >> 2][j & 3];
+    if (edge) {
+        // this lane's score j and V row j are the same key: k0 + 16*(j/4) + 4*grp + j%4
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int key = k0 + 16 * (j >> 2) + 4 * grp + (j & 3);
+            const bool ok = key >= kb && key < ke;
+            sc[j] = ok ? sc[j] : -INFINITY;
+            vr[j] = ok ? vr[j] : (VT)(0u);
+        }
+    }
+    float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
+                     fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx * c_log2);
+    const float msub = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - msub);
+    float pr[8];
+    float psum = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        pr[j] = __builtin_amdgcn_exp2f(fmaf(sc[j], c_log2, -msub));
+        psum += pr[j];
+    }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+    if (__any(alpha != 1.f)) {
+#pragma unroll
+        for (int t = 0; t < DPL; ++t) oacc[t] *= alpha;
+    }
+    const u32x4 pw = {pack_bf16(pr[0], pr[1]), pack_bf16(pr[2], pr[3]), pack_bf16(pr[4], pr[5]),
+                      pack_bf16(pr[6], pr[7])};
+    const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
+#pragma unroll
+    for (int t = 0; t < DPL; ++t) {
+        const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
+        u32x4 w;
+        w[0] = __builtin_amdgcn_perm(vr[1][t >> 1], vr[0][t >> 1], sel);
+        w[1] = __builtin_amdgcn_perm(vr[3][t >> 1], vr[2][t >> 1], sel);
+        w[2] = __builtin_amdgcn_perm(vr[5][t >> 1], vr[4][t >> 1], sel);
+        w[3] = __builtin_amdgcn_perm(vr[7][t >> 1], vr[6][t >> 1], sel);
+        oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w), pb, oacc[t],
+                                                          0, 0, 0);
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(512) void decode_bf16_kernel(const DecodeArgs a) {
     constexpr int KS = D / 32;   // k-slices of q.K^T
     constexpr int DPL = D / 16;  // dims per lane chunk of a V row = PV MFMAs per step
     typedef typename VRow<D>::T VT;
 
-    const int lane = threadIdx.x;
+    // one workgroup per (sequence, group of up to 8 KV heads, partition); wave w serves KV
+    // head 8*blockIdx.y + w, so the waves of a workgroup stream the same physical blocks
+    // (all KV heads of a token row are adjacent) at the same time
+    const int lane = threadIdx.x & 63;
     const int col = lane & 15;
     const int grp = lane >> 4;
     const int s = blockIdx.x;
-    const int g = blockIdx.y;
+    const int g = blockIdx.y * 8 + (threadIdx.x >> 6);
     const int p = blockIdx.z;
+    if (g >= a.c.num_kv_heads) return;
 
     const int n = a.seq_lens[s];
     const int G = a.group;
@@ -96,107 +202,52 @@ __global__ __launch_bounds__(64) void decode_bf16_kernel(const DecodeArgs a) {
     const int BS = a.c.block_size;
     const int shift = a.c.block_shift;
     const int Hkv = a.c.num_kv_heads;
-    const __bf16* kplane = (const __bf16*)a.c.kv;
-    const __bf16* vplane = kplane + a.c.plane_elems;
-    const int32_t* table = a.table + (int64_t)s * a.max_blocks;
+    const char* __restrict__ kplane = (const char*)a.c.kv;
+    const char* __restrict__ vplane = kplane + a.c.plane_elems * 2;
+    const int32_t* __restrict__ table = a.table + (int64_t)s * a.max_blocks;
     const float c_log2 = a.scale * 1.4426950408889634f;
+    // per-lane byte offsets from a group's first row: K rows (key col, dims 8*grp of each
+    // 32-dim slice), V rows (key 4*grp + j%4, dims DPL*col)
+    const int64_t row_elems = (int64_t)Hkv * D;
+    const uint32_t row_bytes = (uint32_t)(row_elems * 2);
+    const uint32_t k_off = (uint32_t)col * row_bytes + 16u * grp;
+    const uint32_t v_off = (uint32_t)(4 * grp) * row_bytes + 2u * DPL * col;
 
     // Q^T operand: head col, dims 32t + 8*grp .. +8
     bf16x8 qf[KS];
     {
-        const uint4* qrow = (const uint4*)((const __bf16*)a.q + ((int64_t)s * H + head) * D);
+        const u32x4* qrow = (const u32x4*)((const __bf16*)a.q + ((int64_t)s * H + (head_ok ? head : g * G)) * D);
+#pragma unroll
         for (int t = 0; t < KS; ++t) {
-            uint4 x = head_ok ? qrow[4 * t + grp] : make_uint4(0, 0, 0, 0);
-            qf[t] = __builtin_bit_cast(bf16x8, x);
+            const u32x4 x = qrow[4 * t + grp];
+            qf[t] = __builtin_bit_cast(bf16x8, head_ok ? x : (u32x4)(0u));
         }
     }
 
     f32x4 oacc[DPL];
+#pragma unroll
     for (int t = 0; t < DPL; ++t) oacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY;
     float l_run = 0.f;
 
-    for (int k0 = step_begin; k0 < ke; k0 += 32) {
-        const bool edge = (k0 < kb) || (k0 + 32 > ke);
-        // physical blocks of the two 16-key groups (uniform -> scalar loads); a group
-        // outside [kb, ke) is never looked up
-        int64_t rowbase[2];
-        bool gv[2];
-        for (int ga = 0; ga < 2; ++ga) {
-            const int j0 = k0 + 16 * ga;
-            gv[ga] = (j0 < ke) && (j0 + 16 > kb);
-            const int blk = gv[ga] ? table[j0 >> shift] : 0;
-            rowbase[ga] = (int64_t)blk * BS + (j0 & (BS - 1));   // token row of key j0
-        }
-        // K rows: key k0 + 16*ga + col, 16 B at dims 32t + 8*grp
-        uint4 kr[2][KS];
-        for (int ga = 0; ga < 2; ++ga) {
-            const int key = k0 + 16 * ga + col;
-            const bool ok = gv[ga] && (!edge || (key >= kb && key < ke));
-            const uint4* src = (const uint4*)(kplane + ((rowbase[ga] + col) * Hkv + g) * D);
-            for (int t = 0; t < KS; ++t) kr[ga][t] = ok ? src[4 * t + grp] : make_uint4(0, 0, 0, 0);
-        }
-        // V rows: key k0 + 16*(j/4) + 4*grp + j%4, DPL dims at DPL*col
-        VT vr[8];
-        for (int j = 0; j < 8; ++j) {
-            const int ga = j >> 2;
-            const int rk = 4 * grp + (j & 3);
-            const int key = k0 + 16 * ga + rk;
-            const bool ok = gv[ga] && (!edge || (key >= kb && key < ke));
-            const VT* src = (const VT*)(vplane + ((rowbase[ga] + rk) * Hkv + g) * D);
-            VT z;
-            __builtin_memset(&z, 0, sizeof(z));
-            vr[j] = ok ? src[col] : z;
-        }
-
-        // S^T for the two 16-key groups
-        f32x4 sacc[2];
-        for (int ga = 0; ga < 2; ++ga) {
-            sacc[ga] = f32x4{0.f, 0.f, 0.f, 0.f};
-            for (int t = 0; t < KS; ++t)
-                sacc[ga] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    __builtin_bit_cast(bf16x8, kr[ga][t]), qf[t], sacc[ga], 0, 0, 0);
-        }
-        float sc[8];
-        float mx = -INFINITY;
-        for (int j = 0; j < 8; ++j) {
-            float v = sacc[j >> 2][j & 3];
-            if (edge) {
-                const int key = k0 + 16 * (j >> 2) + 4 * grp + (j & 3);
-                v = (key >= kb && key < ke) ? v : -INFINITY;
-            }
-            sc[j] = v;
-            mx = fmaxf(mx, v);
-        }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx * c_log2);
-        const float msub = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - msub);
-        float pr[8];
-        float psum = 0.f;
-        for (int j = 0; j < 8; ++j) {
-            pr[j] = __builtin_amdgcn_exp2f(fmaf(sc[j], c_log2, -msub));
-            psum += pr[j];
-        }
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
-        for (int t = 0; t < DPL; ++t) oacc[t] *= alpha;
-
-        uint32_t pk[4];
-        for (int i = 0; i < 4; ++i) pk[i] = pack_bf16(pr[2 * i], pr[2 * i + 1]);
-        const bf16x8 pb = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
-
-        for (int t = 0; t < DPL; ++t) {
-            const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
-            uint4 w;
-            w.x = __builtin_amdgcn_perm(dw(vr[1], t >> 1), dw(vr[0], t >> 1), sel);
-            w.y = __builtin_amdgcn_perm(dw(vr[3], t >> 1), dw(vr[2], t >> 1), sel);
-            w.z = __builtin_amdgcn_perm(dw(vr[5], t >> 1), dw(vr[4], t >> 1), sel);
-            w.w = __builtin_amdgcn_perm(dw(vr[7], t >> 1), dw(vr[6], t >> 1), sel);
-            oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w), pb,
-                                                              oacc[t], 0, 0, 0);
-        }
+    // Two register sets: the loads of step i+1 are in flight while step i computes.  The
+    // prefetch is unconditional (the last step re-reads its own rows, which hit in cache)
+    // so that every iteration issues the same number of loads and the waits stay exact.
+    u32x4 kA[2][KS], kB[2][KS];
+    VT vA[8], vB[8];
+    int k0 = step_begin;
+    load_step<D>(k0, kb, ke, table, shift, BS, row_elems, g, kplane, vplane, k_off, v_off, row_bytes, kA, vA);
+    while (true) {
+        const int n1 = k0 + 32 < ke ? k0 + 32 : k0;
+        load_step<D>(n1, kb, ke, table, shift, BS, row_elems, g, kplane, vplane, k_off, v_off, row_bytes, kB, vB);
+        compute_step<D>(k0, kb, ke, grp, c_log2, qf, kA, vA, oacc, m_run, l_run);
+        k0 += 32;
+        if (k0 >= ke) break;
+        const int n2 = k0 + 32 < ke ? k0 + 32 : k0;
+        load_step<D>(n2, kb, ke, table, shift, BS, row_elems, g, kplane, vplane, k_off, v_off, row_bytes, kA, vA);
+        compute_step<D>(k0, kb, ke, grp, c_log2, qf, kB, vB, oacc, m_run, l_run);
+        k0 += 32;
+        if (k0 >= ke) break;
     }
 
     float l_tot = l_run + __shfl_xor(l_run, 16);
@@ -255,11 +306,13 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const DecodeArgs a) {
 }
 
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t st) {
-    const dim3 grid(a.num_seqs, a.c.num_kv_heads, a.max_parts);
+    const int hkv = a.c.num_kv_heads;
+    const dim3 grid(a.num_seqs, (hkv + 7) / 8, a.max_parts);
+    const dim3 block(64 * (hkv < 8 ? hkv : 8));
     if (a.c.head_size == 128)
-        hipLaunchKernelGGL(decode_bf16_kernel<128>, grid, dim3(64), 0, st, a);
+        hipLaunchKernelGGL(decode_bf16_kernel<128>, grid, block, 0, st, a);
     else
-        hipLaunchKernelGGL(decode_bf16_kernel<64>, grid, dim3(64), 0, st, a);
+        hipLaunchKernelGGL(decode_bf16_kernel<64>, grid, block, 0, st, a);
     if (a.max_parts > 1) {
         const dim3 mg(a.num_seqs, a.num_heads);
         if (a.c.head_size == 128)

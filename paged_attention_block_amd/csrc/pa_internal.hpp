@@ -9,6 +9,8 @@ namespace pa {
 // ---------------------------------------------------------------- device vector types
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 // Lanes of one wavefront.
 constexpr int kWave = 64;
