@@ -38,11 +38,7 @@ __device__ inline float wave_sum(float v) {
     for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
     return v;
 }
-__device__ inline uint32_t pack_bf16(float lo, float hi) {
-    const uint32_t a = __builtin_bit_cast(unsigned short, (__bf16)lo);
-    const uint32_t b = __builtin_bit_cast(unsigned short, (__bf16)hi);
-    return a | (b << 16);
-}
+__device__ inline uint32_t pack_bf16(float lo, float hi) { return pack_bf16x2(lo, hi); }
 
 // DPL = dims per lane chunk of a V row: 8 (16 B) for D = 128, 4 (8 B) for D = 64.
 template <int D> struct VRow;

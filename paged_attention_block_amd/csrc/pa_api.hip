@@ -83,13 +83,14 @@ int launch_status(hipError_t e) {
     return PA_OK;
 }
 
-// Split-K partition size: aim for ~8 work items per SIMD (4 per CU x 256 CUs x 8) with at
-// least 128 keys per item, and keep the partial states small against the KV bytes.
+// Split-K partition size.  Measured on MI355X: long partitions stream best (the start of
+// each one pays a full memory latency), so aim for about 2048 (sequence, KV head,
+// partition) items -- 2 per SIMD at the longest sequence -- within [128, 2048] keys.
 int32_t auto_part(int32_t num_seqs, int32_t num_kv_heads, int32_t max_keys) {
-    const int64_t items_target = 8192;
+    const int64_t items_target = 2048;
     const int64_t total = (int64_t)num_seqs * num_kv_heads * max_keys;
     int64_t part = 128;
-    while (part < 8192 && total / part > items_target) part *= 2;
+    while (part < 2048 && total / part > items_target) part *= 2;
     return (int32_t)part;
 }
 
