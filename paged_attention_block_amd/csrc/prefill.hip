@@ -13,17 +13,21 @@
 //   S^T[64 keys x 32 rows] = K . Q^T      (16x16x32 bf16 MFMA, K from LDS, Q^T in VGPRs)
 //   online softmax on S^T, P^T packed to bf16 straight from the accumulators
 //   O^T[D x 32 rows]   += V^T . P^T        (V^T from LDS)
-// V is transposed on its way into LDS: a thread loads one 16-byte chunk (8 dims) of 8 keys
-// and writes 8 dims x 8 keys with byte permutes.  The 8 keys of a chunk are the ones one
-// PV MFMA lane group needs (keys 32c + 16*(j/4) + 4*grp + j%4), so every MFMA operand is a
-// single 16-byte LDS read.  LDS rows are padded by 16 bytes, which keeps the 16 lanes that
-// read 16 different rows on distinct banks.
+// K and V rows go from HBM straight into LDS (global_load_lds, 16 B per lane, no register
+// staging), two tiles deep, so the copy of tile i+1 overlaps the math of tile i.  The
+// V^T operand is read with the transposing LDS read (ds_read_b64_tr_b16): within a
+// 16-lane group, lane i receives element i%4 of the 4-element vectors addressed by lanes
+// i/4 + 4j, so when source lane s addresses row base + s/4, dims d0 + 4*(s%4), lane i
+// receives 4 consecutive keys at dim d0 + i -- the MFMA layout, from a row-major tile.
+// LDS rows are packed; the 16-byte chunks of row r are XOR-swizzled (K: chunk ^ (r & 15),
+// V: chunk ^ 2*(r & 7)) so the operand reads hit distinct banks.  The swizzle is applied
+// on the global side: a lane fetches the global chunk that belongs at its fixed LDS slot.
 //
 // Tiles outside the union of the rows' live key ranges are never visited; inside a
-// visited tile, keys outside that union are loaded from a live block of the same tile
-// (never through an unread block-table entry) and zeroed before they reach LDS, so cache
-// slots outside every row's window may hold anything.  Tiles crossing the causal diagonal
-// or the window edge get an element mask; interior tiles do not.
+// visited tile, keys outside that union are copied from a live block of the same tile
+// (never through an unread block-table entry) and then overwritten with zeros in LDS by
+// the wave that copied them, so cache slots outside every row's window may hold anything.
+// Tiles crossing the causal diagonal or the window edge get an element mask.
 //
 // Workgroups are numbered so that each XCD (work dispatched round-robin over 8) runs the
 // q-tiles of one (sequence, KV head) back to back: those share K/V through that XCD's L2.
@@ -44,20 +48,22 @@ struct PrefillGrid {
     int n_qtiles;       // ceil(max_seqlen_q / BM)
 };
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
 template <int D, int RW>
 __global__ __launch_bounds__(512) void prefill_bf16_kernel(const PrefillArgs a, const PrefillGrid pg) {
     constexpr int BM = 32 * RW;       // query rows per tile
     constexpr int KS = D / 32;        // k-slices of q.K^T
     constexpr int DB = D / 16;        // 16-dim output blocks
-    constexpr int CPR = D / 8;        // 16-byte chunks per K row
-    constexpr int KIT = BN * CPR / 256;   // K chunks per staging thread (threads 0..255)
-    constexpr int KRPI = 256 / CPR;       // K rows per staging round
-    constexpr int VOCT = (BN / 8) * (D / 8);  // 8-key x 8-dim V blocks per tile
-    constexpr int KROW = D + 8;       // LDS row stride of K (elements)
-    constexpr int VROW = BN + 8;      // LDS row stride of V^T (elements)
+    constexpr int CPR = D / 8;        // 16-byte chunks per row
+    constexpr int RPI = 64 / CPR;     // rows per 1 KB copy instruction
+    constexpr int NQ = BN / RPI;      // copy instructions per plane per tile
+    constexpr int TILE = BN * D * 2;  // bytes of one plane of one tile
+    constexpr int KSW = CPR >= 16 ? 15 : CPR - 1;        // K swizzle mask
+    constexpr int VSW = CPR >= 16 ? 14 : CPR - 2;        // V swizzle mask (even values)
 
-    __shared__ __attribute__((aligned(16))) __bf16 lds_k[2][BN * KROW];
-    __shared__ __attribute__((aligned(16))) __bf16 lds_v[2][D * VROW];
+    __shared__ __attribute__((aligned(1024))) char lds[2][2][TILE];  // [buffer][plane]
 
     // ---------------------------------------------------------------- work item
     const int b = blockIdx.x;
@@ -81,6 +87,7 @@ __global__ __launch_bounds__(512) void prefill_bf16_kernel(const PrefillArgs a, 
     const int rows_end = min(i0 + BM, sq);
 
     const int tid = threadIdx.x;
+    const int nwaves = blockDim.x >> 6;
     const int wave = tid >> 6;
     const int lane = tid & 63;
     const int col = lane & 15;
@@ -109,7 +116,7 @@ __global__ __launch_bounds__(512) void prefill_bf16_kernel(const PrefillArgs a, 
     const int BS = a.c.block_size;
     const int shift = a.c.block_shift;
     const char* __restrict__ kplane = (const char*)a.c.kv;
-    const char* __restrict__ vplane = kplane + a.c.plane_elems * 2;
+    const int64_t vdelta = a.c.plane_elems * 2;
     const int32_t* __restrict__ table = a.table + (int64_t)s * a.max_blocks;
     const int64_t RB = (int64_t)Hkv * D * 2;  // cache token-row bytes
 
@@ -138,28 +145,31 @@ __global__ __launch_bounds__(512) void prefill_bf16_kernel(const PrefillArgs a, 
     float m_run[2] = {-INFINITY, -INFINITY};
     float l_run[2] = {0.f, 0.f};
 
-    // ---------------------------------------------------------------- K/V tile staging
-    // K: thread tid < 256 stages chunks (row k_r0 + KRPI*i, column k_dc), i < KIT; the row's
-    // 16-key group is (k_r0 >> 4) + (KRPI / 16) * i, uniform within a wave.
-    const bool k_worker = tid < 256;
-    const int k_r0 = tid / CPR;
-    const int k_dc = tid - k_r0 * CPR;
-    const uint32_t k_goff = (uint32_t)((((k_r0 & 15) * Hkv + g) * D + k_dc * 8) * 2);
-    const uint32_t k_loff = (uint32_t)(k_r0 * KROW + k_dc * 8);
-    // V: thread tid < VOCT stages the 8 keys 32*v_c + 16*(j/4) + 4*v_gq + j%4 at dims
-    // 8*v_dc .. +8 (rows 4*v_gq + j%4 of groups 2*v_c + j/4)
-    const bool v_worker = tid < VOCT;
-    const int v_o = tid & 7;
-    const int v_dc = tid >> 3;
-    const int v_c = v_o >> 2;
-    const int v_gq = v_o & 3;
-    const uint32_t v_goff = (uint32_t)((((4 * v_gq) * Hkv + g) * D + v_dc * 8) * 2);
-    const uint32_t v_loff = (uint32_t)(8 * v_dc * VROW + 32 * v_c + 8 * v_gq);
+    // ---------------------------------------------------------------- tile copies
+    // Copy instruction q (0 .. 2*NQ-1; plane q / NQ) fills LDS bytes [1024*qq, +1024) of its
+    // plane, qq = q % NQ: rows RPI*qq + lane / CPR, slot lane % CPR.  Wave w issues
+    // q = w, w + nwaves, ...  The lane offsets relative to the first token row of the row's
+    // 16-key group are the same for every tile.
+    const int crow = lane / CPR;           // row within the instruction's rows
+    const int cslot = lane % CPR;          // LDS chunk slot within the row
+    auto lane_goff = [&](int q) -> uint32_t {
+        const bool isv = q >= NQ;
+        const int row = RPI * (isv ? q - NQ : q) + crow;
+        const int chunk = cslot ^ (isv ? (2 * row) & VSW : row & KSW);
+        return (uint32_t)((((row & 15) * Hkv + g) * D + chunk * 8) * 2);
+    };
 
-    u32x4 kreg[KIT];
-    u32x4 vreg[8];
+    // this wave's copies: q = wave + nwaves*i (at most CPW of them, >= 4 waves per
+    // workgroup); lane offsets computed once
+    constexpr int CPW = (2 * NQ + 3) / 4;
+    uint32_t cgoff[CPW];
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) {
+        const int q = wave + nwaves * i;
+        cgoff[i] = q < 2 * NQ ? lane_goff(q) : 0u;
+    }
 
-    auto load_tile = [&](int k0) {
+    auto issue = [&](int k0, int buf) {
         int64_t gb[4];
         bool gv[4];
 #pragma unroll
@@ -173,67 +183,59 @@ __global__ __launch_bounds__(512) void prefill_bf16_kernel(const PrefillArgs a, 
         const int64_t live = gv[0] ? gb[0] : gv[1] ? gb[1] : gv[2] ? gb[2] : gb[3];
 #pragma unroll
         for (int ga = 0; ga < 4; ++ga) gb[ga] = gv[ga] ? gb[ga] : live;
-        if (k_worker) {
 #pragma unroll
-            for (int i = 0; i < KIT; ++i) {
-                const int ga = (k_r0 >> 4) + (KRPI / 16) * i;
+        for (int i = 0; i < CPW; ++i) {
+            const int q = wave + nwaves * i;
+            if (q < 2 * NQ) {
+                const bool isv = q >= NQ;
+                const int qq = isv ? q - NQ : q;
+                const int ga = (RPI * qq) >> 4;
                 const int64_t base = ga == 0 ? gb[0] : ga == 1 ? gb[1] : ga == 2 ? gb[2] : gb[3];
-                kreg[i] = *(const u32x4*)(kplane + base + k_goff);
-            }
-        }
-        if (v_worker) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int64_t base = v_c ? gb[2 + (j >> 2)] : gb[j >> 2];
-                vreg[j] = *(const u32x4*)(vplane + base + v_goff + (j & 3) * RB);
+                const char* src = kplane + (isv ? vdelta + base : base) + cgoff[i];
+                __builtin_amdgcn_global_load_lds(
+                    (const void*)src, (__attribute__((address_space(3))) void*)(lds[buf][isv ? 1 : 0] + 1024 * qq), 16, 0, 0);
             }
         }
     };
-    auto store_tile = [&](int buf, int k0) {
-        const bool zero = (k0 < wg_lo) || (k0 + BN - 1 > wg_hi);
-        if (k_worker) {
+    // after this wave's copies of the tile at k0 landed: zero the rows it copied whose key
+    // lies outside [wg_lo, wg_hi]
+    auto zero_dead = [&](int k0, int buf) {
+        if (k0 >= wg_lo && k0 + BN - 1 <= wg_hi) return;
 #pragma unroll
-            for (int i = 0; i < KIT; ++i) {
-                u32x4 x = kreg[i];
-                if (zero) {
-                    const int key = k0 + k_r0 + KRPI * i;
-                    x = (key >= wg_lo && key <= wg_hi) ? x : (u32x4)(0u);
-                }
-                *(u32x4*)(&lds_k[buf][k_loff + KRPI * i * KROW]) = x;
-            }
-        }
-        if (v_worker) {
-            if (zero) {
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const int key = k0 + 32 * v_c + 16 * (j >> 2) + 4 * v_gq + (j & 3);
-                    vreg[j] = (key >= wg_lo && key <= wg_hi) ? vreg[j] : (u32x4)(0u);
-                }
-            }
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-                const int ws = e >> 1;
-                u32x4 w;
-                w[0] = __builtin_amdgcn_perm(vreg[1][ws], vreg[0][ws], sel);
-                w[1] = __builtin_amdgcn_perm(vreg[3][ws], vreg[2][ws], sel);
-                w[2] = __builtin_amdgcn_perm(vreg[5][ws], vreg[4][ws], sel);
-                w[3] = __builtin_amdgcn_perm(vreg[7][ws], vreg[6][ws], sel);
-                *(u32x4*)(&lds_v[buf][v_loff + e * VROW]) = w;
+        for (int i = 0; i < CPW; ++i) {
+            const int q = wave + nwaves * i;
+            if (q < 2 * NQ) {
+                const bool isv = q >= NQ;
+                const int qq = isv ? q - NQ : q;
+                const int key = k0 + RPI * qq + crow;
+                if (key < wg_lo || key > wg_hi)
+                    *(u32x4*)(lds[buf][isv ? 1 : 0] + 1024 * qq + 16 * lane) = (u32x4)(0u);
             }
         }
     };
 
-    // LDS operand offsets of this lane (elements)
-    const int kop = col * KROW + 8 * grp;
-    const int vop = col * VROW + 8 * grp;
+    // LDS operand addresses of this lane
+    uint32_t koff[4][KS];  // [16-key group][k-slice]
+#pragma unroll
+    for (int ga = 0; ga < 4; ++ga)
+#pragma unroll
+        for (int t = 0; t < KS; ++t) {
+            const int row = 16 * ga + col;
+            koff[ga][t] = (uint32_t)(row * D * 2 + (((4 * t + grp) ^ (row & KSW)) * 16));
+        }
+    // V^T: source lane col of group grp addresses row 32cc + 16hh + 4*grp + col/4, dims
+    // 16*db + 4*(col%4) .. +4; the row's swizzle depends on (row & 7) = (4*grp + col/4) & 7
+    const int vrow0 = 4 * grp + (col >> 2);
+    const int vsw = (2 * vrow0) & VSW;
+    uint32_t voff_base = (uint32_t)(vrow0 * D * 2 + 8 * (col & 1));
+    const int vch = (col & 3) >> 1;  // chunk within the 16-dim block
 
     // ---------------------------------------------------------------- one tile of math
     auto compute_tile = [&](int buf, int k0) {
         if (!wave_active || k0 > wv_hi || k0 + BN - 1 < wv_lo) return;
         const bool edge = (k0 + BN - 1 > wv_p_min) || (W > 0 && k0 < wv_lo_max);
-        const __bf16* kt = lds_k[buf] + kop;
-        const __bf16* vt = lds_v[buf] + vop;
+        const char* kt = lds[buf][0];
+        const char* vt = lds[buf][1];
 
         f32x4 sacc[4][2];
 #pragma unroll
@@ -244,7 +246,7 @@ __global__ __launch_bounds__(512) void prefill_bf16_kernel(const PrefillArgs a, 
         for (int t = 0; t < KS; ++t) {
 #pragma unroll
             for (int ga = 0; ga < 4; ++ga) {
-                const bf16x8 kf = *(const bf16x8*)(kt + 16 * ga * KROW + 32 * t);
+                const bf16x8 kf = *(const bf16x8*)(kt + koff[ga][t]);
 #pragma unroll
                 for (int nb = 0; nb < 2; ++nb)
                     sacc[ga][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[nb][t], sacc[ga][nb], 0, 0, 0);
@@ -276,14 +278,10 @@ __global__ __launch_bounds__(512) void prefill_bf16_kernel(const PrefillArgs a, 
             alpha[nb] = __builtin_amdgcn_exp2f(m_run[nb] - msub);
             m_run[nb] = m_new;
             float pv[4][4];
-            float ps[4];
 #pragma unroll
-            for (int ga = 0; ga < 4; ++ga) {
+            for (int ga = 0; ga < 4; ++ga)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) pv[ga][r] = __builtin_amdgcn_exp2f(fmaf(sacc[ga][nb][r], c_log2, -msub));
-                ps[ga] = (pv[ga][0] + pv[ga][1]) + (pv[ga][2] + pv[ga][3]);
-            }
-            l_run[nb] = l_run[nb] * alpha[nb] + ((ps[0] + ps[1]) + (ps[2] + ps[3]));
 #pragma unroll
             for (int cc = 0; cc < 2; ++cc) {
                 pk[cc][nb][0] = pack_bf16x2(pv[2 * cc][0], pv[2 * cc][1]);
@@ -291,6 +289,10 @@ __global__ __launch_bounds__(512) void prefill_bf16_kernel(const PrefillArgs a, 
                 pk[cc][nb][2] = pack_bf16x2(pv[2 * cc + 1][0], pv[2 * cc + 1][1]);
                 pk[cc][nb][3] = pack_bf16x2(pv[2 * cc + 1][2], pv[2 * cc + 1][3]);
             }
+            float ps[4];
+#pragma unroll
+            for (int ga = 0; ga < 4; ++ga) ps[ga] = (pv[ga][0] + pv[ga][1]) + (pv[ga][2] + pv[ga][3]);
+            l_run[nb] = l_run[nb] * alpha[nb] + ((ps[0] + ps[1]) + (ps[2] + ps[3]));
         }
         if (__any(alpha[0] != 1.f || alpha[1] != 1.f)) {
 #pragma unroll
@@ -302,7 +304,14 @@ __global__ __launch_bounds__(512) void prefill_bf16_kernel(const PrefillArgs a, 
         for (int cc = 0; cc < 2; ++cc) {
 #pragma unroll
             for (int d = 0; d < DB; ++d) {
-                const bf16x8 vf = *(const bf16x8*)(vt + 16 * d * VROW + 32 * cc);
+                s16x4 vh[2];
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int rowoff = (32 * cc + 16 * hh) * D * 2;  // rows shift by 16: same swizzle
+                    const uint32_t o = voff_base + rowoff + (((2 * d + vch) ^ vsw) * 16);
+                    vh[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)((__attribute__((address_space(3))) char*)vt + o));
+                }
+                const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(vh[0], vh[1], 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
                 for (int nb = 0; nb < 2; ++nb)
                     oacc[d][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
@@ -315,16 +324,14 @@ __global__ __launch_bounds__(512) void prefill_bf16_kernel(const PrefillArgs a, 
     if (wg_hi >= wg_lo) {
         const int kt_begin = wg_lo / BN;
         const int kt_end = wg_hi / BN + 1;
-        load_tile(kt_begin * BN);
-        store_tile(0, kt_begin * BN);
-        __syncthreads();
+        issue(kt_begin * BN, 0);
         for (int kt = kt_begin; kt < kt_end; ++kt) {
             const int buf = (kt - kt_begin) & 1;
-            const bool has_next = kt + 1 < kt_end;
-            if (has_next) load_tile((kt + 1) * BN);
+            __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): this wave's copies landed
+            zero_dead(kt * BN, buf);
+            __syncthreads();                     // all copies of tile kt visible; buf^1 free
+            if (kt + 1 < kt_end) issue((kt + 1) * BN, buf ^ 1);
             compute_tile(buf, kt * BN);
-            if (has_next) store_tile(buf ^ 1, (kt + 1) * BN);
-            __syncthreads();
         }
     }
 
@@ -355,7 +362,8 @@ static void launch_rw(const PrefillArgs& a, const PrefillGrid& pg, int threads, 
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t st) {
     const int G = a.group;
-    // row-waves per head: keep 4..8 waves per workgroup
+    // row-waves per head: 4..8 waves per workgroup (measured: two independent 4-wave
+    // workgroups per CU beat one 8-wave workgroup)
     const int RW = G >= 4 ? 1 : (G >= 2 ? 2 : 4);
     PrefillGrid pg;
     pg.heads_per_wg = G * RW <= 8 ? G : 8 / RW;
