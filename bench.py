@@ -178,17 +178,15 @@ def cpu_threads() -> int:
         return 1
 
 
-def cpu_baseline_decode(wl, op, budget_s: float = 20.0):
-    """Oracle decode of as many sequences as fit ~budget_s (at least 4), in GB/s."""
-    import numpy as np
+def cpu_baseline_decode(wl, op, budget_s: float = 10.0):
+    """Oracle decode of the sequences in order (wrapping around) until ~budget_s, in GB/s."""
     import oracle
     vals = wl.kv_cache.float().numpy()
     q = op.query.float().numpy()
     done, bytes_done, t_used = 0, 0.0, 0.0
     b = len(op.seq_lens)
-    t_start = time.perf_counter()
-    while done < b and (t_used < budget_s or done < 4):
-        s = done
+    while t_used < budget_s or done < 4:
+        s = done % b
         sub = type(op)(query=op.query[s:s + 1], block_table=op.block_table[s:s + 1],
                        seq_lens=op.seq_lens[s:s + 1], max_seq_len=int(op.seq_lens[s]),
                        out_rows=op.out_rows, seq_ids=[s])
@@ -198,14 +196,13 @@ def cpu_baseline_decode(wl, op, budget_s: float = 20.0):
         t_used += time.perf_counter() - t0
         bytes_done += decode_bytes(sub, wl)
         done += 1
-    del t_start
     return {"value": round(bytes_done / t_used / 1e9, 4), "unit": "GB/s", "cores": cpu_threads(),
             "kind": "oracle",
-            "sample": f"fp64 numpy oracle decode of the first {done} of {b} sequences "
-                      f"({bytes_done / 1e6:.1f} MB algorithmic, {t_used:.1f} s)"}
+            "sample": f"fp64 numpy oracle decode of {done} sequence decodes (the batch of {b} in order, "
+                      f"repeated) ({bytes_done / 1e6:.1f} MB algorithmic, {t_used:.1f} s)"}
 
 
-def cpu_baseline_prefill(wl, op, budget_s: float = 20.0):
+def cpu_baseline_prefill(wl, op, budget_s: float = 10.0):
     """Oracle prefill of whole sequences, shortest first, until ~budget_s; TFLOP/s."""
     import numpy as np
     import oracle
@@ -214,9 +211,10 @@ def cpu_baseline_prefill(wl, op, budget_s: float = 20.0):
     lens = np.diff(op.cu_seqlens_q)
     order = np.argsort(lens)
     flops, t_used, n = 0.0, 0.0, 0
-    for s in order:
-        if t_used >= budget_s and n >= 1:
-            break
+    k = 0
+    while t_used < budget_s or n < 1:
+        s = order[k % len(order)]
+        k += 1
         a, b = int(op.cu_seqlens_q[s]), int(op.cu_seqlens_q[s + 1])
         cu_q = np.array([0, b - a]); cu_k = np.array([0, int(op.cu_seqlens_k[s + 1] - op.cu_seqlens_k[s])])
         t0 = time.perf_counter()
@@ -230,33 +228,45 @@ def cpu_baseline_prefill(wl, op, budget_s: float = 20.0):
         n += 1
     return {"value": round(flops / t_used / 1e12, 6), "unit": "TFLOP/s", "cores": cpu_threads(),
             "kind": "oracle",
-            "sample": f"fp64 numpy oracle prefill of the {n} shortest of {len(lens)} sequences "
+            "sample": f"fp64 numpy oracle prefill of {n} sequences, shortest first (the batch of "
+                      f"{len(lens)}, repeated) "
                       f"({flops / 1e9:.1f} GFLOP algorithmic, {t_used:.1f} s)"}
 
 
 # ----------------------------------------------------------------------------- traffic (PMC)
 
 
-def read_traffic(kernel_tag: str):
-    """HBM bytes per launch from a committed counter summary, if it still matches the source."""
+def source_digest(names) -> str:
+    """First 16 hex digits of the sha256 over the named csrc files (in order)."""
     import hashlib
+    h = hashlib.sha256()
+    for name in names:
+        with open(os.path.join(ROOT, "paged_attention_block_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel_tag: str):
+    """HBM bytes per launch from a committed counter summary, if it still matches the sources.
+
+    ``profiles/<tag>_traffic.txt`` holds ``key = value`` lines: ``sources`` (csrc files the
+    kernels are built from), ``source_sha256_16`` (their digest when the counters were taken)
+    and ``hbm_bytes_per_launch``.  Returns None when the file is missing or the sources changed.
+    """
     path = os.path.join(ROOT, "profiles", f"{kernel_tag}_traffic.txt")
     if not os.path.exists(path):
         return None
     kv = {}
     for line in open(path):
-        if "=" in line and not line.startswith("#"):
+        if "=" in line and not line.lstrip().startswith("#"):
             k, v = line.split("=", 1)
             kv[k.strip()] = v.strip()
-    src = os.path.join(ROOT, "paged_attention_block_amd", "csrc", kv.get("source", ""))
-    if not os.path.exists(src):
-        return None
-    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-    if digest != kv.get("source_sha256_16"):
-        return None
     try:
+        names = kv["sources"].split()
+        if source_digest(names) != kv.get("source_sha256_16"):
+            return None
         return float(kv["hbm_bytes_per_launch"])
-    except (KeyError, ValueError):
+    except (KeyError, ValueError, OSError):
         return None
 
 
@@ -320,6 +330,9 @@ def main() -> int:
     ap.add_argument("--workload", default="decode", choices=sorted(WORKLOAD_CONFIG))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--partition-size", type=int, default=0, help="decode split-K keys per item (0 = auto)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
+                    help="only run a plain device-to-device copy of MB megabytes (3 times): the "
+                         "reference kernel for scaling HBM byte counters")
     ap.add_argument("--no-prefill", action="store_true", help="skip the secondary prefill measurement")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -329,6 +342,15 @@ def main() -> int:
 
     import torch
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        n = args.copy_calibration * 1000 * 1000
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
+        return 0
     with_cpu = not args.no_cpu_baseline
     main_res = bench_workload(args.workload, args.steps, args.warmup, dev, with_cpu, args.partition_size)
     line = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
