@@ -120,8 +120,7 @@ class Step:
             elif name == "DecodeOp":
                 d.update(q=op.query.to(dev), table=i32(op.block_table), lens=i32(op.seq_lens))
                 d["out"] = torch.empty_like(d["q"])
-                d["part"] = partition_size or pa.pa_decode_partition_size(
-                    self.cache, len(op.seq_lens), wl.num_heads, op.max_seq_len, wl.sliding_window)
+                d["part"] = partition_size
                 need = pa.pa_decode_workspace_size(self.cache, len(op.seq_lens), wl.num_heads,
                                                    op.max_seq_len, wl.sliding_window, d["part"])
                 d["ws"] = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
@@ -294,7 +293,7 @@ def bench_workload(name, steps, warmup, dev, with_cpu, partition_size=0):
             total_bytes += b
             res["ops"]["decode"] = {"ms": round(t * 1e3, 4), "GB/s": round(b / t / 1e9, 1),
                                     "bytes": b, "tokens_per_s": round(len(op.seq_lens) / t, 1),
-                                    "partition_size": step.prepared[ops.index(op)]["part"],
+                                    "partition_size": step.prepared[ops.index(op)]["part"] or "auto",
                                     "roofline": roofline(b / t / 1e9, HBM_PEAK_GBS, "GB/s", "hbm",
                                                          read_traffic("decode"))}
         elif n == "PrefillOp":
@@ -329,7 +328,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode", choices=sorted(WORKLOAD_CONFIG))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--partition-size", type=int, default=0, help="decode split-K keys per item (0 = auto)")
+    ap.add_argument("--partition-size", type=int, default=0, help="decode split-K: fewest keys per chunk (0 = auto: one chunk per resident workgroup)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
                     help="only run a plain device-to-device copy of MB megabytes (3 times): the "
                          "reference kernel for scaling HBM byte counters")

@@ -117,16 +117,10 @@ int pa_prefill_varlen(const pa_cache_desc* cache, void* out, const void* query,
                       int32_t num_heads, float scale, int32_t sliding_window, void* stream);
 
 /*
- * pa_decode_partition_size — the split-K partition (keys per work item) pa_decode uses for
- * these sizes when called with partition_size = 0.  Always a multiple of 64.
- */
-int32_t pa_decode_partition_size(const pa_cache_desc* cache, int32_t num_seqs,
-                                 int32_t num_heads, int32_t max_seq_len,
-                                 int32_t sliding_window);
-
-/*
- * pa_decode_workspace_size — bytes of device workspace pa_decode needs (0 when every
- * sequence fits one partition).  partition_size 0 = the automatic choice.
+ * pa_decode_workspace_size — bytes of device workspace pa_decode needs for these sizes
+ * (0 when the batch is too small to be split, and for float32 caches).  With
+ * partition_size 0 the size depends on how many decode workgroups the current device
+ * holds at once; query it on the device that runs the decode.
  */
 size_t pa_decode_workspace_size(const pa_cache_desc* cache, int32_t num_seqs,
                                 int32_t num_heads, int32_t max_seq_len,
@@ -140,9 +134,11 @@ size_t pa_decode_workspace_size(const pa_cache_desc* cache, int32_t num_seqs,
  * (split-KV for long-context decode).  Sequence s attends keys [lo, n) with
  * n = seq_lens[s] (the keys stored so far, the new token's included) and
  * lo = max(0, n - sliding_window) when sliding_window > 0, else 0: the seqlen_q = 1 case
- * of pa_prefill_varlen.  The key range is cut into partitions of partition_size keys
- * (0 = automatic; otherwise a multiple of 64), each reduced to a partial softmax state in
- * the workspace and merged with a log-sum-exp rescale.
+ * of pa_prefill_varlen.  The 32-key steps of all sequences, in order, are cut into equal
+ * chunks, one per workgroup; a sequence cut by chunk boundaries leaves a partial softmax
+ * state per piece in the workspace, merged afterwards with a log-sum-exp rescale.
+ * partition_size 0 = automatic (as many chunks as the device runs at once, of at least
+ * 256 keys); otherwise a multiple of 32: chunks of at least that many keys.
  *
  *   out, query   [num_seqs][num_heads][head_size], contiguous, cache dtype
  *   block_table  [num_seqs][max_blocks_per_seq] int32

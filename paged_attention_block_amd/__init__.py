@@ -12,6 +12,7 @@ float32, contiguous); plane 0 keys, plane 1 values.  Index tensors are int32.
 
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 from typing import Optional
@@ -20,7 +21,7 @@ import torch
 
 __all__ = [
     "PaError", "lib_path", "load", "pa_store_kv", "pa_copy_blocks", "pa_prefill_varlen",
-    "pa_decode", "pa_decode_workspace_size", "pa_decode_partition_size",
+    "pa_decode", "pa_decode_workspace_size",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -66,8 +67,6 @@ def load() -> ctypes.CDLL:
     lib.pa_store_kv.argtypes = [D, P, P, P, I32, P]
     lib.pa_copy_blocks.argtypes = [D, P, I32, P]
     lib.pa_prefill_varlen.argtypes = [D, P, P, P, I32, P, P, I32, I32, I32, I32, F32, I32, P]
-    lib.pa_decode_partition_size.argtypes = [D, I32, I32, I32, I32]
-    lib.pa_decode_partition_size.restype = I32
     lib.pa_decode_workspace_size.argtypes = [D, I32, I32, I32, I32, I32]
     lib.pa_decode_workspace_size.restype = SZ
     lib.pa_decode.argtypes = [D, P, P, P, I32, P, I32, I32, I32, F32, I32, I32, P, SZ, P]
@@ -184,16 +183,18 @@ def pa_prefill_varlen(query: torch.Tensor, kv_cache: torch.Tensor, block_table: 
     return out
 
 
-def pa_decode_partition_size(kv_cache: torch.Tensor, num_seqs: int, num_heads: int,
-                             max_seq_len: int, sliding_window: int = 0) -> int:
-    return int(load().pa_decode_partition_size(ctypes.byref(_desc(kv_cache)), num_seqs, num_heads,
-                                                max_seq_len, sliding_window))
-
-
 def pa_decode_workspace_size(kv_cache: torch.Tensor, num_seqs: int, num_heads: int, max_seq_len: int,
                              sliding_window: int = 0, partition_size: int = 0) -> int:
-    return int(load().pa_decode_workspace_size(ctypes.byref(_desc(kv_cache)), num_seqs, num_heads,
-                                                max_seq_len, sliding_window, partition_size))
+    """Workspace bytes ``pa_decode`` needs; asked on the cache's device (the automatic
+    split depends on how many workgroups that device holds at once)."""
+    lib = load()
+    desc = _desc(kv_cache)
+    if kv_cache.is_cuda:
+        with torch.cuda.device(kv_cache.device):
+            return int(lib.pa_decode_workspace_size(ctypes.byref(desc), num_seqs, num_heads,
+                                                    max_seq_len, sliding_window, partition_size))
+    return int(lib.pa_decode_workspace_size(ctypes.byref(desc), num_seqs, num_heads, max_seq_len,
+                                            sliding_window, partition_size))
 
 
 def pa_decode(query: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
@@ -231,8 +232,9 @@ def pa_decode(query: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Te
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if workspace is not None and workspace.device != dev:
         raise ValueError("workspace must be on the cache's device")
-    _check(lib.pa_decode(ctypes.byref(desc), _ptr(out), _ptr(query), _ptr(block_table),
-                         block_table.shape[1], _ptr(seq_lens), num_seqs, int(max_seq_len),
-                         query.shape[1], float(scale), int(sliding_window), int(partition_size),
-                         _ptr(workspace), ws_bytes, _stream(kv_cache)), "pa_decode")
+    with (torch.cuda.device(dev) if dev.type == "cuda" else contextlib.nullcontext()):
+        _check(lib.pa_decode(ctypes.byref(desc), _ptr(out), _ptr(query), _ptr(block_table),
+                             block_table.shape[1], _ptr(seq_lens), num_seqs, int(max_seq_len),
+                             query.shape[1], float(scale), int(sliding_window), int(partition_size),
+                             _ptr(workspace), ws_bytes, _stream(kv_cache)), "pa_decode")
     return out

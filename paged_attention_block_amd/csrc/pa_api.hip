@@ -7,15 +7,8 @@
 #include <stdio.h>
 #include <string.h>
 
-#include "../../include/pa.h"
+#include "pa.h"
 #include "pa_internal.hpp"
-
-namespace pa {
-hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);
-hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s);
-hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s);
-hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t s);
-}  // namespace pa
 
 namespace {
 
@@ -83,19 +76,38 @@ int launch_status(hipError_t e) {
     return PA_OK;
 }
 
-// Split-K partition size.  Measured on MI355X: long partitions stream best (the start of
-// each one pays a full memory latency), so aim for about 2048 (sequence, KV head,
-// partition) items -- 2 per SIMD at the longest sequence -- within [128, 2048] keys.
-int32_t auto_part(int32_t num_seqs, int32_t num_kv_heads, int32_t max_keys) {
-    const int64_t items_target = 2048;
-    const int64_t total = (int64_t)num_seqs * num_kv_heads * max_keys;
-    int64_t part = 128;
-    while (part < 2048 && total / part > items_target) part *= 2;
-    return (int32_t)part;
+// Chunks of the decode step list per group of 8 KV heads.  Automatic: as many as the
+// device holds at once (every chunk then runs in one wave of workgroups and they finish
+// together), each of at least 8 steps (256 keys) so short batches are not cut into pieces
+// that cost more to merge than to stream.  partition_size > 0: chunks of at least that
+// many keys, as many as a batch of max_seq_len sequences needs (tests use small ones to
+// cut sequences many times).
+struct Chunks {
+    int32_t nw;
+    int32_t min_steps;
+};
+Chunks decode_chunks(int32_t num_seqs, int32_t head_size, int32_t num_kv_heads, int32_t max_keys,
+                     int32_t partition_size) {
+    Chunks c;
+    const int32_t ygroups = (num_kv_heads + 7) / 8;
+    if (partition_size > 0) {
+        c.min_steps = partition_size / 32;
+        const int64_t smax = (int64_t)num_seqs * ((max_keys + 31) / 32);
+        const int64_t nw = (smax + c.min_steps - 1) / c.min_steps;
+        c.nw = (int32_t)(nw < 1 ? 1 : (nw > (1 << 24) ? (1 << 24) : nw));
+    } else {
+        c.min_steps = 8;
+        const int64_t smax = (int64_t)num_seqs * ((max_keys + 31) / 32);
+        const int64_t use = (smax + c.min_steps - 1) / c.min_steps;
+        int32_t nw = pa::decode_resident_slots(head_size, num_kv_heads) / ygroups;
+        if (nw > use) nw = (int32_t)use;
+        c.nw = nw < 1 ? 1 : nw;
+    }
+    return c;
 }
 
-// Largest key span a partitioned sequence covers: its live keys [lo, n) plus the < 32 keys
-// between lo and the 32-aligned start of its first partition.
+// Largest key span a sequence's steps cover: its live keys [lo, n) plus the < 32 keys
+// between lo and the 32-aligned start of its first step.
 int32_t max_keys_of(int32_t max_seq_len, int32_t window) {
     if (window > 0 && max_seq_len > window) return max_seq_len < window + 31 ? max_seq_len : window + 31;
     return max_seq_len;
@@ -184,24 +196,15 @@ int pa_prefill_varlen(const pa_cache_desc* cache, void* out, const void* query,
     return launch_status(a.c.dtype == PA_BF16 ? pa::launch_prefill_bf16(a, s) : pa::launch_prefill_f32(a, s));
 }
 
-int32_t pa_decode_partition_size(const pa_cache_desc* cache, int32_t num_seqs, int32_t num_heads,
-                                 int32_t max_seq_len, int32_t sliding_window) {
-    (void)num_heads;
-    const int32_t hkv = (cache && cache->num_kv_heads > 0) ? cache->num_kv_heads : 1;
-    return auto_part(num_seqs > 0 ? num_seqs : 1, hkv,
-                     max_keys_of(max_seq_len > 0 ? max_seq_len : 1, sliding_window));
-}
-
 size_t pa_decode_workspace_size(const pa_cache_desc* cache, int32_t num_seqs, int32_t num_heads,
                                 int32_t max_seq_len, int32_t sliding_window, int32_t partition_size) {
-    if (!cache || num_seqs <= 0 || num_heads <= 0 || max_seq_len <= 0) return 0;
+    if (!cache || num_seqs <= 0 || num_heads <= 0 || max_seq_len <= 0 || partition_size < 0) return 0;
     if (cache->dtype != PA_BF16) return 0;  // the float32 path needs no workspace
-    const int32_t part = partition_size > 0
-                             ? partition_size
-                             : pa_decode_partition_size(cache, num_seqs, num_heads, max_seq_len, sliding_window);
-    const int32_t parts = (max_keys_of(max_seq_len, sliding_window) + part - 1) / part;
-    if (parts <= 1) return 0;
-    return (size_t)num_seqs * num_heads * parts * ((size_t)cache->head_size + 2) * sizeof(float);
+    const Chunks c = decode_chunks(num_seqs, cache->head_size, cache->num_kv_heads,
+                                   max_keys_of(max_seq_len, sliding_window > 0 ? sliding_window : 0),
+                                   partition_size);
+    if (c.nw <= 1) return 0;
+    return (size_t)c.nw * 2 * num_heads * ((size_t)cache->head_size + 2) * sizeof(float);
 }
 
 int pa_decode(const pa_cache_desc* cache, void* out, const void* query, const int32_t* block_table,
@@ -220,10 +223,12 @@ int pa_decode(const pa_cache_desc* cache, void* out, const void* query, const in
     if (max_blocks_per_seq < 1) return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq must be >= 1");
     if ((int64_t)max_seq_len > (int64_t)max_blocks_per_seq * a.c.block_size)
         return fail(PA_ERR_INVALID_ARG, "max_seq_len %d exceeds max_blocks_per_seq * block_size", max_seq_len);
-    if (partition_size < 0 || partition_size % 64 != 0)
-        return fail(PA_ERR_INVALID_ARG, "partition_size must be 0 or a positive multiple of 64 (got %d)", partition_size);
+    if (partition_size < 0 || partition_size % 32 != 0)
+        return fail(PA_ERR_INVALID_ARG, "partition_size must be 0 or a positive multiple of 32 (got %d)", partition_size);
     if (!(scale == scale)) return fail(PA_ERR_INVALID_ARG, "scale is NaN");
-    if (num_seqs > 0x7fffffff / 64) return fail(PA_ERR_INVALID_ARG, "num_seqs too large");
+    const int32_t win = sliding_window > 0 ? sliding_window : 0;
+    if ((int64_t)num_seqs * ((max_keys_of(max_seq_len, win) + 31) / 32 + 1) > 0x7fffffff)
+        return fail(PA_ERR_INVALID_ARG, "num_seqs * max_seq_len too large");
     a.out = out;
     a.q = query;
     a.table = block_table;
@@ -235,24 +240,23 @@ int pa_decode(const pa_cache_desc* cache, void* out, const void* query, const in
     a.scale = scale;
     a.window = sliding_window > 0 ? sliding_window : 0;
     hipStream_t s = (hipStream_t)stream;
-    if (a.c.dtype == PA_F32) {
-        a.part = 0;
-        a.max_parts = 1;
-        a.ws_o = nullptr;
-        a.ws_ml = nullptr;
-        return launch_status(pa::launch_decode_f32(a, s));
-    }
-    const int32_t mkeys = max_keys_of(max_seq_len > 0 ? max_seq_len : 1, a.window);
-    a.part = partition_size > 0 ? partition_size : auto_part(num_seqs, a.c.num_kv_heads, mkeys);
-    a.max_parts = (mkeys + a.part - 1) / a.part;
-    if (a.max_parts < 1) a.max_parts = 1;
-    if (a.max_parts > 65535) return fail(PA_ERR_INVALID_ARG, "too many partitions; raise partition_size");
+    a.nw = 1;
+    a.min_steps = 1;
+    a.ws_o = nullptr;
+    a.ws_ml = nullptr;
+    if (a.c.dtype == PA_F32) return launch_status(pa::launch_decode_f32(a, s));
     if (a.c.num_kv_heads > 65535) return fail(PA_ERR_INVALID_ARG, "num_kv_heads too large");
-    const size_t need = pa_decode_workspace_size(cache, num_seqs, num_heads, max_seq_len, sliding_window, a.part);
+    const size_t need = pa_decode_workspace_size(cache, num_seqs, num_heads, max_seq_len, sliding_window, partition_size);
     if (need > 0 && (!workspace || workspace_bytes < need))
         return fail(PA_ERR_WORKSPACE, "decode needs %zu workspace bytes, got %zu", need, workspace ? workspace_bytes : 0);
-    a.ws_o = (float*)workspace;
-    a.ws_ml = need > 0 ? (float*)workspace + (size_t)num_seqs * num_heads * a.max_parts * a.c.head_size : nullptr;
+    if (need > 0) {
+        const Chunks c = decode_chunks(num_seqs, a.c.head_size, a.c.num_kv_heads, max_keys_of(max_seq_len, win),
+                                       partition_size);
+        a.nw = c.nw;
+        a.min_steps = c.min_steps;
+        a.ws_o = (float*)workspace;
+        a.ws_ml = a.ws_o + (size_t)c.nw * 2 * num_heads * a.c.head_size;
+    }
     return launch_status(pa::launch_decode_bf16(a, s));
 }
 

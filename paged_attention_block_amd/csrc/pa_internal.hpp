@@ -14,6 +14,22 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
+// Reductions over the four lanes l, l^16, l^32, l^48 (the four 16-lane groups), with the
+// register-only lane swaps of gfx950: permlane16_swap(v, v) yields v of lanes l and l^16
+// (in some order), permlane32_swap(v, v) those of l and l^32.
+__device__ inline float group4_max(float v) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, v), __builtin_bit_cast(unsigned, v), false, false);
+    v = fmaxf(__builtin_bit_cast(float, (unsigned)a[0]), __builtin_bit_cast(float, (unsigned)a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, v), __builtin_bit_cast(unsigned, v), false, false);
+    return fmaxf(__builtin_bit_cast(float, (unsigned)b[0]), __builtin_bit_cast(float, (unsigned)b[1]));
+}
+__device__ inline float group4_sum(float v) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, v), __builtin_bit_cast(unsigned, v), false, false);
+    v = __builtin_bit_cast(float, (unsigned)a[0]) + __builtin_bit_cast(float, (unsigned)a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, v), __builtin_bit_cast(unsigned, v), false, false);
+    return __builtin_bit_cast(float, (unsigned)b[0]) + __builtin_bit_cast(float, (unsigned)b[1]);
+}
+
 // Two floats -> packed bf16 pair (round to nearest even), one v_cvt_pk_bf16_f32.
 __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
@@ -22,17 +38,16 @@ __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
 // Lanes of one wavefront.
 constexpr int kWave = 64;
 
-// Split-K bookkeeping for decode.  A sequence with n keys and window lower bound lo is cut
-// into partitions of `part` keys (a multiple of 64) starting at lo rounded down to 32, so
-// every 32-key step is aligned in absolute key index.
+// Split-K bookkeeping for decode.  Sequence s with n keys attends [lo, n); its keys are
+// walked in 32-key steps from lo rounded down to 32, so every step is aligned in absolute
+// key index.  The steps of the whole batch, sequence after sequence, form one list that is
+// cut into equal chunks, one per partition workgroup.
 __host__ __device__ inline int decode_base(int lo) { return lo & ~31; }
 __host__ __device__ inline int decode_lo(int n, int window) {
     return (window > 0 && n > window) ? n - window : 0;
 }
-__host__ __device__ inline int decode_num_parts(int n, int window, int part) {
-    if (n <= 0) return 0;
-    int base = decode_base(decode_lo(n, window));
-    return (n - base + part - 1) / part;
+__host__ __device__ inline int decode_steps(int n, int window) {
+    return n > 0 ? (n - decode_base(decode_lo(n, window)) + 31) >> 5 : 0;
 }
 
 // ---------------------------------------------------------------- launch parameter blocks
@@ -89,16 +104,21 @@ struct DecodeArgs {
     int32_t group;
     float scale;
     int32_t window;
-    int32_t part;        // keys per partition (multiple of 64)
-    int32_t max_parts;   // partitions per sequence the workspace holds
-    float* ws_o;         // [B][H][max_parts][D] unnormalised partial outputs
-    float* ws_ml;        // [B][H][max_parts][2] running max (log2 units) and sum
+    int32_t nw;          // chunk workgroups per group of 8 KV heads (grid x)
+    int32_t min_steps;   // fewest 32-key steps per chunk
+    float* ws_o;         // [nw][2][H][D] unnormalised partial outputs (first, last segment)
+    float* ws_ml;        // [nw][2][H][2] running max (log2 units) and sum
 };
 
 // Host launchers (return hipGetLastError() of the launches).
 hipError_t launch_store(const StoreArgs& a, hipStream_t s);
 hipError_t launch_copy_blocks(const CopyArgs& a, hipStream_t s);
-hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);
+hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s);
+hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t s);
+// Partition workgroups of the bf16 decode kernel that fit on the current device at once
+// (compute units x resident workgroups per unit); 256 when the device cannot be queried.
+int decode_resident_slots(int head_size, int num_kv_heads);
 
 }  // namespace pa

@@ -63,7 +63,12 @@ __global__ __launch_bounds__(512) void prefill_bf16_kernel(const PrefillArgs a, 
     constexpr int KSW = CPR >= 16 ? 15 : CPR - 1;        // K swizzle mask
     constexpr int VSW = CPR >= 16 ? 14 : CPR - 2;        // V swizzle mask (even values)
 
-    __shared__ __attribute__((aligned(1024))) char lds[2][2][TILE];  // [buffer][plane]
+    // two K and two V buffers as distinct objects, so the compiler can tell a copy into one
+    // from a read of another and does not wait for in-flight copies before every LDS read
+    __shared__ __attribute__((aligned(1024))) char lds_k0[TILE];
+    __shared__ __attribute__((aligned(1024))) char lds_k1[TILE];
+    __shared__ __attribute__((aligned(1024))) char lds_v0[TILE];
+    __shared__ __attribute__((aligned(1024))) char lds_v1[TILE];
 
     // ---------------------------------------------------------------- work item
     const int b = blockIdx.x;
@@ -146,30 +151,26 @@ __global__ __launch_bounds__(512) void prefill_bf16_kernel(const PrefillArgs a, 
     float l_run[2] = {0.f, 0.f};
 
     // ---------------------------------------------------------------- tile copies
-    // Copy instruction q (0 .. 2*NQ-1; plane q / NQ) fills LDS bytes [1024*qq, +1024) of its
-    // plane, qq = q % NQ: rows RPI*qq + lane / CPR, slot lane % CPR.  Wave w issues
-    // q = w, w + nwaves, ...  The lane offsets relative to the first token row of the row's
-    // 16-key group are the same for every tile.
+    // A plane of a tile is NQ copy instructions of 1 KB: instruction q fills LDS bytes
+    // [1024*q, +1024): rows RPI*q + lane / CPR, slot lane % CPR.  Wave w issues q = w,
+    // w + nwaves, ...  The lane offsets relative to the first token row of the row's 16-key
+    // group are the same for every tile.
     const int crow = lane / CPR;           // row within the instruction's rows
     const int cslot = lane % CPR;          // LDS chunk slot within the row
-    auto lane_goff = [&](int q) -> uint32_t {
-        const bool isv = q >= NQ;
-        const int row = RPI * (isv ? q - NQ : q) + crow;
-        const int chunk = cslot ^ (isv ? (2 * row) & VSW : row & KSW);
-        return (uint32_t)((((row & 15) * Hkv + g) * D + chunk * 8) * 2);
-    };
-
-    // this wave's copies: q = wave + nwaves*i (at most CPW of them, >= 4 waves per
-    // workgroup); lane offsets computed once
-    constexpr int CPW = (2 * NQ + 3) / 4;
-    uint32_t cgoff[CPW];
+    constexpr int CPW = (NQ + 3) / 4;      // copies per wave and plane (>= 4 waves)
+    uint32_t cgk[CPW], cgv[CPW];
 #pragma unroll
     for (int i = 0; i < CPW; ++i) {
         const int q = wave + nwaves * i;
-        cgoff[i] = q < 2 * NQ ? lane_goff(q) : 0u;
+        const int row = RPI * q + crow;
+        const int ck = cslot ^ (row & KSW);
+        const int cv = cslot ^ ((2 * row) & VSW);
+        cgk[i] = q < NQ ? (uint32_t)((((row & 15) * Hkv + g) * D + ck * 8) * 2) : 0u;
+        cgv[i] = q < NQ ? (uint32_t)((((row & 15) * Hkv + g) * D + cv * 8) * 2) : 0u;
     }
 
-    auto issue = [&](int k0, int buf) {
+    // copy one plane of the tile at k0 into LDS buffer dst
+    auto issue = [&](int k0, const char* plane, const uint32_t (&cg)[CPW], char* dst) {
         int64_t gb[4];
         bool gv[4];
 #pragma unroll
@@ -186,58 +187,43 @@ __global__ __launch_bounds__(512) void prefill_bf16_kernel(const PrefillArgs a, 
 #pragma unroll
         for (int i = 0; i < CPW; ++i) {
             const int q = wave + nwaves * i;
-            if (q < 2 * NQ) {
-                const bool isv = q >= NQ;
-                const int qq = isv ? q - NQ : q;
-                const int ga = (RPI * qq) >> 4;
+            if (q < NQ) {
+                const int ga = (RPI * q) >> 4;
                 const int64_t base = ga == 0 ? gb[0] : ga == 1 ? gb[1] : ga == 2 ? gb[2] : gb[3];
-                const char* src = kplane + (isv ? vdelta + base : base) + cgoff[i];
-                __builtin_amdgcn_global_load_lds(
-                    (const void*)src, (__attribute__((address_space(3))) void*)(lds[buf][isv ? 1 : 0] + 1024 * qq), 16, 0, 0);
+                __builtin_amdgcn_global_load_lds((const void*)(plane + base + cg[i]),
+                                                 (__attribute__((address_space(3))) void*)(dst + 1024 * q), 16, 0, 0);
             }
         }
     };
-    // after this wave's copies of the tile at k0 landed: zero the rows it copied whose key
-    // lies outside [wg_lo, wg_hi]
-    auto zero_dead = [&](int k0, int buf) {
+    // after this wave's copies of a plane of the tile at k0 landed: zero the rows it copied
+    // whose key lies outside [wg_lo, wg_hi]
+    auto zero_dead = [&](int k0, char* dst) {
         if (k0 >= wg_lo && k0 + BN - 1 <= wg_hi) return;
 #pragma unroll
         for (int i = 0; i < CPW; ++i) {
             const int q = wave + nwaves * i;
-            if (q < 2 * NQ) {
-                const bool isv = q >= NQ;
-                const int qq = isv ? q - NQ : q;
-                const int key = k0 + RPI * qq + crow;
-                if (key < wg_lo || key > wg_hi)
-                    *(u32x4*)(lds[buf][isv ? 1 : 0] + 1024 * qq + 16 * lane) = (u32x4)(0u);
+            if (q < NQ) {
+                const int key = k0 + RPI * q + crow;
+                if (key < wg_lo || key > wg_hi) *(u32x4*)(dst + 1024 * q + 16 * lane) = (u32x4)(0u);
             }
         }
     };
+    const char* vplane = kplane + vdelta;
 
-    // LDS operand addresses of this lane
-    uint32_t koff[4][KS];  // [16-key group][k-slice]
+    // LDS operand addresses of this lane: K row 16*ga + col, chunk (4t + grp) swizzled by
+    // the row, and (16*ga + col) & KSW == col & KSW, so only the 16*ga row offset depends on ga
+    uint32_t koff[KS];
 #pragma unroll
-    for (int ga = 0; ga < 4; ++ga)
-#pragma unroll
-        for (int t = 0; t < KS; ++t) {
-            const int row = 16 * ga + col;
-            koff[ga][t] = (uint32_t)(row * D * 2 + (((4 * t + grp) ^ (row & KSW)) * 16));
-        }
+    for (int t = 0; t < KS; ++t) koff[t] = (uint32_t)(col * D * 2 + (((4 * t + grp) ^ (col & KSW)) * 16));
     // V^T: source lane col of group grp addresses row 32cc + 16hh + 4*grp + col/4, dims
     // 16*db + 4*(col%4) .. +4; the row's swizzle depends on (row & 7) = (4*grp + col/4) & 7
     const int vrow0 = 4 * grp + (col >> 2);
     const int vsw = (2 * vrow0) & VSW;
-    uint32_t voff_base = (uint32_t)(vrow0 * D * 2 + 8 * (col & 1));
+    const uint32_t voff_base = (uint32_t)(vrow0 * D * 2 + 8 * (col & 1));
     const int vch = (col & 3) >> 1;  // chunk within the 16-dim block
 
-    // ---------------------------------------------------------------- one tile of math
-    auto compute_tile = [&](int buf, int k0) {
-        if (!wave_active || k0 > wv_hi || k0 + BN - 1 < wv_lo) return;
-        const bool edge = (k0 + BN - 1 > wv_p_min) || (W > 0 && k0 < wv_lo_max);
-        const char* kt = lds[buf][0];
-        const char* vt = lds[buf][1];
-
-        f32x4 sacc[4][2];
+    // S^T of the tile whose K sits at kbuf
+    auto qk = [&](const char* kt, f32x4 (&sacc)[4][2]) {
 #pragma unroll
         for (int ga = 0; ga < 4; ++ga)
 #pragma unroll
@@ -246,12 +232,17 @@ __global__ __launch_bounds__(512) void prefill_bf16_kernel(const PrefillArgs a, 
         for (int t = 0; t < KS; ++t) {
 #pragma unroll
             for (int ga = 0; ga < 4; ++ga) {
-                const bf16x8 kf = *(const bf16x8*)(kt + koff[ga][t]);
+                const bf16x8 kf = *(const bf16x8*)(kt + koff[t] + 16 * ga * D * 2);
 #pragma unroll
                 for (int nb = 0; nb < 2; ++nb)
                     sacc[ga][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[nb][t], sacc[ga][nb], 0, 0, 0);
             }
         }
+    };
+
+    // mask, online softmax, P^T pack; returns whether O needs rescaling
+    auto softmax = [&](int k0, f32x4 (&sacc)[4][2], u32x4 (&pk)[2][2], float (&alpha)[2]) {
+        const bool edge = (k0 + BN - 1 > wv_p_min) || (W > 0 && k0 < wv_lo_max);
         if (edge) {
 #pragma unroll
             for (int ga = 0; ga < 4; ++ga)
@@ -263,16 +254,13 @@ __global__ __launch_bounds__(512) void prefill_bf16_kernel(const PrefillArgs a, 
                         sacc[ga][nb][r] = (key > prow[nb] || key < plo[nb]) ? -INFINITY : sacc[ga][nb][r];
                 }
         }
-        u32x4 pk[2][2];  // [32-key chunk][nb]
-        float alpha[2];
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
             float mx = fmaxf(fmaxf(sacc[0][nb][0], sacc[0][nb][1]), fmaxf(sacc[0][nb][2], sacc[0][nb][3]));
 #pragma unroll
             for (int ga = 1; ga < 4; ++ga)
                 mx = fmaxf(mx, fmaxf(fmaxf(sacc[ga][nb][0], sacc[ga][nb][1]), fmaxf(sacc[ga][nb][2], sacc[ga][nb][3])));
-            mx = fmaxf(mx, __shfl_xor(mx, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            mx = group4_max(mx);
             const float m_new = fmaxf(m_run[nb], mx * c_log2);
             const float msub = m_new == -INFINITY ? 0.f : m_new;
             alpha[nb] = __builtin_amdgcn_exp2f(m_run[nb] - msub);
@@ -282,6 +270,10 @@ __global__ __launch_bounds__(512) void prefill_bf16_kernel(const PrefillArgs a, 
             for (int ga = 0; ga < 4; ++ga)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) pv[ga][r] = __builtin_amdgcn_exp2f(fmaf(sacc[ga][nb][r], c_log2, -msub));
+            float ps[4];
+#pragma unroll
+            for (int ga = 0; ga < 4; ++ga) ps[ga] = (pv[ga][0] + pv[ga][1]) + (pv[ga][2] + pv[ga][3]);
+            l_run[nb] = l_run[nb] * alpha[nb] + ((ps[0] + ps[1]) + (ps[2] + ps[3]));
 #pragma unroll
             for (int cc = 0; cc < 2; ++cc) {
                 pk[cc][nb][0] = pack_bf16x2(pv[2 * cc][0], pv[2 * cc][1]);
@@ -289,11 +281,10 @@ __global__ __launch_bounds__(512) void prefill_bf16_kernel(const PrefillArgs a, 
                 pk[cc][nb][2] = pack_bf16x2(pv[2 * cc + 1][0], pv[2 * cc + 1][1]);
                 pk[cc][nb][3] = pack_bf16x2(pv[2 * cc + 1][2], pv[2 * cc + 1][3]);
             }
-            float ps[4];
-#pragma unroll
-            for (int ga = 0; ga < 4; ++ga) ps[ga] = (pv[ga][0] + pv[ga][1]) + (pv[ga][2] + pv[ga][3]);
-            l_run[nb] = l_run[nb] * alpha[nb] + ((ps[0] + ps[1]) + (ps[2] + ps[3]));
         }
+    };
+
+    auto pv_mfma = [&](const char* vt, const u32x4 (&pk)[2][2], const float (&alpha)[2]) {
         if (__any(alpha[0] != 1.f || alpha[1] != 1.f)) {
 #pragma unroll
             for (int d = 0; d < DB; ++d)
@@ -302,6 +293,7 @@ __global__ __launch_bounds__(512) void prefill_bf16_kernel(const PrefillArgs a, 
         }
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc) {
+            bf16x8 vf[DB];
 #pragma unroll
             for (int d = 0; d < DB; ++d) {
                 s16x4 vh[2];
@@ -311,27 +303,47 @@ __global__ __launch_bounds__(512) void prefill_bf16_kernel(const PrefillArgs a, 
                     const uint32_t o = voff_base + rowoff + (((2 * d + vch) ^ vsw) * 16);
                     vh[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)((__attribute__((address_space(3))) char*)vt + o));
                 }
-                const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(vh[0], vh[1], 0, 1, 2, 3, 4, 5, 6, 7));
+                vf[d] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(vh[0], vh[1], 0, 1, 2, 3, 4, 5, 6, 7));
+            }
+#pragma unroll
+            for (int d = 0; d < DB; ++d)
 #pragma unroll
                 for (int nb = 0; nb < 2; ++nb)
                     oacc[d][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        vf, __builtin_bit_cast(bf16x8, pk[cc][nb]), oacc[d][nb], 0, 0, 0);
-            }
+                        vf[d], __builtin_bit_cast(bf16x8, pk[cc][nb]), oacc[d][nb], 0, 0, 0);
         }
     };
 
     // ---------------------------------------------------------------- main loop
+    // K/V of tile kt+1 are copied into the other buffer pair while tile kt computes; the
+    // loop body is written out twice so each half names fixed buffers.
+    auto step = [&](int kt, int kt_end, char* kc, char* vc, char* kn, char* vn) {
+        const int k0 = kt * BN;
+        __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): this wave's copies of tile kt landed
+        zero_dead(k0, kc);
+        zero_dead(k0, vc);
+        __syncthreads();                     // all copies of tile kt visible; kn/vn free
+        if (kt + 1 < kt_end) {
+            issue(k0 + BN, kplane, cgk, kn);
+            issue(k0 + BN, vplane, cgv, vn);
+        }
+        if (wave_active && k0 <= wv_hi && k0 + BN - 1 >= wv_lo) {
+            f32x4 sacc[4][2];
+            u32x4 pk[2][2];
+            float alpha[2];
+            qk(kc, sacc);
+            softmax(k0, sacc, pk, alpha);
+            pv_mfma(vc, pk, alpha);
+        }
+    };
     if (wg_hi >= wg_lo) {
         const int kt_begin = wg_lo / BN;
         const int kt_end = wg_hi / BN + 1;
-        issue(kt_begin * BN, 0);
-        for (int kt = kt_begin; kt < kt_end; ++kt) {
-            const int buf = (kt - kt_begin) & 1;
-            __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): this wave's copies landed
-            zero_dead(kt * BN, buf);
-            __syncthreads();                     // all copies of tile kt visible; buf^1 free
-            if (kt + 1 < kt_end) issue((kt + 1) * BN, buf ^ 1);
-            compute_tile(buf, kt * BN);
+        issue(kt_begin * BN, kplane, cgk, lds_k0);
+        issue(kt_begin * BN, vplane, cgv, lds_v0);
+        for (int kt = kt_begin; kt < kt_end; kt += 2) {
+            step(kt, kt_end, lds_k0, lds_v0, lds_k1, lds_v1);
+            if (kt + 1 < kt_end) step(kt + 1, kt_end, lds_k1, lds_v1, lds_k0, lds_v0);
         }
     }
 
@@ -339,8 +351,7 @@ __global__ __launch_bounds__(512) void prefill_bf16_kernel(const PrefillArgs a, 
     if (!wave_active) return;
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
-        float lt = l_run[nb] + __shfl_xor(l_run[nb], 16);
-        lt += __shfl_xor(lt, 32);
+        const float lt = group4_sum(l_run[nb]);
         const int row = r0 + 16 * nb + col;
         if (row >= rows_end) continue;
         const float inv = lt > 0.f ? 1.f / lt : 0.f;

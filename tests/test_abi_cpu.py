@@ -99,23 +99,32 @@ def test_prefill_argument_checks(lib):
 
 def test_decode_argument_and_workspace_checks(lib):
     d = desc(nb=1000, bs=16, hkv=8, d=128)
+    # partition_size 128 = chunks of at least 4 steps of 32 keys: 64 sequences of at most
+    # ceil(4097 / 32) = 129 steps -> ceil(64 * 129 / 4) chunks, two partial slots each
     need = lib.pa_decode_workspace_size(d, 64, 32, 4097, 0, 128)
-    parts = -(-4097 // 128)
-    assert need == 64 * 32 * parts * (128 + 2) * 4
+    assert need == -(-64 * 129 // 4) * 2 * 32 * (128 + 2) * 4
     # too small a workspace is rejected before any launch
     assert lib.pa_decode(d, FAKE, FAKE, FAKE, 300, FAKE, 64, 4097, 32, 0.1, 0, 128, FAKE, need - 1, None) == 3
     assert lib.pa_decode(d, FAKE, FAKE, FAKE, 300, FAKE, 64, 4097, 32, 0.1, 0, 128, None, need, None) == 3
-    assert lib.pa_decode(d, FAKE, FAKE, FAKE, 300, FAKE, 64, 4097, 32, 0.1, 0, 96, FAKE, need, None) == 1
+    assert lib.pa_decode(d, FAKE, FAKE, FAKE, 300, FAKE, 64, 4097, 32, 0.1, 0, 48, FAKE, need, None) == 1
+    assert lib.pa_decode(d, FAKE, FAKE, FAKE, 300, FAKE, 64, 4097, 32, 0.1, 0, -32, FAKE, need, None) == 1
     assert lib.pa_decode(d, FAKE, FAKE, FAKE, 200, FAKE, 64, 4097, 32, 0.1, 0, 128, FAKE, need, None) == 1
     assert lib.pa_decode(d, None, FAKE, FAKE, 300, FAKE, 64, 4097, 32, 0.1, 0, 128, FAKE, need, None) == 1
-    # one partition: no workspace needed; float32 never needs one
-    assert lib.pa_decode_workspace_size(d, 64, 32, 100, 0, 128) == 0
+    # a batch that fits one chunk needs no workspace; float32 never needs one
+    assert lib.pa_decode_workspace_size(d, 1, 32, 100, 0, 128) == 0
+    assert lib.pa_decode_workspace_size(d, 64, 32, 0, 0, 0) == 0
     assert lib.pa_decode_workspace_size(desc(dtype=0), 64, 32, 4097, 0, 128) == 0
-    # a window bounds the key span
-    assert lib.pa_decode_workspace_size(d, 8, 40, 33281, 4096, 128) == 8 * 40 * (-(-(4096 + 31) // 128)) * 130 * 4
+    # a window bounds the key span: at most 4096 + 31 keys = 129 steps per sequence
+    assert lib.pa_decode_workspace_size(d, 8, 40, 33281, 4096, 128) == -(-8 * 129 // 4) * 2 * 40 * 130 * 4
 
 
-def test_auto_partition_is_multiple_of_64(lib):
-    for b, n in ((1, 100), (64, 4097), (8, 33281), (252, 8193), (1024, 100000)):
-        p = lib.pa_decode_partition_size(desc(hkv=8), b, 32, n, 0)
-        assert p >= 128 and p % 64 == 0
+def test_decode_auto_chunks_without_device(lib):
+    # with no device to ask, the automatic split assumes 256 resident workgroups, shared by
+    # the groups of 8 KV heads, and never cuts below 8 steps (256 keys) per chunk
+    d8 = desc(nb=1000, bs=16, hkv=8, d=128)
+    assert lib.pa_decode_workspace_size(d8, 64, 32, 4097, 0, 0) == 256 * 2 * 32 * 130 * 4
+    d16 = desc(nb=1000, bs=16, hkv=16, d=64)
+    assert lib.pa_decode_workspace_size(d16, 64, 32, 4097, 0, 0) == 128 * 2 * 32 * 66 * 4
+    # 4 sequences of at most 100 keys: 16 steps -> 2 chunks
+    assert lib.pa_decode_workspace_size(d8, 4, 32, 100, 0, 0) == 2 * 2 * 32 * 130 * 4
+    assert lib.pa_decode_workspace_size(d8, 2, 32, 100, 0, 0) == 0

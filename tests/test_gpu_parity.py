@@ -163,6 +163,36 @@ def test_decode_zero_length_sequence_and_empty_batch():
     assert empty.shape[0] == 0
 
 
+def test_decode_workspace_reuse_across_shapes():
+    """One workspace (filled with garbage first: its contents need no initialisation) serves
+    calls of several batch sizes and partition sizes; each result matches a fresh-workspace
+    call bit for bit and the oracle within tolerance.  Twelve KV heads also exercise a
+    workgroup whose last four waves have no KV head."""
+    import paged_attention_block_amd as pa
+    seqs = [W.SeqSpec(c, [1], ["decode"]) for c in (700, 64, 1, 2000, 333, 129, 0, 1500, 65)]
+    wl = W.build("wsr", 302, seqs, num_heads=24, num_kv_heads=12, head_size=128, block_size=16,
+                 dtype=torch.bfloat16)
+    run = GpuRun(wl, DEV)
+    store, dec = wl.phases[0]
+    run.run(store)
+    torch.cuda.synchronize()
+    vals = host_values(run.cache.cpu())
+    need = pa.pa_decode_workspace_size(run.cache, len(seqs), 24, int(dec.max_seq_len), 0, 64)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device=DEV)
+    for b, part in ((9, 64), (4, 128), (9, 64), (2, 64)):
+        say(f"[workspace reuse] batch {b} partition {part}")
+        lens = dec.seq_lens[:b]
+        args = (dec.query[:b].to(DEV), run.cache, run.i32(dec.block_table[:b]), run.i32(lens),
+                int(dec.max_seq_len), wl.scale, wl.num_kv_heads)
+        out = pa.pa_decode(*args, workspace=ws, partition_size=part)
+        fresh = pa.pa_decode(*args, partition_size=part)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), fresh.view(torch.int16))
+        ref = oracle.decode(host_values(dec.query[:b]), vals, dec.block_table[:b], lens, wl.scale,
+                            wl.num_kv_heads)
+        assert_close(out.float().cpu().numpy(), ref, wl.dtype, f"reuse b{b} p{part}")
+
+
 def test_prefill_zero_length_sequence_in_batch():
     seqs = [W.SeqSpec(0, [40], ["prefill"]), W.SeqSpec(30, [0], [None]), W.SeqSpec(0, [70], ["prefill"])]
     wl = W.build("zlp", 301, seqs, num_heads=8, num_kv_heads=2, head_size=128, block_size=16,
