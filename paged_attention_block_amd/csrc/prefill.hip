@@ -33,13 +33,49 @@
 // q-tiles of one (sequence, KV head) back to back: those share K/V through that XCD's L2.
 #include <math.h>
 
+#include <type_traits>
+
 #include "pa_internal.hpp"
 
 namespace pa {
 
-namespace {
-constexpr int BN = 64;  // keys per K/V tile
-}  // namespace
+// Tile copies and their synchronisation are written as inline assembly on purpose.  The
+// compiler tracks its own HBM->LDS copies (global_load_lds) and, unable to tell that a
+// later LDS read targets a different buffer than a copy still in flight, waits for every
+// copy (vmcnt 0) before the read: that exposed the full copy latency in every other step.
+// Copies it cannot see never make its own waits unsafe (vmcnt counts complete in order,
+// extra outstanding operations only make a wait stricter), so the kernel waits for its
+// copies itself: wait_vmcnt before a tile is used, then lds_barrier.
+
+// one 16-byte-per-lane copy HBM -> LDS: lane l's 16 bytes at base + voff (base wave-uniform,
+// voff the lane's 32-bit offset) land at LDS byte address lds + 16*l (lds wave-uniform)
+__device__ __forceinline__ void copy_to_lds16(const void* base, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(base), "s"(lds)
+                 : "memory", "m0");
+}
+
+// s_waitcnt vmcnt(n) for a wave-uniform n (the count is an instruction immediate; counts
+// above 23 wait for everything, which is always safe)
+__device__ __forceinline__ void wait_vmcnt(int n) {
+#define PA_VMCNT_CASE(N) \
+    case N: asm volatile("s_waitcnt vmcnt(" #N ")" ::: "memory"); break;
+    switch (n) {
+        PA_VMCNT_CASE(1) PA_VMCNT_CASE(2) PA_VMCNT_CASE(3) PA_VMCNT_CASE(4) PA_VMCNT_CASE(5)
+        PA_VMCNT_CASE(6) PA_VMCNT_CASE(7) PA_VMCNT_CASE(8) PA_VMCNT_CASE(9) PA_VMCNT_CASE(10)
+        PA_VMCNT_CASE(11) PA_VMCNT_CASE(12) PA_VMCNT_CASE(13) PA_VMCNT_CASE(14) PA_VMCNT_CASE(15)
+        PA_VMCNT_CASE(16) PA_VMCNT_CASE(17) PA_VMCNT_CASE(18) PA_VMCNT_CASE(19) PA_VMCNT_CASE(20)
+        PA_VMCNT_CASE(21) PA_VMCNT_CASE(22) PA_VMCNT_CASE(23)
+        default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    }
+#undef PA_VMCNT_CASE
+}
+
+// workgroup barrier after this wave's LDS writes completed; no wait for copies in flight
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 struct PrefillGrid {
     int n_head_chunks;  // workgroups per KV head (heads of the group split in chunks)
@@ -51,9 +87,12 @@ struct PrefillGrid {
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-template <int D, int RW>
-__global__ __launch_bounds__(512) void prefill_bf16_kernel(const PrefillArgs a, const PrefillGrid pg) {
-    constexpr int BM = 32 * RW;       // query rows per tile
+template <int D, int NBR, int RW, int BN, int NBUF>
+__global__ __launch_bounds__(NBR == 4 ? 128 : 512) void prefill_bf16_kernel(const PrefillArgs a, const PrefillGrid pg) {
+    constexpr int NGA = BN / 16;      // 16-key groups per K/V tile
+    constexpr int NCC = BN / 32;      // 32-key chunks per K/V tile (PV MFMA k-steps)
+    constexpr int RPW = 16 * NBR;     // query rows per wave (NBR blocks of 16)
+    constexpr int BM = RPW * RW;      // query rows per tile
     constexpr int KS = D / 32;        // k-slices of q.K^T
     constexpr int DB = D / 16;        // 16-dim output blocks
     constexpr int CPR = D / 8;        // 16-byte chunks per row
@@ -63,12 +102,16 @@ __global__ __launch_bounds__(512) void prefill_bf16_kernel(const PrefillArgs a, 
     constexpr int KSW = CPR >= 16 ? 15 : CPR - 1;        // K swizzle mask
     constexpr int VSW = CPR >= 16 ? 14 : CPR - 2;        // V swizzle mask (even values)
 
-    // two K and two V buffers as distinct objects, so the compiler can tell a copy into one
+    // NBUF K and NBUF V buffers as distinct objects, so the compiler can tell a copy into one
     // from a read of another and does not wait for in-flight copies before every LDS read
     __shared__ __attribute__((aligned(1024))) char lds_k0[TILE];
     __shared__ __attribute__((aligned(1024))) char lds_k1[TILE];
+    __shared__ __attribute__((aligned(1024))) char lds_k2[NBUF > 2 ? TILE : 16];
+    __shared__ __attribute__((aligned(1024))) char lds_k3[NBUF > 3 ? TILE : 16];
     __shared__ __attribute__((aligned(1024))) char lds_v0[TILE];
     __shared__ __attribute__((aligned(1024))) char lds_v1[TILE];
+    __shared__ __attribute__((aligned(1024))) char lds_v2[NBUF > 2 ? TILE : 16];
+    __shared__ __attribute__((aligned(1024))) char lds_v3[NBUF > 3 ? TILE : 16];
 
     // ---------------------------------------------------------------- work item
     const int b = blockIdx.x;
@@ -93,7 +136,7 @@ __global__ __launch_bounds__(512) void prefill_bf16_kernel(const PrefillArgs a, 
 
     const int tid = threadIdx.x;
     const int nwaves = blockDim.x >> 6;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: copy setup stays scalar
     const int lane = tid & 63;
     const int col = lane & 15;
     const int grp = lane >> 4;
@@ -109,8 +152,8 @@ __global__ __launch_bounds__(512) void prefill_bf16_kernel(const PrefillArgs a, 
     const int wg_lo = W > 0 ? max(0, off + i0 - W + 1) : 0;
     const int wg_hi = min(off + rows_end - 1, sk - 1);
     // this wave's rows and key range
-    const int r0 = i0 + 32 * rw;
-    const int r_last = min(r0 + 31, rows_end - 1);
+    const int r0 = i0 + RPW * rw;
+    const int r_last = min(r0 + RPW - 1, rows_end - 1);
     const bool wave_active = wave_ok && r0 < rows_end;
     const int wv_hi = min(off + r_last, sk - 1);
     const int wv_lo = W > 0 ? max(0, off + r0 - W + 1) : 0;
@@ -122,14 +165,18 @@ __global__ __launch_bounds__(512) void prefill_bf16_kernel(const PrefillArgs a, 
     const int shift = a.c.block_shift;
     const char* __restrict__ kplane = (const char*)a.c.kv;
     const int64_t vdelta = a.c.plane_elems * 2;
-    const int32_t* __restrict__ table = a.table + (int64_t)s * a.max_blocks;
+    // the block table through the constant address space: it is never written while the
+    // kernel runs, so the (wave-uniform) lookups become scalar loads that do not share the
+    // vector-memory counter with the in-flight tile copies
+    typedef __attribute__((address_space(4))) const int32_t cint32;
+    cint32* table = (cint32*)(a.table + (int64_t)s * a.max_blocks);
     const int64_t RB = (int64_t)Hkv * D * 2;  // cache token-row bytes
 
     // ---------------------------------------------------------------- Q^T operands
-    bf16x8 qf[2][KS];
-    int prow[2], plo[2];
+    bf16x8 qf[NBR][KS];
+    int prow[NBR], plo[NBR];
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
+    for (int nb = 0; nb < NBR; ++nb) {
         const int row = r0 + 16 * nb + col;
         const bool ok = wave_active && row < rows_end;
         const u32x4* src = (const u32x4*)((const __bf16*)a.q + ((int64_t)(q0 + (ok ? row : 0)) * H + (wave_ok ? h : 0)) * D);
@@ -142,69 +189,78 @@ __global__ __launch_bounds__(512) void prefill_bf16_kernel(const PrefillArgs a, 
         plo[nb] = W > 0 ? max(0, off + row - W + 1) : 0;
     }
 
-    f32x4 oacc[DB][2];
+    f32x4 oacc[DB][NBR];
 #pragma unroll
     for (int d = 0; d < DB; ++d)
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) oacc[d][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run[2] = {-INFINITY, -INFINITY};
-    float l_run[2] = {0.f, 0.f};
+        for (int nb = 0; nb < NBR; ++nb) oacc[d][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run[NBR], l_run[NBR];
+#pragma unroll
+    for (int nb = 0; nb < NBR; ++nb) {
+        m_run[nb] = -INFINITY;
+        l_run[nb] = 0.f;
+    }
 
     // ---------------------------------------------------------------- tile copies
     // A plane of a tile is NQ copy instructions of 1 KB: instruction q fills LDS bytes
-    // [1024*q, +1024): rows RPI*q + lane / CPR, slot lane % CPR.  Wave w issues q = w,
-    // w + nwaves, ...  The lane offsets relative to the first token row of the row's 16-key
-    // group are the same for every tile.
+    // [1024*q, +1024): rows RPI*q + lane / CPR, slot lane % CPR; the IPG instructions of
+    // 16-key group ga are q = IPG*ga .. IPG*ga + IPG-1.  Wave w copies only group w % NGA
+    // (the first NGA*(nwaves/NGA) waves; the others copy nothing), instructions
+    // w / NGA + nsub*j of it, so per tile it looks up one block and forms one base address
+    // (kept in scalar registers: the copy address is that base plus a per-lane 32-bit
+    // offset fixed for the whole kernel).
+    constexpr int IPG = 16 / RPI;          // copy instructions per 16-key group
     const int crow = lane / CPR;           // row within the instruction's rows
     const int cslot = lane % CPR;          // LDS chunk slot within the row
-    constexpr int CPW = (NQ + 3) / 4;      // copies per wave and plane (>= 4 waves)
-    uint32_t cgk[CPW], cgv[CPW];
+    const int nsub = nwaves / NGA;         // waves per group
+    const bool copier = wave < NGA * nsub;
+    const int cga = wave % NGA;            // the group this wave copies
+    const int csub = wave / NGA;
+    uint32_t cgk[IPG], cgv[IPG];
+    int my_copies = 0;                     // copy instructions this wave issues per tile
 #pragma unroll
-    for (int i = 0; i < CPW; ++i) {
-        const int q = wave + nwaves * i;
-        const int row = RPI * q + crow;
+    for (int jj = 0; jj < IPG; ++jj) {
+        const int ig = csub + nsub * jj;   // instruction within the group
+        const int row = RPI * ig + crow;   // token row within the group (0..15)
         const int ck = cslot ^ (row & KSW);
         const int cv = cslot ^ ((2 * row) & VSW);
-        cgk[i] = q < NQ ? (uint32_t)((((row & 15) * Hkv + g) * D + ck * 8) * 2) : 0u;
-        cgv[i] = q < NQ ? (uint32_t)((((row & 15) * Hkv + g) * D + cv * 8) * 2) : 0u;
+        cgk[jj] = (uint32_t)(((row * Hkv + g) * D + ck * 8) * 2);
+        cgv[jj] = (uint32_t)(((row * Hkv + g) * D + cv * 8) * 2);
+        my_copies += (copier && ig < IPG) ? 2 : 0;
     }
 
-    // copy one plane of the tile at k0 into LDS buffer dst
-    auto issue = [&](int k0, const char* plane, const uint32_t (&cg)[CPW], char* dst) {
-        int64_t gb[4];
-        bool gv[4];
+    // byte offset in a plane of the first token row of this wave's group of the tile at k0
+    // (KV head 0).  A group with no live key takes the rows of the tile's first live group
+    // instead, so no block-table entry outside the live range is read.
+    auto group_base = [&](int k0) -> int64_t {
+        const int j0 = k0 + 16 * cga;
+        const bool live = (j0 <= wg_hi) && (j0 + 15 >= wg_lo);
+        const int src = live ? j0 : (max(k0, wg_lo) & ~15);
+        const int blk = table[src >> shift];
+        return ((int64_t)blk * BS + (src & (BS - 1))) * RB;
+    };
+    // copy this wave's share of one plane of a tile (group base gbase) into LDS buffer dst
+    auto issue = [&](const char* plane, int64_t gbase, const uint32_t (&cg)[IPG], char* dst) {
+        if (!copier) return;
+        const char* src = plane + gbase;
+        const uint32_t lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)dst;
 #pragma unroll
-        for (int ga = 0; ga < 4; ++ga) {
-            const int j0 = k0 + 16 * ga;
-            gv[ga] = (j0 <= wg_hi) && (j0 + 15 >= wg_lo);
-            const int blk = gv[ga] ? table[j0 >> shift] : 0;
-            gb[ga] = ((int64_t)blk * BS + (j0 & (BS - 1))) * RB;
-        }
-        // a group with no live key borrows the rows of a live group of the tile
-        const int64_t live = gv[0] ? gb[0] : gv[1] ? gb[1] : gv[2] ? gb[2] : gb[3];
-#pragma unroll
-        for (int ga = 0; ga < 4; ++ga) gb[ga] = gv[ga] ? gb[ga] : live;
-#pragma unroll
-        for (int i = 0; i < CPW; ++i) {
-            const int q = wave + nwaves * i;
-            if (q < NQ) {
-                const int ga = (RPI * q) >> 4;
-                const int64_t base = ga == 0 ? gb[0] : ga == 1 ? gb[1] : ga == 2 ? gb[2] : gb[3];
-                __builtin_amdgcn_global_load_lds((const void*)(plane + base + cg[i]),
-                                                 (__attribute__((address_space(3))) void*)(dst + 1024 * q), 16, 0, 0);
-            }
+        for (int jj = 0; jj < IPG; ++jj) {
+            const int ig = csub + nsub * jj;
+            if (ig < IPG) copy_to_lds16(src, cg[jj], lds + 1024u * (uint32_t)(IPG * cga + ig));
         }
     };
     // after this wave's copies of a plane of the tile at k0 landed: zero the rows it copied
     // whose key lies outside [wg_lo, wg_hi]
     auto zero_dead = [&](int k0, char* dst) {
-        if (k0 >= wg_lo && k0 + BN - 1 <= wg_hi) return;
+        if (!copier || (k0 >= wg_lo && k0 + BN - 1 <= wg_hi)) return;
 #pragma unroll
-        for (int i = 0; i < CPW; ++i) {
-            const int q = wave + nwaves * i;
-            if (q < NQ) {
-                const int key = k0 + RPI * q + crow;
-                if (key < wg_lo || key > wg_hi) *(u32x4*)(dst + 1024 * q + 16 * lane) = (u32x4)(0u);
+        for (int jj = 0; jj < IPG; ++jj) {
+            const int ig = csub + nsub * jj;
+            if (ig < IPG) {
+                const int key = k0 + 16 * cga + RPI * ig + crow;
+                if (key < wg_lo || key > wg_hi)
+                    *(u32x4*)(dst + 1024 * (IPG * cga + ig) + 16 * lane) = (u32x4)(0u);
             }
         }
     };
@@ -223,59 +279,64 @@ __global__ __launch_bounds__(512) void prefill_bf16_kernel(const PrefillArgs a, 
     const int vch = (col & 3) >> 1;  // chunk within the 16-dim block
 
     // S^T of the tile whose K sits at kbuf
-    auto qk = [&](const char* kt, f32x4 (&sacc)[4][2]) {
+    auto qk = [&](const char* kt, f32x4 (&sacc)[NGA][NBR]) {
 #pragma unroll
-        for (int ga = 0; ga < 4; ++ga)
+        for (int ga = 0; ga < NGA; ++ga)
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb) sacc[ga][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int nb = 0; nb < NBR; ++nb) sacc[ga][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int t = 0; t < KS; ++t) {
 #pragma unroll
-            for (int ga = 0; ga < 4; ++ga) {
+            for (int ga = 0; ga < NGA; ++ga) {
                 const bf16x8 kf = *(const bf16x8*)(kt + koff[t] + 16 * ga * D * 2);
 #pragma unroll
-                for (int nb = 0; nb < 2; ++nb)
+                for (int nb = 0; nb < NBR; ++nb)
                     sacc[ga][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[nb][t], sacc[ga][nb], 0, 0, 0);
             }
         }
     };
 
     // mask, online softmax, P^T pack; returns whether O needs rescaling
-    auto softmax = [&](int k0, f32x4 (&sacc)[4][2], u32x4 (&pk)[2][2], float (&alpha)[2]) {
+    auto softmax = [&](int k0, f32x4 (&sacc)[NGA][NBR], u32x4 (&pk)[NCC][NBR], float (&alpha)[NBR]) {
         const bool edge = (k0 + BN - 1 > wv_p_min) || (W > 0 && k0 < wv_lo_max);
         if (edge) {
 #pragma unroll
-            for (int ga = 0; ga < 4; ++ga)
+            for (int ga = 0; ga < NGA; ++ga)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int key = k0 + 16 * ga + 4 * grp + r;
 #pragma unroll
-                    for (int nb = 0; nb < 2; ++nb)
+                    for (int nb = 0; nb < NBR; ++nb)
                         sacc[ga][nb][r] = (key > prow[nb] || key < plo[nb]) ? -INFINITY : sacc[ga][nb][r];
                 }
         }
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
+        for (int nb = 0; nb < NBR; ++nb) {
             float mx = fmaxf(fmaxf(sacc[0][nb][0], sacc[0][nb][1]), fmaxf(sacc[0][nb][2], sacc[0][nb][3]));
 #pragma unroll
-            for (int ga = 1; ga < 4; ++ga)
+            for (int ga = 1; ga < NGA; ++ga)
                 mx = fmaxf(mx, fmaxf(fmaxf(sacc[ga][nb][0], sacc[ga][nb][1]), fmaxf(sacc[ga][nb][2], sacc[ga][nb][3])));
             mx = group4_max(mx);
-            const float m_new = fmaxf(m_run[nb], mx * c_log2);
-            const float msub = m_new == -INFINITY ? 0.f : m_new;
-            alpha[nb] = __builtin_amdgcn_exp2f(m_run[nb] - msub);
+            // The reference maximum moves only when the tile's maximum exceeds it by more
+            // than 8 (log2 units): P = exp2(s - m) then stays below 2^8, and O and l are
+            // rescaled only on those rare moves instead of on every increase.
+            const float mt = mx * c_log2;
+            const bool move = mt > m_run[nb] + 8.f;
+            const float m_new = move ? mt : m_run[nb];
+            alpha[nb] = (move && m_run[nb] != -INFINITY) ? __builtin_amdgcn_exp2f(m_run[nb] - m_new) : 1.f;
             m_run[nb] = m_new;
-            float pv[4][4];
+            const float msub = m_new == -INFINITY ? 0.f : m_new;
+            float pv[NGA][4];
 #pragma unroll
-            for (int ga = 0; ga < 4; ++ga)
+            for (int ga = 0; ga < NGA; ++ga)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) pv[ga][r] = __builtin_amdgcn_exp2f(fmaf(sacc[ga][nb][r], c_log2, -msub));
-            float ps[4];
+            float ps = 0.f;
 #pragma unroll
-            for (int ga = 0; ga < 4; ++ga) ps[ga] = (pv[ga][0] + pv[ga][1]) + (pv[ga][2] + pv[ga][3]);
-            l_run[nb] = l_run[nb] * alpha[nb] + ((ps[0] + ps[1]) + (ps[2] + ps[3]));
+            for (int ga = 0; ga < NGA; ++ga) ps += (pv[ga][0] + pv[ga][1]) + (pv[ga][2] + pv[ga][3]);
+            l_run[nb] = l_run[nb] * alpha[nb] + ps;
 #pragma unroll
-            for (int cc = 0; cc < 2; ++cc) {
+            for (int cc = 0; cc < NCC; ++cc) {
                 pk[cc][nb][0] = pack_bf16x2(pv[2 * cc][0], pv[2 * cc][1]);
                 pk[cc][nb][1] = pack_bf16x2(pv[2 * cc][2], pv[2 * cc][3]);
                 pk[cc][nb][2] = pack_bf16x2(pv[2 * cc + 1][0], pv[2 * cc + 1][1]);
@@ -284,15 +345,18 @@ __global__ __launch_bounds__(512) void prefill_bf16_kernel(const PrefillArgs a, 
         }
     };
 
-    auto pv_mfma = [&](const char* vt, const u32x4 (&pk)[2][2], const float (&alpha)[2]) {
-        if (__any(alpha[0] != 1.f || alpha[1] != 1.f)) {
+    auto pv_mfma = [&](const char* vt, const u32x4 (&pk)[NCC][NBR], const float (&alpha)[NBR]) {
+        bool rescale = false;
+#pragma unroll
+        for (int nb = 0; nb < NBR; ++nb) rescale = rescale || alpha[nb] != 1.f;
+        if (__any(rescale)) {
 #pragma unroll
             for (int d = 0; d < DB; ++d)
 #pragma unroll
-                for (int nb = 0; nb < 2; ++nb) oacc[d][nb] *= alpha[nb];
+                for (int nb = 0; nb < NBR; ++nb) oacc[d][nb] *= alpha[nb];
         }
 #pragma unroll
-        for (int cc = 0; cc < 2; ++cc) {
+        for (int cc = 0; cc < NCC; ++cc) {
             bf16x8 vf[DB];
 #pragma unroll
             for (int d = 0; d < DB; ++d) {
@@ -308,29 +372,48 @@ __global__ __launch_bounds__(512) void prefill_bf16_kernel(const PrefillArgs a, 
 #pragma unroll
             for (int d = 0; d < DB; ++d)
 #pragma unroll
-                for (int nb = 0; nb < 2; ++nb)
+                for (int nb = 0; nb < NBR; ++nb)
                     oacc[d][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                         vf[d], __builtin_bit_cast(bf16x8, pk[cc][nb]), oacc[d][nb], 0, 0, 0);
         }
     };
 
     // ---------------------------------------------------------------- main loop
-    // K/V of tile kt+1 are copied into the other buffer pair while tile kt computes; the
-    // loop body is written out twice so each half names fixed buffers.
-    auto step = [&](int kt, int kt_end, char* kc, char* vc, char* kn, char* vn) {
+    // A ring of NBUF buffer pairs: while tile kt computes, the copies of tiles kt+1 ..
+    // kt+NBUF-1 are in flight.  Tile kt sits in buffer (kt - kt_begin) % NBUF; the loop body
+    // is written out NBUF times so each step names fixed buffers.
+    auto kbuf = [&](auto J) -> char* {
+        constexpr int j = decltype(J)::value;
+        return j == 0 ? lds_k0 : j == 1 ? lds_k1 : j == 2 ? lds_k2 : lds_k3;
+    };
+    auto vbuf = [&](auto J) -> char* {
+        constexpr int j = decltype(J)::value;
+        return j == 0 ? lds_v0 : j == 1 ? lds_v1 : j == 2 ? lds_v2 : lds_v3;
+    };
+    auto step = [&](int kt, int kt_end, auto J) {
+        constexpr int j = decltype(J)::value;
+        constexpr int jn = (j + NBUF - 1) % NBUF;  // buffer of tile kt + NBUF - 1
+        char* kc = kbuf(J);
+        char* vc = vbuf(J);
         const int k0 = kt * BN;
-        __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): this wave's copies of tile kt landed
+        // this wave's copies of tile kt have landed once at most those of the tiles after
+        // it (up to NBUF - 2 of them) are still in flight
+        const int later = min(NBUF - 2, kt_end - 1 - kt);
+        wait_vmcnt(my_copies * later);
         zero_dead(k0, kc);
         zero_dead(k0, vc);
-        __syncthreads();                     // all copies of tile kt visible; kn/vn free
-        if (kt + 1 < kt_end) {
-            issue(k0 + BN, kplane, cgk, kn);
-            issue(k0 + BN, vplane, cgv, vn);
+        // all copies of tile kt visible; buffer jn (tile kt - 1) is free.  Not a fenced
+        // barrier: that would also wait for the copies of the later tiles
+        lds_barrier();
+        if (kt + NBUF - 1 < kt_end) {
+            const int64_t gb = group_base(k0 + (NBUF - 1) * BN);
+            issue(kplane, gb, cgk, kbuf(std::integral_constant<int, jn>{}));
+            issue(vplane, gb, cgv, vbuf(std::integral_constant<int, jn>{}));
         }
         if (wave_active && k0 <= wv_hi && k0 + BN - 1 >= wv_lo) {
-            f32x4 sacc[4][2];
-            u32x4 pk[2][2];
-            float alpha[2];
+            f32x4 sacc[NGA][NBR];
+            u32x4 pk[NCC][NBR];
+            float alpha[NBR];
             qk(kc, sacc);
             softmax(k0, sacc, pk, alpha);
             pv_mfma(vc, pk, alpha);
@@ -339,18 +422,35 @@ __global__ __launch_bounds__(512) void prefill_bf16_kernel(const PrefillArgs a, 
     if (wg_hi >= wg_lo) {
         const int kt_begin = wg_lo / BN;
         const int kt_end = wg_hi / BN + 1;
-        issue(kt_begin * BN, kplane, cgk, lds_k0);
-        issue(kt_begin * BN, vplane, cgv, lds_v0);
-        for (int kt = kt_begin; kt < kt_end; kt += 2) {
-            step(kt, kt_end, lds_k0, lds_v0, lds_k1, lds_v1);
-            if (kt + 1 < kt_end) step(kt + 1, kt_end, lds_k1, lds_v1, lds_k0, lds_v0);
+        {
+            int64_t gb = group_base(kt_begin * BN);
+            issue(kplane, gb, cgk, lds_k0);
+            issue(vplane, gb, cgv, lds_v0);
+            if (NBUF > 2 && kt_begin + 1 < kt_end) {
+                gb = group_base((kt_begin + 1) * BN);
+                issue(kplane, gb, cgk, lds_k1);
+                issue(vplane, gb, cgv, lds_v1);
+            }
+            if (NBUF > 3 && kt_begin + 2 < kt_end) {
+                gb = group_base((kt_begin + 2) * BN);
+                issue(kplane, gb, cgk, lds_k2);
+                issue(vplane, gb, cgv, lds_v2);
+            }
+        }
+        for (int kt = kt_begin; kt < kt_end; kt += NBUF) {
+            step(kt, kt_end, std::integral_constant<int, 0>{});
+            if (kt + 1 < kt_end) step(kt + 1, kt_end, std::integral_constant<int, 1>{});
+            if constexpr (NBUF > 2)
+                if (kt + 2 < kt_end) step(kt + 2, kt_end, std::integral_constant<int, 2>{});
+            if constexpr (NBUF > 3)
+                if (kt + 3 < kt_end) step(kt + 3, kt_end, std::integral_constant<int, 3>{});
         }
     }
 
     // ---------------------------------------------------------------- epilogue
     if (!wave_active) return;
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
+    for (int nb = 0; nb < NBR; ++nb) {
         const float lt = group4_sum(l_run[nb]);
         const int row = r0 + 16 * nb + col;
         if (row >= rows_end) continue;
@@ -364,33 +464,51 @@ __global__ __launch_bounds__(512) void prefill_bf16_kernel(const PrefillArgs a, 
     }
 }
 
-template <int D, int RW>
+// Launch shape: query rows per wave (16 * NBR) and keys per K/V tile.
+constexpr int kPrefillNBR = 2;
+constexpr int kPrefillBN = 64;
+constexpr int kPrefillNBUF = 2;
+// every 16-key group of a tile needs a wave of its own to copy it
+static_assert(kPrefillBN / 16 <= (kPrefillNBR == 4 ? 2 : 4), "fewer waves than key groups per tile");
+
+template <int D, int NBR, int RW>
 static void launch_rw(const PrefillArgs& a, const PrefillGrid& pg, int threads, hipStream_t st) {
     const int64_t nsg_pad = ((int64_t)pg.n_sg + 7) / 8 * 8;
     const dim3 grid((unsigned)(nsg_pad * pg.n_qtiles));
-    hipLaunchKernelGGL((prefill_bf16_kernel<D, RW>), grid, dim3(threads), 0, st, a, pg);
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, NBR, RW, kPrefillBN, kPrefillNBUF>), grid, dim3(threads), 0, st, a, pg);
 }
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t st) {
     const int G = a.group;
-    // row-waves per head: 4..8 waves per workgroup (measured: two independent 4-wave
-    // workgroups per CU beat one 8-wave workgroup)
-    const int RW = G >= 4 ? 1 : (G >= 2 ? 2 : 4);
+    constexpr int NBR = kPrefillNBR;
     PrefillGrid pg;
-    pg.heads_per_wg = G * RW <= 8 ? G : 8 / RW;
+    int RW, threads;
+    if (NBR == 4) {
+        // 64 query rows per wave, 2 waves per workgroup (two heads of the group, or two row
+        // halves of one head when G = 1): each K/V byte read from LDS feeds 64 rows of MFMA
+        // work, and two workgroups per CU overlap one's tile-copy start with the other's math
+        RW = G >= 2 ? 1 : 2;
+        pg.heads_per_wg = G >= 2 ? 2 : 1;
+        threads = 128;
+    } else {
+        // 32 rows per wave, 4..8 waves per workgroup (measured: two independent 4-wave
+        // workgroups per CU beat one 8-wave workgroup)
+        RW = G >= 4 ? 1 : (G >= 2 ? 2 : 4);
+        pg.heads_per_wg = G * RW <= 8 ? G : 8 / RW;
+        threads = 64 * RW * pg.heads_per_wg < 256 ? 256 : 64 * RW * pg.heads_per_wg;
+    }
     pg.n_head_chunks = (G + pg.heads_per_wg - 1) / pg.heads_per_wg;
     pg.n_sg = a.num_seqs * a.c.num_kv_heads * pg.n_head_chunks;
-    const int BM = 32 * RW;
+    const int BM = 16 * NBR * RW;
     pg.n_qtiles = (a.max_seqlen_q + BM - 1) / BM;
-    const int threads = 64 * RW * pg.heads_per_wg < 256 ? 256 : 64 * RW * pg.heads_per_wg;
     if (a.c.head_size == 128) {
-        if (RW == 1) launch_rw<128, 1>(a, pg, threads, st);
-        else if (RW == 2) launch_rw<128, 2>(a, pg, threads, st);
-        else launch_rw<128, 4>(a, pg, threads, st);
+        if (RW == 1) launch_rw<128, NBR, 1>(a, pg, threads, st);
+        else if (RW == 2) launch_rw<128, NBR, 2>(a, pg, threads, st);
+        else launch_rw<128, NBR, 4>(a, pg, threads, st);
     } else {
-        if (RW == 1) launch_rw<64, 1>(a, pg, threads, st);
-        else if (RW == 2) launch_rw<64, 2>(a, pg, threads, st);
-        else launch_rw<64, 4>(a, pg, threads, st);
+        if (RW == 1) launch_rw<64, NBR, 1>(a, pg, threads, st);
+        else if (RW == 2) launch_rw<64, NBR, 2>(a, pg, threads, st);
+        else launch_rw<64, NBR, 4>(a, pg, threads, st);
     }
     return hipGetLastError();
 }
