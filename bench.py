@@ -3,7 +3,12 @@
 Default run (one JSON line on stdout):
   * headline, ``value``: GQA paged decode, B 64, contexts U[512, 4096], H 32 / Hkv 8,
     D 128, block 16, bf16.  One step = store the 64 new tokens through slot_mapping, then
-    decode.  ``value`` = algorithmic bytes of the step / wall time of the step (GB/s).
+    decode.  ``value`` = algorithmic bytes of the step / time of the step (GB/s).
+  * Before every timed step an untimed read of a 1 GiB buffer evicts the 256 MB last-level
+    cache (MALL) and the L2s, so the step's data comes from HBM (a read leaves clean lines:
+    an eviction by writing would leave dirty ones whose write-back lands inside the timed
+    step); the step is timed with HIP events around its ops (``--flush-mb 0`` turns the
+    eviction off and times back-to-back steps).
   * ``prefill``: varlen causal prefill, 16 prompts of U[128, 2048] tokens, same heads;
     one step = store every prompt token, then prefill.  TFLOP/s of algorithmic FLOPs.
   * ``roofline`` per op: algorithmic bytes (decode) or FLOPs (prefill) of one launch over
@@ -142,10 +147,16 @@ class Step:
                          wl.num_kv_heads, wl.sliding_window, out=d["out"], workspace=d["ws"],
                          partition_size=d["part"])
 
-    def time(self, steps: int, warmup: int):
-        """Wall time per step and mean HIP-event duration of every op over the timed steps."""
+    def time(self, steps: int, warmup: int, flush_bytes: int = 0):
+        """Mean step time, mean HIP-event duration of every op, and wall time per step
+        (eviction writes included) over the timed steps.  With flush_bytes > 0 each step is
+        preceded by an untimed read of that many bytes (cache eviction)."""
         torch = self.torch
-        for _ in range(warmup):
+        scratch = torch.ones(flush_bytes // 4, dtype=torch.int32, device=self.dev) if flush_bytes else None
+        sink = torch.zeros(1, dtype=torch.int32, device=self.dev)
+        for w in range(warmup):
+            if scratch is not None:
+                torch.amax(scratch, dim=0, keepdim=True, out=sink)
             for d in self.prepared:
                 self.run_op(d)
         torch.cuda.synchronize()
@@ -154,15 +165,19 @@ class Step:
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for k in range(steps):
+            if scratch is not None:
+                torch.amax(scratch, dim=0, keepdim=True, out=sink)
             evs[k][0].record(stream)
             for i, d in enumerate(self.prepared):
                 self.run_op(d)
                 evs[k][i + 1].record(stream)
         torch.cuda.synchronize()
         wall = (time.perf_counter() - t0) / steps
+        n_ops = len(self.prepared)
+        step_t = sum(evs[k][0].elapsed_time(evs[k][n_ops]) for k in range(steps)) / steps / 1e3
         per_op = [sum(evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(steps)) / steps / 1e3
-                  for i in range(len(self.prepared))]
-        return wall, per_op
+                  for i in range(n_ops)]
+        return step_t, per_op, wall
 
 
 # ----------------------------------------------------------------------------- CPU baseline
@@ -277,14 +292,15 @@ def roofline(achieved, peak, unit, bound, traffic=None):
             "frac": round(achieved / peak, 4), "traffic": traffic}
 
 
-def bench_workload(name, steps, warmup, dev, with_cpu, partition_size=0):
+def bench_workload(name, steps, warmup, dev, with_cpu, partition_size=0, flush_mb=1024):
     import workloads as W
     wl = W.config(WORKLOAD_CONFIG[name])
     phase = wl.phases[-1] if name == "chunked_decode" else wl.phases[0]
     step = Step(wl, phase, dev, partition_size)
-    wall, per_op = step.time(steps, warmup)
+    step_t, per_op, wall = step.time(steps, warmup, flush_mb * 1024 * 1024)
     ops = [d["op"] for d in step.prepared]
-    res = {"workload": W.CONFIG_NAMES[WORKLOAD_CONFIG[name]], "ms_per_step": round(wall * 1e3, 4), "ops": {}}
+    res = {"workload": W.CONFIG_NAMES[WORKLOAD_CONFIG[name]], "ms_per_step": round(step_t * 1e3, 4),
+           "wall_ms_per_step": round(wall * 1e3, 4), "cache_eviction_MiB_per_step": flush_mb, "ops": {}}
     total_bytes, total_flops = 0.0, 0.0
     for op, t in zip(ops, per_op):
         n = type(op).__name__
@@ -310,8 +326,8 @@ def bench_workload(name, steps, warmup, dev, with_cpu, partition_size=0):
             b = copy_bytes(op, wl)
             total_bytes += b
             res["ops"]["copy_blocks"] = {"ms": round(t * 1e3, 4), "GB/s": round(b / t / 1e9, 1), "bytes": b}
-    res["step_GB/s"] = round(total_bytes / wall / 1e9, 2)
-    res["step_TFLOP/s"] = round(total_flops / wall / 1e12, 3)
+    res["step_GB/s"] = round(total_bytes / step_t / 1e9, 2)
+    res["step_TFLOP/s"] = round(total_flops / step_t / 1e12, 3)
     if with_cpu:
         for op in ops:
             if type(op).__name__ == "DecodeOp" and name == "decode":
@@ -333,6 +349,8 @@ def main() -> int:
                     help="only run a plain device-to-device copy of MB megabytes (3 times): the "
                          "reference kernel for scaling HBM byte counters")
     ap.add_argument("--no-prefill", action="store_true", help="skip the secondary prefill measurement")
+    ap.add_argument("--flush-mb", type=int, default=1024,
+                    help="untimed read of this many MiB before every step to evict the caches (0 = off)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the library has no multi-GPU path (run with --gpus 1)",
@@ -351,7 +369,8 @@ def main() -> int:
         print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
         return 0
     with_cpu = not args.no_cpu_baseline
-    main_res = bench_workload(args.workload, args.steps, args.warmup, dev, with_cpu, args.partition_size)
+    main_res = bench_workload(args.workload, args.steps, args.warmup, dev, with_cpu, args.partition_size,
+                              args.flush_mb)
     line = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
             "ms_per_step": main_res["ms_per_step"], "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1) bf16, seeded lengths and block tables)"}
@@ -362,10 +381,13 @@ def main() -> int:
         line.update(value=main_res["step_TFLOP/s"], unit="TFLOP/s")
         line["roofline"] = main_res["ops"]["prefill"]["roofline"]
     wl_cfg = WORKLOAD_CONFIG[args.workload]
-    line["config"] = {"workload": main_res["workload"], "config_index": wl_cfg, "ops": main_res["ops"]}
+    line["config"] = {"workload": main_res["workload"], "config_index": wl_cfg, "ops": main_res["ops"],
+                      "cache_eviction_MiB_per_step": args.flush_mb,
+                      "wall_ms_per_step": main_res["wall_ms_per_step"]}
     line["cpu_baseline"] = main_res.get("cpu_baseline")
     if args.workload == "decode" and not args.no_prefill:
-        pre = bench_workload("prefill", max(10, args.steps // 2), max(3, args.warmup // 2), dev, with_cpu)
+        pre = bench_workload("prefill", max(10, args.steps // 2), max(3, args.warmup // 2), dev, with_cpu,
+                             flush_mb=args.flush_mb)
         line["prefill"] = {"workload": pre["workload"], "value": pre["step_TFLOP/s"], "unit": "TFLOP/s",
                            "ms_per_step": pre["ms_per_step"], "ops": pre["ops"],
                            "roofline": pre["ops"]["prefill"]["roofline"],
