@@ -312,10 +312,11 @@ __global__ __launch_bounds__(NBR == 4 ? 128 : 512) void prefill_bf16_kernel(cons
         }
 #pragma unroll
         for (int nb = 0; nb < NBR; ++nb) {
-            float mx = fmaxf(fmaxf(sacc[0][nb][0], sacc[0][nb][1]), fmaxf(sacc[0][nb][2], sacc[0][nb][3]));
+            // three-operand chain: one v_max3 per two scores
+            float mx = fmaxf(sacc[0][nb][0], sacc[0][nb][1]);
 #pragma unroll
-            for (int ga = 1; ga < NGA; ++ga)
-                mx = fmaxf(mx, fmaxf(fmaxf(sacc[ga][nb][0], sacc[ga][nb][1]), fmaxf(sacc[ga][nb][2], sacc[ga][nb][3])));
+            for (int x = 2; x < 4 * NGA; x += 2)
+                mx = fmaxf(fmaxf(mx, sacc[x >> 2][nb][x & 3]), sacc[x >> 2][nb][(x & 3) + 1]);
             mx = group4_max(mx);
             // The reference maximum moves only when the tile's maximum exceeds it by more
             // than 8 (log2 units): P = exp2(s - m) then stays below 2^8, and O and l are
