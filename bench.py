@@ -11,6 +11,9 @@ Default run (one JSON line on stdout):
     eviction off and times back-to-back steps).
   * ``prefill``: varlen causal prefill, 16 prompts of U[128, 2048] tokens, same heads;
     one step = store every prompt token, then prefill.  TFLOP/s of algorithmic FLOPs.
+  * ``secondary``: chunked prefill of 512-token chunks over long contexts with a 4096-key
+    window and the decode after it (config 4), and the mixed step copy_blocks -> store ->
+    prefill -> decode (config 5); every op with its roofline.
   * ``roofline`` per op: algorithmic bytes (decode) or FLOPs (prefill) of one launch over
     its mean duration, timed with HIP events on the stream the library launches on.
   * ``cpu_baseline``: the fp64 numpy oracle on the host, on a bounded sample of the same
@@ -28,6 +31,7 @@ Usage: python bench.py [--steps K] [--warmup W] [--workload decode|prefill|chunk
 from __future__ import annotations
 
 import argparse
+import functools
 import json
 import math
 import os
@@ -42,7 +46,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CU x 4096 FLOP/clk x 2.4 GHz)
 METRIC = "paged decode HBM GB/s (% peak); varlen prefill bf16 TFLOP/s (% MFMA peak)"
 
-WORKLOAD_CONFIG = {"decode": 2, "prefill": 3, "chunked": 4, "mixed": 5}
+WORKLOAD_CONFIG = {"decode": 2, "prefill": 3, "chunked": 4, "chunked_decode": 4, "mixed": 5}
 
 
 # ----------------------------------------------------------------------------- algorithmic work
@@ -292,9 +296,15 @@ def roofline(achieved, peak, unit, bound, traffic=None):
             "frac": round(achieved / peak, 4), "traffic": traffic}
 
 
+@functools.lru_cache(maxsize=1)
+def _workload(n):
+    import workloads as W
+    return W.config(n)
+
+
 def bench_workload(name, steps, warmup, dev, with_cpu, partition_size=0, flush_mb=1024):
     import workloads as W
-    wl = W.config(WORKLOAD_CONFIG[name])
+    wl = _workload(WORKLOAD_CONFIG[name])
     phase = wl.phases[-1] if name == "chunked_decode" else wl.phases[0]
     step = Step(wl, phase, dev, partition_size)
     step_t, per_op, wall = step.time(steps, warmup, flush_mb * 1024 * 1024)
@@ -311,21 +321,23 @@ def bench_workload(name, steps, warmup, dev, with_cpu, partition_size=0, flush_m
                                     "bytes": b, "tokens_per_s": round(len(op.seq_lens) / t, 1),
                                     "partition_size": step.prepared[ops.index(op)]["part"] or "auto",
                                     "roofline": roofline(b / t / 1e9, HBM_PEAK_GBS, "GB/s", "hbm",
-                                                         read_traffic("decode"))}
+                                                         read_traffic("decode") if name == "decode" else None)}
         elif n == "PrefillOp":
             f = prefill_flops(op, wl)
             total_flops += f
             res["ops"]["prefill"] = {"ms": round(t * 1e3, 4), "TFLOP/s": round(f / t / 1e12, 2), "flops": f,
                                      "roofline": roofline(f / t / 1e12, BF16_PEAK_TFLOPS, "TFLOP/s", "mfma",
-                                                          read_traffic("prefill"))}
+                                                          read_traffic("prefill") if name == "prefill" else None)}
         elif n == "StoreOp":
             b = store_bytes(op, wl)
             total_bytes += b
-            res["ops"]["store"] = {"ms": round(t * 1e3, 4), "GB/s": round(b / t / 1e9, 1), "bytes": b}
+            res["ops"]["store"] = {"ms": round(t * 1e3, 4), "GB/s": round(b / t / 1e9, 1), "bytes": b,
+                                   "roofline": roofline(b / t / 1e9, HBM_PEAK_GBS, "GB/s", "hbm")}
         elif n == "CopyOp":
             b = copy_bytes(op, wl)
             total_bytes += b
-            res["ops"]["copy_blocks"] = {"ms": round(t * 1e3, 4), "GB/s": round(b / t / 1e9, 1), "bytes": b}
+            res["ops"]["copy_blocks"] = {"ms": round(t * 1e3, 4), "GB/s": round(b / t / 1e9, 1), "bytes": b,
+                                         "roofline": roofline(b / t / 1e9, HBM_PEAK_GBS, "GB/s", "hbm")}
     res["step_GB/s"] = round(total_bytes / step_t / 1e9, 2)
     res["step_TFLOP/s"] = round(total_flops / step_t / 1e12, 3)
     if with_cpu:
@@ -349,6 +361,8 @@ def main() -> int:
                     help="only run a plain device-to-device copy of MB megabytes (3 times): the "
                          "reference kernel for scaling HBM byte counters")
     ap.add_argument("--no-prefill", action="store_true", help="skip the secondary prefill measurement")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the chunked-prefill (config 4) and mixed-step (config 5) measurements")
     ap.add_argument("--flush-mb", type=int, default=1024,
                     help="untimed read of this many MiB before every step to evict the caches (0 = off)")
     args = ap.parse_args()
@@ -392,6 +406,14 @@ def main() -> int:
                            "ms_per_step": pre["ms_per_step"], "ops": pre["ops"],
                            "roofline": pre["ops"]["prefill"]["roofline"],
                            "cpu_baseline": pre.get("cpu_baseline")}
+    if args.workload == "decode" and not args.no_secondary:
+        # the other two workloads, every op with its roofline (no CPU baseline): chunked prefill
+        # with a 4096-key window and the decode after it (config 4), and the mixed step
+        # copy_blocks -> store -> prefill -> decode (config 5)
+        line["secondary"] = {}
+        for name in ("chunked", "chunked_decode", "mixed"):
+            r = bench_workload(name, 10, 3, dev, False, flush_mb=args.flush_mb)
+            line["secondary"][name] = {"workload": r["workload"], "ms_per_step": r["ms_per_step"], "ops": r["ops"]}
     print(json.dumps(line), flush=True)
     return 0
 

@@ -143,7 +143,7 @@ __global__ __launch_bounds__(NBR == 4 ? 128 : 512) void prefill_bf16_kernel(cons
     const int hw = wave / RW;
     const int rw = wave % RW;
     const int hig = hc * pg.heads_per_wg + hw;  // head within the group
-    const bool wave_ok = hig < a.group;
+    const bool wave_ok = hw < pg.heads_per_wg && hig < a.group;
     const int h = g * a.group + hig;
     const int H = a.num_heads;
     const int Hkv = a.c.num_kv_heads;
@@ -492,10 +492,13 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t st) {
         pg.heads_per_wg = G >= 2 ? 2 : 1;
         threads = 128;
     } else {
-        // 32 rows per wave, 4..8 waves per workgroup (measured: two independent 4-wave
-        // workgroups per CU beat one 8-wave workgroup)
+        // 32 rows per wave, 4 waves per workgroup so that two workgroups share a CU
+        // (measured: two independent 4-wave workgroups per CU beat one workgroup of 5..8
+        // waves); a group of more than 4 heads is split into workgroups of at most 4 heads,
+        // each copying the K/V tiles itself (the second copy comes from the L2 / MALL)
         RW = G >= 4 ? 1 : (G >= 2 ? 2 : 4);
-        pg.heads_per_wg = G * RW <= 8 ? G : 8 / RW;
+        const int chunks = G >= 4 ? (G + 3) / 4 : 1;
+        pg.heads_per_wg = G >= 4 ? (G + chunks - 1) / chunks : G;
         threads = 64 * RW * pg.heads_per_wg < 256 ? 256 : 64 * RW * pg.heads_per_wg;
     }
     pg.n_head_chunks = (G + pg.heads_per_wg - 1) / pg.heads_per_wg;
