@@ -388,7 +388,7 @@ def main() -> int:
     line = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
             "ms_per_step": main_res["ms_per_step"], "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1) bf16, seeded lengths and block tables)"}
-    if args.workload in ("decode", "mixed", "chunked") and "decode" in main_res["ops"]:
+    if "decode" in main_res["ops"]:
         line.update(value=main_res["step_GB/s"], unit="GB/s")
         line["roofline"] = main_res["ops"]["decode"]["roofline"]
     else:

@@ -342,22 +342,29 @@ __global__ __launch_bounds__(512) void decode_bf16_kernel(const DecodeArgs a) {
 }
 
 // Merge of the pieces of a sequence cut by chunk boundaries (log-sum-exp rescale by
-// exp2(m_p - max m)): a wavefront per (sequence, four query heads); lanes 16h .. 16h+15 take
-// query head 4*blockIdx.y + h, D/16 dims each.  The states of four pieces are loaded
-// together (one memory round trip per four) and folded in with a running maximum.
-template <int D>
-__global__ __launch_bounds__(64) void decode_merge_kernel(const DecodeArgs a) {
+// exp2(m_p - max m)): a workgroup of MW waves per (sequence, four query heads); in each wave
+// lanes 16h .. 16h+15 take query head 4*blockIdx.y + h, D/16 dims each.  Wave w folds pieces
+// w, w + MW, ... loading MP of them per memory round trip, with a running maximum; the MW
+// partial states are then combined through LDS by wave 0.  MW = 4 when sequences are cut
+// into many pieces (few long sequences), else 1.
+template <int D, int MW>
+__global__ __launch_bounds__(64 * MW) void decode_merge_kernel(const DecodeArgs a) {
     constexpr int DL = D / 16;
+    constexpr int MP = 8;  // pieces loaded per memory round trip
+    __shared__ float red[MW > 1 ? MW : 1][2 + DL][64];
     const int s = blockIdx.x;
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int wv_id = threadIdx.x >> 6;
     int S, nw, off;
     decode_chunking(a, lane, s, S, nw, off);
     const int steps = decode_steps(a.seq_lens[s], a.window);
-    const int h = blockIdx.y * 4 + (lane >> 4);
-    if (steps == 0 || h >= a.num_heads) return;
+    if (steps == 0) return;
     const int w_lo = chunk_of(off, S, nw);
     const int np = chunk_of(off + steps - 1, S, nw) - w_lo + 1;
     if (np <= 1) return;  // written whole by its chunk
+    const int h_lane = blockIdx.y * 4 + (lane >> 4);
+    const bool h_ok = h_lane < a.num_heads;
+    const int h = h_ok ? h_lane : a.num_heads - 1;
     // piece q lives in chunk w_lo + q, slot 0, except the first when the sequence starts
     // after that chunk's first step (then it is that chunk's last sequence: slot 1)
     const int first_slot = off > chunk_begin(w_lo, S, nw) ? 1 : 0;
@@ -366,22 +373,23 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const DecodeArgs a) {
     float acc[DL];
 #pragma unroll
     for (int t = 0; t < DL; ++t) acc[t] = 0.f;
-    for (int q0 = 0; q0 < np; q0 += 4) {
-        f32x2 mv[4];
-        f32x4 ov[4][DL / 4];
+    const int nmine = np > wv_id ? (np - wv_id + MW - 1) / MW : 0;  // pieces of this wave
+    for (int k0 = 0; k0 < nmine; k0 += MP) {
+        f32x2 mv[MP];
+        f32x4 ov[MP][DL / 4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int q = min(q0 + j, np - 1);
+        for (int j = 0; j < MP; ++j) {
+            const int q = wv_id + MW * min(k0 + j, nmine - 1);
             const int64_t slot = ((int64_t)(2 * (w_lo + q) + (q == 0 ? first_slot : 0))) * a.num_heads + h;
             mv[j] = *(const f32x2*)(a.ws_ml + slot * 2);
 #pragma unroll
             for (int t = 0; t < DL / 4; ++t) ov[j][t] = *(const f32x4*)(a.ws_o + slot * D + d0 + 4 * t);
         }
-        float mj[4];
+        float mj[MP];
         float Mn = M;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            mj[j] = q0 + j < np ? mv[j][0] : -INFINITY;
+        for (int j = 0; j < MP; ++j) {
+            mj[j] = k0 + j < nmine ? mv[j][0] : -INFINITY;
             Mn = fmaxf(Mn, mj[j]);
         }
         const float msub = Mn == -INFINITY ? 0.f : Mn;
@@ -390,7 +398,7 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const DecodeArgs a) {
 #pragma unroll
         for (int t = 0; t < DL; ++t) acc[t] *= alpha;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < MP; ++j) {
             const float wq = __builtin_amdgcn_exp2f(mj[j] - msub);
             L = fmaf(wq, mv[j][1], L);
 #pragma unroll
@@ -398,7 +406,30 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const DecodeArgs a) {
         }
         M = Mn;
     }
-    const float inv = L > 0.f ? 1.f / L : 0.f;
+    float Lt = L;
+    if constexpr (MW > 1) {
+        red[wv_id][0][lane] = M;
+        red[wv_id][1][lane] = L;
+#pragma unroll
+        for (int t = 0; t < DL; ++t) red[wv_id][2 + t][lane] = acc[t];
+        __syncthreads();
+        if (wv_id != 0) return;
+        float Mt = red[0][0][lane];
+#pragma unroll
+        for (int w = 1; w < MW; ++w) Mt = fmaxf(Mt, red[w][0][lane]);
+        Lt = 0.f;
+#pragma unroll
+        for (int t = 0; t < DL; ++t) acc[t] = 0.f;
+#pragma unroll
+        for (int w = 0; w < MW; ++w) {
+            const float sc = __builtin_amdgcn_exp2f(red[w][0][lane] - Mt);  // 0 for a wave with no piece
+            Lt = fmaf(sc, red[w][1][lane], Lt);
+#pragma unroll
+            for (int t = 0; t < DL; ++t) acc[t] = fmaf(sc, red[w][2 + t][lane], acc[t]);
+        }
+    }
+    if (!h_ok) return;
+    const float inv = Lt > 0.f ? 1.f / Lt : 0.f;
     uint32_t wv[DL / 2];
 #pragma unroll
     for (int t = 0; t < DL / 2; ++t) wv[t] = pack_bf16(acc[2 * t] * inv, acc[2 * t + 1] * inv);
@@ -448,10 +479,14 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t st) {
         hipLaunchKernelGGL(decode_bf16_kernel<64>, grid, block, 0, st, a);
     if (a.nw > 1) {
         const dim3 mg(a.num_seqs, (a.num_heads + 3) / 4);
-        if (a.c.head_size == 128)
-            hipLaunchKernelGGL(decode_merge_kernel<128>, mg, dim3(64), 0, st, a);
-        else
-            hipLaunchKernelGGL(decode_merge_kernel<64>, mg, dim3(64), 0, st, a);
+        const bool many = a.nw > 8 * a.num_seqs;  // more than ~8 pieces per sequence
+        if (a.c.head_size == 128) {
+            if (many) hipLaunchKernelGGL((decode_merge_kernel<128, 4>), mg, dim3(256), 0, st, a);
+            else hipLaunchKernelGGL((decode_merge_kernel<128, 1>), mg, dim3(64), 0, st, a);
+        } else {
+            if (many) hipLaunchKernelGGL((decode_merge_kernel<64, 4>), mg, dim3(256), 0, st, a);
+            else hipLaunchKernelGGL((decode_merge_kernel<64, 1>), mg, dim3(64), 0, st, a);
+        }
     }
     return hipGetLastError();
 }

@@ -78,7 +78,7 @@ int launch_status(hipError_t e) {
 
 // Chunks of the decode step list per group of 8 KV heads.  Automatic: as many as the
 // device holds at once (every chunk then runs in one wave of workgroups and they finish
-// together), each of at least 8 steps (256 keys) so short batches are not cut into pieces
+// together), each of at least 4 steps (128 keys) so short batches are not cut into pieces
 // that cost more to merge than to stream.  partition_size > 0: chunks of at least that
 // many keys, as many as a batch of max_seq_len sequences needs (tests use small ones to
 // cut sequences many times).
@@ -96,7 +96,7 @@ Chunks decode_chunks(int32_t num_seqs, int32_t head_size, int32_t num_kv_heads, 
         const int64_t nw = (smax + c.min_steps - 1) / c.min_steps;
         c.nw = (int32_t)(nw < 1 ? 1 : (nw > (1 << 24) ? (1 << 24) : nw));
     } else {
-        c.min_steps = 8;
+        c.min_steps = 4;
         const int64_t smax = (int64_t)num_seqs * ((max_keys + 31) / 32);
         const int64_t use = (smax + c.min_steps - 1) / c.min_steps;
         int32_t nw = pa::decode_resident_slots(head_size, num_kv_heads) / ygroups;

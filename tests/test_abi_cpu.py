@@ -120,11 +120,11 @@ def test_decode_argument_and_workspace_checks(lib):
 
 def test_decode_auto_chunks_without_device(lib):
     # with no device to ask, the automatic split assumes 256 resident workgroups, shared by
-    # the groups of 8 KV heads, and never cuts below 8 steps (256 keys) per chunk
+    # the groups of 8 KV heads, and never cuts below 4 steps (128 keys) per chunk
     d8 = desc(nb=1000, bs=16, hkv=8, d=128)
     assert lib.pa_decode_workspace_size(d8, 64, 32, 4097, 0, 0) == 256 * 2 * 32 * 130 * 4
     d16 = desc(nb=1000, bs=16, hkv=16, d=64)
     assert lib.pa_decode_workspace_size(d16, 64, 32, 4097, 0, 0) == 128 * 2 * 32 * 66 * 4
-    # 4 sequences of at most 100 keys: 16 steps -> 2 chunks
-    assert lib.pa_decode_workspace_size(d8, 4, 32, 100, 0, 0) == 2 * 2 * 32 * 130 * 4
-    assert lib.pa_decode_workspace_size(d8, 2, 32, 100, 0, 0) == 0
+    # 4 sequences of at most 100 keys: 16 steps -> 4 chunks; one sequence: 4 steps -> 1 chunk
+    assert lib.pa_decode_workspace_size(d8, 4, 32, 100, 0, 0) == 4 * 2 * 32 * 130 * 4
+    assert lib.pa_decode_workspace_size(d8, 1, 32, 100, 0, 0) == 0
