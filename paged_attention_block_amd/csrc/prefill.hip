@@ -6,10 +6,10 @@
 // query's own position, GQA, keys read through the block table (vLLM learning book
 // section 5).
 //
-// Work item = one workgroup per (sequence, KV head, head chunk, q-tile of BM = 32*RW rows).
-// Wave w of the workgroup owns one query head of the KV head's group and 32 rows of the
-// tile; all waves share the K/V tiles (64 keys) staged in LDS, so a K/V byte is fetched
-// once per q-tile for the whole head group.  Per 64-key tile each wave computes
+// Work item = one 4-wave workgroup per (sequence, KV head, q-tile, part of the tile's
+// (query head, 32-row block) pairs).  Wave w owns one query head of the KV head's group and
+// 32 rows; all waves share the K/V tiles (64 keys) staged in LDS, so a K/V byte is fetched
+// once per workgroup for up to four heads.  Per 64-key tile each wave computes
 //   S^T[64 keys x 32 rows] = K . Q^T      (16x16x32 bf16 MFMA, K from LDS, Q^T in VGPRs)
 //   online softmax on S^T, P^T packed to bf16 straight from the accumulators
 //   O^T[D x 32 rows]   += V^T . P^T        (V^T from LDS)
@@ -77,22 +77,26 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Work decomposition.  A q-tile is rb blocks of 32 query rows of one (sequence, KV head);
+// its (query head of the group, row block) pairs, row block major, are dealt four at a time
+// to 4-wave workgroups (rb = 4 / gcd(G, 4), so the G * rb pairs fill whole workgroups for
+// every group size G and no wave idles).
 struct PrefillGrid {
-    int n_head_chunks;  // workgroups per KV head (heads of the group split in chunks)
-    int heads_per_wg;
-    int n_sg;           // num_seqs * num_kv_heads * n_head_chunks
-    int n_qtiles;       // ceil(max_seqlen_q / BM)
+    int rb;             // 32-row blocks per q-tile
+    int wgs_per_tile;   // G * rb / 4
+    int n_sg;           // num_seqs * num_kv_heads
+    int n_tiles;        // ceil(max_seqlen_q / (32 * rb)) * wgs_per_tile
 };
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-template <int D, int NBR, int RW, int BN, int NBUF>
-__global__ __launch_bounds__(NBR == 4 ? 128 : 512) void prefill_bf16_kernel(const PrefillArgs a, const PrefillGrid pg) {
+template <int D, int NBR, int BN, int NBUF>
+__global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const PrefillArgs a, const PrefillGrid pg) {
     constexpr int NGA = BN / 16;      // 16-key groups per K/V tile
     constexpr int NCC = BN / 32;      // 32-key chunks per K/V tile (PV MFMA k-steps)
     constexpr int RPW = 16 * NBR;     // query rows per wave (NBR blocks of 16)
-    constexpr int BM = RPW * RW;      // query rows per tile
+    static_assert(RPW == 32, "row blocks of 32");
     constexpr int KS = D / 32;        // k-slices of q.K^T
     constexpr int DB = D / 16;        // 16-dim output blocks
     constexpr int CPR = D / 8;        // 16-byte chunks per row
@@ -114,25 +118,31 @@ __global__ __launch_bounds__(NBR == 4 ? 128 : 512) void prefill_bf16_kernel(cons
     __shared__ __attribute__((aligned(1024))) char lds_v3[NBUF > 3 ? TILE : 16];
 
     // ---------------------------------------------------------------- work item
+    // Workgroups are numbered so that each XCD (work dispatched round-robin over 8) runs the
+    // tiles of one (sequence, KV head) back to back, longest q-tiles first.
     const int b = blockIdx.x;
     const int xcd = b & 7;
     const int li = b >> 3;
-    const int sg = (li / pg.n_qtiles) * 8 + xcd;
+    const int sg = (li / pg.n_tiles) * 8 + xcd;
     if (sg >= pg.n_sg) return;
-    const int qt = pg.n_qtiles - 1 - li % pg.n_qtiles;  // later (longer) tiles first
-    const int per_seq = a.c.num_kv_heads * pg.n_head_chunks;
-    const int s = sg / per_seq;
-    const int g = (sg % per_seq) / pg.n_head_chunks;
-    const int hc = sg % pg.n_head_chunks;
+    const int ti = pg.n_tiles - 1 - li % pg.n_tiles;
+    const int qt = ti / pg.wgs_per_tile;
+    const int jw = ti % pg.wgs_per_tile;
+    const int s = sg / a.c.num_kv_heads;
+    const int g = sg % a.c.num_kv_heads;
+    const int G = a.group;
 
     const int q0 = a.cu_q[s];
     const int sq = a.cu_q[s + 1] - q0;
-    const int i0 = qt * BM;
-    if (i0 >= sq) return;
+    const int i0 = qt * 32 * pg.rb;
+    // the rows of this workgroup's pairs: row blocks (4 jw) / G .. (4 jw + 3) / G
+    const int wg_row0 = i0 + 32 * ((4 * jw) / G);
+    if (wg_row0 >= sq) return;
+    const int wg_row_end = min(i0 + 32 * ((4 * jw + 3) / G + 1), sq);
     const int sk = a.cu_k[s + 1] - a.cu_k[s];
     const int off = sk - sq;
     const int W = a.window;
-    const int rows_end = min(i0 + BM, sq);
+    const int rows_end = sq;
 
     const int tid = threadIdx.x;
     const int nwaves = blockDim.x >> 6;
@@ -140,19 +150,18 @@ __global__ __launch_bounds__(NBR == 4 ? 128 : 512) void prefill_bf16_kernel(cons
     const int lane = tid & 63;
     const int col = lane & 15;
     const int grp = lane >> 4;
-    const int hw = wave / RW;
-    const int rw = wave % RW;
-    const int hig = hc * pg.heads_per_wg + hw;  // head within the group
-    const bool wave_ok = hw < pg.heads_per_wg && hig < a.group;
-    const int h = g * a.group + hig;
+    const int pair = 4 * jw + wave;        // (head, row block) pair of this wave
+    const int hig = pair % G;              // head within the group
+    const bool wave_ok = pair < G * pg.rb;
+    const int h = g * G + hig;
     const int H = a.num_heads;
     const int Hkv = a.c.num_kv_heads;
 
-    // key range of the whole tile (union over its rows)
-    const int wg_lo = W > 0 ? max(0, off + i0 - W + 1) : 0;
-    const int wg_hi = min(off + rows_end - 1, sk - 1);
+    // key range of the whole workgroup (union over its rows)
+    const int wg_lo = W > 0 ? max(0, off + wg_row0 - W + 1) : 0;
+    const int wg_hi = min(off + wg_row_end - 1, sk - 1);
     // this wave's rows and key range
-    const int r0 = i0 + RPW * rw;
+    const int r0 = i0 + RPW * (pair / G);
     const int r_last = min(r0 + RPW - 1, rows_end - 1);
     const bool wave_active = wave_ok && r0 < rows_end;
     const int wv_hi = min(off + r_last, sk - 1);
@@ -465,55 +474,27 @@ __global__ __launch_bounds__(NBR == 4 ? 128 : 512) void prefill_bf16_kernel(cons
     }
 }
 
-// Launch shape: query rows per wave (16 * NBR) and keys per K/V tile.
-constexpr int kPrefillNBR = 2;
+// Launch shape: keys per K/V tile and K/V buffers in the copy ring.
 constexpr int kPrefillBN = 64;
 constexpr int kPrefillNBUF = 2;
-// every 16-key group of a tile needs a wave of its own to copy it
-static_assert(kPrefillBN / 16 <= (kPrefillNBR == 4 ? 2 : 4), "fewer waves than key groups per tile");
-
-template <int D, int NBR, int RW>
-static void launch_rw(const PrefillArgs& a, const PrefillGrid& pg, int threads, hipStream_t st) {
-    const int64_t nsg_pad = ((int64_t)pg.n_sg + 7) / 8 * 8;
-    const dim3 grid((unsigned)(nsg_pad * pg.n_qtiles));
-    hipLaunchKernelGGL((prefill_bf16_kernel<D, NBR, RW, kPrefillBN, kPrefillNBUF>), grid, dim3(threads), 0, st, a, pg);
-}
+// every 16-key group of a tile needs a wave of its own to copy it (4 waves per workgroup)
+static_assert(kPrefillBN / 16 <= 4, "fewer waves than key groups per tile");
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t st) {
     const int G = a.group;
-    constexpr int NBR = kPrefillNBR;
+    // 32 query rows per wave, 4 waves per workgroup, two workgroups per CU (measured: two
+    // independent 4-wave workgroups per CU beat one workgroup of 5..8 waves)
     PrefillGrid pg;
-    int RW, threads;
-    if (NBR == 4) {
-        // 64 query rows per wave, 2 waves per workgroup (two heads of the group, or two row
-        // halves of one head when G = 1): each K/V byte read from LDS feeds 64 rows of MFMA
-        // work, and two workgroups per CU overlap one's tile-copy start with the other's math
-        RW = G >= 2 ? 1 : 2;
-        pg.heads_per_wg = G >= 2 ? 2 : 1;
-        threads = 128;
-    } else {
-        // 32 rows per wave, 4 waves per workgroup so that two workgroups share a CU
-        // (measured: two independent 4-wave workgroups per CU beat one workgroup of 5..8
-        // waves); a group of more than 4 heads is split into workgroups of at most 4 heads,
-        // each copying the K/V tiles itself (the second copy comes from the L2 / MALL)
-        RW = G >= 4 ? 1 : (G >= 2 ? 2 : 4);
-        const int chunks = G >= 4 ? (G + 3) / 4 : 1;
-        pg.heads_per_wg = G >= 4 ? (G + chunks - 1) / chunks : G;
-        threads = 64 * RW * pg.heads_per_wg < 256 ? 256 : 64 * RW * pg.heads_per_wg;
-    }
-    pg.n_head_chunks = (G + pg.heads_per_wg - 1) / pg.heads_per_wg;
-    pg.n_sg = a.num_seqs * a.c.num_kv_heads * pg.n_head_chunks;
-    const int BM = 16 * NBR * RW;
-    pg.n_qtiles = (a.max_seqlen_q + BM - 1) / BM;
-    if (a.c.head_size == 128) {
-        if (RW == 1) launch_rw<128, NBR, 1>(a, pg, threads, st);
-        else if (RW == 2) launch_rw<128, NBR, 2>(a, pg, threads, st);
-        else launch_rw<128, NBR, 4>(a, pg, threads, st);
-    } else {
-        if (RW == 1) launch_rw<64, NBR, 1>(a, pg, threads, st);
-        else if (RW == 2) launch_rw<64, NBR, 2>(a, pg, threads, st);
-        else launch_rw<64, NBR, 4>(a, pg, threads, st);
-    }
+    pg.rb = (G % 4 == 0) ? 1 : (G % 2 == 0 ? 2 : 4);
+    pg.wgs_per_tile = G * pg.rb / 4;
+    pg.n_sg = a.num_seqs * a.c.num_kv_heads;
+    pg.n_tiles = (a.max_seqlen_q + 32 * pg.rb - 1) / (32 * pg.rb) * pg.wgs_per_tile;
+    const int64_t nsg_pad = ((int64_t)pg.n_sg + 7) / 8 * 8;
+    const dim3 grid((unsigned)(nsg_pad * pg.n_tiles));
+    if (a.c.head_size == 128)
+        hipLaunchKernelGGL((prefill_bf16_kernel<128, 2, kPrefillBN, kPrefillNBUF>), grid, dim3(256), 0, st, a, pg);
+    else
+        hipLaunchKernelGGL((prefill_bf16_kernel<64, 2, kPrefillBN, kPrefillNBUF>), grid, dim3(256), 0, st, a, pg);
     return hipGetLastError();
 }
 
