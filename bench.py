@@ -106,7 +106,9 @@ def copy_bytes(op, wl) -> float:
 class Step:
     """Device-resident inputs of one phase and a callable that runs it."""
 
-    def __init__(self, wl, ops, dev, partition_size=0):
+    def __init__(self, wl, ops, dev, partition_size=0, fused=False):
+        """fused: every attention op runs as its *_with_store call on its own rows of the
+        phase's store (the separate store op is dropped)."""
         import numpy as np
         import torch
         import paged_attention_block_amd as pa
@@ -115,9 +117,16 @@ class Step:
         i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)  # noqa: E731
         self.cache = wl.kv_cache.to(dev)
         self.prepared = []
+        store = next((op for op in ops if type(op).__name__ == "StoreOp"), None)
         for op in ops:
             d = {"op": op}
             name = type(op).__name__
+            if fused and name == "StoreOp":
+                continue
+            if fused and name in ("PrefillOp", "DecodeOp"):
+                d["fused"] = True
+                d.update(nk=store.key[op.out_rows].to(dev), nv=store.value[op.out_rows].to(dev),
+                         nslots=i32(store.slot_mapping[op.out_rows]))
             if name == "CopyOp":
                 d["pairs"] = i32(op.pairs)
             elif name == "StoreOp":
@@ -143,9 +152,17 @@ class Step:
             pa.pa_copy_blocks(self.cache, d["pairs"])
         elif name == "StoreOp":
             pa.pa_store_kv(d["k"], d["v"], self.cache, d["slots"])
+        elif name == "PrefillOp" and d.get("fused"):
+            pa.pa_prefill_varlen_with_store(d["q"], d["nk"], d["nv"], d["nslots"], self.cache, d["table"],
+                                            d["cuq"], d["cuk"], op.max_seqlen_q, op.max_seqlen_k, wl.scale,
+                                            wl.num_kv_heads, wl.sliding_window, out=d["out"])
         elif name == "PrefillOp":
             pa.pa_prefill_varlen(d["q"], self.cache, d["table"], d["cuq"], d["cuk"], op.max_seqlen_q,
                                  op.max_seqlen_k, wl.scale, wl.num_kv_heads, wl.sliding_window, out=d["out"])
+        elif name == "DecodeOp" and d.get("fused"):
+            pa.pa_decode_with_store(d["q"], d["nk"], d["nv"], d["nslots"], self.cache, d["table"], d["lens"],
+                                    op.max_seq_len, wl.scale, wl.num_kv_heads, wl.sliding_window,
+                                    out=d["out"], workspace=d["ws"], partition_size=d["part"])
         elif name == "DecodeOp":
             pa.pa_decode(d["q"], self.cache, d["table"], d["lens"], op.max_seq_len, wl.scale,
                          wl.num_kv_heads, wl.sliding_window, out=d["out"], workspace=d["ws"],
@@ -302,32 +319,42 @@ def _workload(n):
     return W.config(n)
 
 
-def bench_workload(name, steps, warmup, dev, with_cpu, partition_size=0, flush_mb=1024):
+def bench_workload(name, steps, warmup, dev, with_cpu, partition_size=0, flush_mb=1024, fused=False):
     import workloads as W
     wl = _workload(WORKLOAD_CONFIG[name])
     phase = wl.phases[-1] if name == "chunked_decode" else wl.phases[0]
-    step = Step(wl, phase, dev, partition_size)
+    step = Step(wl, phase, dev, partition_size, fused)
     step_t, per_op, wall = step.time(steps, warmup, flush_mb * 1024 * 1024)
     ops = [d["op"] for d in step.prepared]
     res = {"workload": W.CONFIG_NAMES[WORKLOAD_CONFIG[name]], "ms_per_step": round(step_t * 1e3, 4),
            "wall_ms_per_step": round(wall * 1e3, 4), "cache_eviction_MiB_per_step": flush_mb, "ops": {}}
     total_bytes, total_flops = 0.0, 0.0
-    for op, t in zip(ops, per_op):
+    for op, t, d in zip(ops, per_op, step.prepared):
         n = type(op).__name__
+        fused = bool(d.get("fused"))
+        # a fused call also does the store of its rows: its bytes count toward the step
+        sb = 0.0
+        if fused:
+            rows = d["nk"].shape[0]
+            elt = 2 if wl.dtype.itemsize == 2 else 4
+            sb = float(2 * 2 * rows * wl.num_kv_heads * wl.head_size * elt + 4 * rows)
+            total_bytes += sb
         if n == "DecodeOp":
             b = decode_bytes(op, wl)
             total_bytes += b
-            res["ops"]["decode"] = {"ms": round(t * 1e3, 4), "GB/s": round(b / t / 1e9, 1),
-                                    "bytes": b, "tokens_per_s": round(len(op.seq_lens) / t, 1),
-                                    "partition_size": step.prepared[ops.index(op)]["part"] or "auto",
-                                    "roofline": roofline(b / t / 1e9, HBM_PEAK_GBS, "GB/s", "hbm",
-                                                         read_traffic("decode") if name == "decode" else None)}
+            res["ops"]["decode_with_store" if fused else "decode"] = {
+                "ms": round(t * 1e3, 4), "GB/s": round((b + sb) / t / 1e9, 1),
+                "bytes": b + sb, "tokens_per_s": round(len(op.seq_lens) / t, 1),
+                "partition_size": d["part"] or "auto",
+                "roofline": roofline((b + sb) / t / 1e9, HBM_PEAK_GBS, "GB/s", "hbm",
+                                     read_traffic("decode") if name == "decode" and not fused else None)}
         elif n == "PrefillOp":
             f = prefill_flops(op, wl)
             total_flops += f
-            res["ops"]["prefill"] = {"ms": round(t * 1e3, 4), "TFLOP/s": round(f / t / 1e12, 2), "flops": f,
-                                     "roofline": roofline(f / t / 1e12, BF16_PEAK_TFLOPS, "TFLOP/s", "mfma",
-                                                          read_traffic("prefill") if name == "prefill" else None)}
+            res["ops"]["prefill_with_store" if fused else "prefill"] = {
+                "ms": round(t * 1e3, 4), "TFLOP/s": round(f / t / 1e12, 2), "flops": f,
+                "roofline": roofline(f / t / 1e12, BF16_PEAK_TFLOPS, "TFLOP/s", "mfma",
+                                     read_traffic("prefill") if name == "prefill" and not fused else None)}
         elif n == "StoreOp":
             b = store_bytes(op, wl)
             total_bytes += b
@@ -407,6 +434,14 @@ def main() -> int:
                            "roofline": pre["ops"]["prefill"]["roofline"],
                            "cpu_baseline": pre.get("cpu_baseline")}
     if args.workload == "decode" and not args.no_secondary:
+        # the same two steps with the store fused into the attention call
+        line["with_store"] = {}
+        for name in ("decode", "prefill"):
+            r = bench_workload(name, 20, 5, dev, False, flush_mb=args.flush_mb, fused=True)
+            line["with_store"][name] = {"workload": r["workload"], "ms_per_step": r["ms_per_step"],
+                                        "step_GB/s" if name == "decode" else "step_TFLOP/s":
+                                        r["step_GB/s"] if name == "decode" else r["step_TFLOP/s"],
+                                        "ops": r["ops"]}
         # the other two workloads, every op with its roofline (no CPU baseline): chunked prefill
         # with a 4096-key window and the decode after it (config 4), and the mixed step
         # copy_blocks -> store -> prefill -> decode (config 5)

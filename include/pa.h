@@ -6,6 +6,8 @@
  *   pa_copy_blocks     duplicate physical blocks of both cache planes
  *   pa_prefill_varlen  varlen causal attention (chunked, optional sliding window)
  *   pa_decode          grouped-query decode, one query per sequence, split-K
+ *   pa_prefill_varlen_with_store, pa_decode_with_store
+ *                      the store of the new tokens and the attention in one call
  *
  * Conventions shared by every entry point
  *   - All tensor arguments are DEVICE pointers, caller-allocated and caller-owned; the
@@ -117,6 +119,33 @@ int pa_prefill_varlen(const pa_cache_desc* cache, void* out, const void* query,
                       int32_t num_heads, float scale, int32_t sliding_window, void* stream);
 
 /*
+ * pa_prefill_varlen_with_store — pa_store_kv of the batch's new tokens, then
+ * pa_prefill_varlen, as one call.
+ *
+ * vLLM learning book, "05. Attention Backends", section 5 (FlashAttentionImpl.forward) and
+ * the section-10 question on how K/V reach the cache: the attention kernel itself writes the
+ * new tokens' K/V at their slot_mapping slots, saving the separate store launch.  Here, for
+ * bf16 caches, the prefill kernel takes the new keys straight from key/value (they are the
+ * last seqlen_q keys of each sequence) and writes them to the cache as it goes; float32 caches
+ * run the store and the attention back to back.
+ *
+ *   key, value    [num_tokens][num_kv_heads][head_size], row t = query row t, cache dtype
+ *   slot_mapping  [num_tokens] int32: the cache slot of each row's token
+ *   num_tokens    == cu_seqlens_q[num_seqs] (the rows of query, key and value)
+ * Other arguments as pa_prefill_varlen.  Precondition (as in the paged layout everywhere):
+ * the slot of the new token at key position j of sequence s is the block-table position of
+ * j, so attending the stored cache and attending key/value give the same keys.  Result and
+ * cache contents equal pa_store_kv followed by pa_prefill_varlen.
+ */
+int pa_prefill_varlen_with_store(const pa_cache_desc* cache, void* out, const void* query,
+                                 const void* key, const void* value, const int32_t* slot_mapping,
+                                 int32_t num_tokens, const int32_t* block_table,
+                                 int32_t max_blocks_per_seq, const int32_t* cu_seqlens_q,
+                                 const int32_t* cu_seqlens_k, int32_t num_seqs, int32_t max_seqlen_q,
+                                 int32_t max_seqlen_k, int32_t num_heads, float scale,
+                                 int32_t sliding_window, void* stream);
+
+/*
  * pa_decode_workspace_size — bytes of device workspace pa_decode needs for these sizes
  * (0 when the batch is too small to be split, and for float32 caches).  With
  * partition_size 0 the size depends on how many decode workgroups the current device
@@ -153,6 +182,20 @@ int pa_decode(const pa_cache_desc* cache, void* out, const void* query,
               int32_t num_heads, float scale, int32_t sliding_window,
               int32_t partition_size, void* workspace, size_t workspace_bytes,
               void* stream);
+
+/*
+ * pa_decode_with_store — pa_store_kv of each sequence's new token, then pa_decode, as one
+ * call (same source as pa_prefill_varlen_with_store).  key, value [num_seqs][num_kv_heads]
+ * [head_size] and slot_mapping [num_seqs]: the token just produced by each sequence, which
+ * seq_lens already counts.  Other arguments as pa_decode.  Runs the store kernel and the decode
+ * kernels back to back on the stream.
+ */
+int pa_decode_with_store(const pa_cache_desc* cache, void* out, const void* query, const void* key,
+                         const void* value, const int32_t* slot_mapping, const int32_t* block_table,
+                         int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t num_seqs,
+                         int32_t max_seq_len, int32_t num_heads, float scale, int32_t sliding_window,
+                         int32_t partition_size, void* workspace, size_t workspace_bytes,
+                         void* stream);
 
 /* Fixed text for a status code. */
 const char* pa_status_string(int status);

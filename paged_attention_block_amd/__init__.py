@@ -21,7 +21,7 @@ import torch
 
 __all__ = [
     "PaError", "lib_path", "load", "pa_store_kv", "pa_copy_blocks", "pa_prefill_varlen",
-    "pa_decode", "pa_decode_workspace_size",
+    "pa_decode", "pa_decode_workspace_size", "pa_prefill_varlen_with_store", "pa_decode_with_store",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -70,7 +70,11 @@ def load() -> ctypes.CDLL:
     lib.pa_decode_workspace_size.argtypes = [D, I32, I32, I32, I32, I32]
     lib.pa_decode_workspace_size.restype = SZ
     lib.pa_decode.argtypes = [D, P, P, P, I32, P, I32, I32, I32, F32, I32, I32, P, SZ, P]
-    for name in ("pa_store_kv", "pa_copy_blocks", "pa_prefill_varlen", "pa_decode"):
+    lib.pa_prefill_varlen_with_store.argtypes = [D, P, P, P, P, P, I32, P, I32, P, P, I32, I32, I32, I32,
+                                                 F32, I32, P]
+    lib.pa_decode_with_store.argtypes = [D, P, P, P, P, P, P, I32, P, I32, I32, I32, F32, I32, I32, P, SZ, P]
+    for name in ("pa_store_kv", "pa_copy_blocks", "pa_prefill_varlen", "pa_decode",
+                 "pa_prefill_varlen_with_store", "pa_decode_with_store"):
         getattr(lib, name).restype = ctypes.c_int
     lib.pa_status_string.argtypes = [ctypes.c_int]
     lib.pa_status_string.restype = ctypes.c_char_p
@@ -237,4 +241,96 @@ def pa_decode(query: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Te
                              block_table.shape[1], _ptr(seq_lens), num_seqs, int(max_seq_len),
                              query.shape[1], float(scale), int(sliding_window), int(partition_size),
                              _ptr(workspace), ws_bytes, _stream(kv_cache)), "pa_decode")
+    return out
+
+
+def _new_rows(key: torch.Tensor, value: torch.Tensor, slot_mapping: torch.Tensor, kv_cache: torch.Tensor,
+              rows: int) -> None:
+    dev = kv_cache.device
+    _need(key, "key", kv_cache.dtype, dev, 3)
+    _need(value, "value", kv_cache.dtype, dev, 3)
+    _need(slot_mapping, "slot_mapping", torch.int32, dev, 1)
+    want = (rows, kv_cache.shape[3], kv_cache.shape[4])
+    if tuple(key.shape) != want or tuple(value.shape) != want or slot_mapping.shape[0] != rows:
+        raise ValueError(f"key/value must be {want} and slot_mapping [{rows}]")
+
+
+def pa_prefill_varlen_with_store(query: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
+                                 slot_mapping: torch.Tensor, kv_cache: torch.Tensor,
+                                 block_table: torch.Tensor, cu_seqlens_q: torch.Tensor,
+                                 cu_seqlens_k: torch.Tensor, max_seqlen_q: int, max_seqlen_k: int,
+                                 scale: float, num_kv_heads: int, sliding_window: int = 0,
+                                 out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Store the batch's new tokens (``key``/``value [Tq, Hkv, D]`` at ``slot_mapping``) and run
+    the varlen causal attention of ``query [Tq, H, D]`` in one call (one kernel for bf16)."""
+    lib = load()
+    desc = _desc(kv_cache)
+    dev = kv_cache.device
+    if num_kv_heads != kv_cache.shape[3]:
+        raise ValueError(f"num_kv_heads {num_kv_heads} != cache's {kv_cache.shape[3]}")
+    _need(query, "query", kv_cache.dtype, dev, 3)
+    _need(block_table, "block_table", torch.int32, dev, 2)
+    _need(cu_seqlens_q, "cu_seqlens_q", torch.int32, dev, 1)
+    _need(cu_seqlens_k, "cu_seqlens_k", torch.int32, dev, 1)
+    _new_rows(key, value, slot_mapping, kv_cache, query.shape[0])
+    num_seqs = cu_seqlens_q.shape[0] - 1
+    if cu_seqlens_k.shape[0] != num_seqs + 1 or block_table.shape[0] < num_seqs:
+        raise ValueError("cu_seqlens_q/k must be [num_seqs + 1] and block_table [num_seqs, max_blocks]")
+    if query.shape[2] != kv_cache.shape[4]:
+        raise ValueError("query head_size does not match the cache")
+    if out is None:
+        out = torch.empty_like(query)
+    else:
+        _need(out, "out", kv_cache.dtype, dev, 3)
+        if out.shape != query.shape:
+            raise ValueError("out must match query's shape")
+    _check(lib.pa_prefill_varlen_with_store(ctypes.byref(desc), _ptr(out), _ptr(query), _ptr(key), _ptr(value),
+                                            _ptr(slot_mapping), query.shape[0], _ptr(block_table),
+                                            block_table.shape[1], _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
+                                            num_seqs, int(max_seqlen_q), int(max_seqlen_k), query.shape[1],
+                                            float(scale), int(sliding_window), _stream(kv_cache)),
+           "pa_prefill_varlen_with_store")
+    return out
+
+
+def pa_decode_with_store(query: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
+                         slot_mapping: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
+                         seq_lens: torch.Tensor, max_seq_len: int, scale: float, num_kv_heads: int,
+                         sliding_window: int = 0, out: Optional[torch.Tensor] = None,
+                         workspace: Optional[torch.Tensor] = None, partition_size: int = 0) -> torch.Tensor:
+    """Store each sequence's new token (``key``/``value [B, Hkv, D]`` at ``slot_mapping``) and
+    decode ``query [B, H, D]`` over the ``seq_lens[s]`` keys that include it, in one call."""
+    lib = load()
+    desc = _desc(kv_cache)
+    dev = kv_cache.device
+    if num_kv_heads != kv_cache.shape[3]:
+        raise ValueError(f"num_kv_heads {num_kv_heads} != cache's {kv_cache.shape[3]}")
+    _need(query, "query", kv_cache.dtype, dev, 3)
+    _need(block_table, "block_table", torch.int32, dev, 2)
+    _need(seq_lens, "seq_lens", torch.int32, dev, 1)
+    num_seqs = query.shape[0]
+    _new_rows(key, value, slot_mapping, kv_cache, num_seqs)
+    if seq_lens.shape[0] != num_seqs or block_table.shape[0] < num_seqs:
+        raise ValueError("seq_lens must be [num_seqs] and block_table [num_seqs, max_blocks]")
+    if query.shape[2] != kv_cache.shape[4]:
+        raise ValueError("query head_size does not match the cache")
+    if out is None:
+        out = torch.empty_like(query)
+    else:
+        _need(out, "out", kv_cache.dtype, dev, 3)
+        if out.shape != query.shape:
+            raise ValueError("out must match query's shape")
+    need = pa_decode_workspace_size(kv_cache, num_seqs, query.shape[1], int(max_seq_len),
+                                    int(sliding_window), int(partition_size))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if workspace is not None and workspace.device != dev:
+        raise ValueError("workspace must be on the cache's device")
+    with (torch.cuda.device(dev) if dev.type == "cuda" else contextlib.nullcontext()):
+        _check(lib.pa_decode_with_store(ctypes.byref(desc), _ptr(out), _ptr(query), _ptr(key), _ptr(value),
+                                        _ptr(slot_mapping), _ptr(block_table), block_table.shape[1],
+                                        _ptr(seq_lens), num_seqs, int(max_seq_len), query.shape[1],
+                                        float(scale), int(sliding_window), int(partition_size),
+                                        _ptr(workspace), ws_bytes, _stream(kv_cache)), "pa_decode_with_store")
     return out

@@ -158,18 +158,20 @@ int pa_copy_blocks(const pa_cache_desc* cache, const int32_t* block_pairs, int32
     return launch_status(pa::launch_copy_blocks(a, (hipStream_t)stream));
 }
 
-int pa_prefill_varlen(const pa_cache_desc* cache, void* out, const void* query,
-                      const int32_t* block_table, int32_t max_blocks_per_seq,
-                      const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
-                      int32_t num_seqs, int32_t max_seqlen_q, int32_t max_seqlen_k,
-                      int32_t num_heads, float scale, int32_t sliding_window, void* stream) {
-    pa::PrefillArgs a;
+static int prefill_args(const pa_cache_desc* cache, void* out, const void* query,
+                        const int32_t* block_table, int32_t max_blocks_per_seq,
+                        const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                        int32_t num_seqs, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                        int32_t num_heads, float scale, int32_t sliding_window, pa::PrefillArgs* pa_out,
+                        bool* empty) {
+    pa::PrefillArgs& a = *pa_out;
+    *empty = false;
     int st = check_cache(cache, &a.c);
     if (st) return st;
     if ((st = check_heads(a.c, num_heads))) return st;
     if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs must be >= 0 (got %d)", num_seqs);
     if (max_seqlen_q < 0 || max_seqlen_k < 0) return fail(PA_ERR_INVALID_ARG, "max_seqlen_q/k must be >= 0");
-    if (num_seqs == 0 || max_seqlen_q == 0) { g_last_error[0] = 0; return PA_OK; }
+    if (num_seqs == 0 || max_seqlen_q == 0) { *empty = true; return PA_OK; }
     if (!out || !query || !block_table || !cu_seqlens_q || !cu_seqlens_k)
         return fail(PA_ERR_INVALID_ARG, "out, query, block_table, cu_seqlens_q and cu_seqlens_k must be non-NULL");
     if (max_blocks_per_seq < 1) return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq must be >= 1");
@@ -192,8 +194,65 @@ int pa_prefill_varlen(const pa_cache_desc* cache, void* out, const void* query,
     a.group = num_heads / a.c.num_kv_heads;
     a.scale = scale;
     a.window = sliding_window > 0 ? sliding_window : 0;
+    a.knew = nullptr;
+    a.vnew = nullptr;
+    a.slots = nullptr;
+    return PA_OK;
+}
+
+int pa_prefill_varlen(const pa_cache_desc* cache, void* out, const void* query,
+                      const int32_t* block_table, int32_t max_blocks_per_seq,
+                      const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                      int32_t num_seqs, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                      int32_t num_heads, float scale, int32_t sliding_window, void* stream) {
+    pa::PrefillArgs a;
+    bool empty;
+    int st = prefill_args(cache, out, query, block_table, max_blocks_per_seq, cu_seqlens_q, cu_seqlens_k,
+                          num_seqs, max_seqlen_q, max_seqlen_k, num_heads, scale, sliding_window, &a, &empty);
+    if (st) return st;
+    if (empty) { g_last_error[0] = 0; return PA_OK; }
     hipStream_t s = (hipStream_t)stream;
     return launch_status(a.c.dtype == PA_BF16 ? pa::launch_prefill_bf16(a, s) : pa::launch_prefill_f32(a, s));
+}
+
+int pa_prefill_varlen_with_store(const pa_cache_desc* cache, void* out, const void* query,
+                                 const void* key, const void* value, const int32_t* slot_mapping,
+                                 int32_t num_tokens, const int32_t* block_table,
+                                 int32_t max_blocks_per_seq, const int32_t* cu_seqlens_q,
+                                 const int32_t* cu_seqlens_k, int32_t num_seqs, int32_t max_seqlen_q,
+                                 int32_t max_seqlen_k, int32_t num_heads, float scale,
+                                 int32_t sliding_window, void* stream) {
+    pa::PrefillArgs a;
+    bool empty;
+    int st = prefill_args(cache, out, query, block_table, max_blocks_per_seq, cu_seqlens_q, cu_seqlens_k,
+                          num_seqs, max_seqlen_q, max_seqlen_k, num_heads, scale, sliding_window, &a, &empty);
+    if (st) return st;
+    if (num_tokens < 0) return fail(PA_ERR_INVALID_ARG, "num_tokens must be >= 0 (got %d)", num_tokens);
+    if (num_tokens > 0 && (!key || !value || !slot_mapping))
+        return fail(PA_ERR_INVALID_ARG, "key, value and slot_mapping must be non-NULL");
+    if (empty || num_tokens == 0) {
+        if (num_tokens == 0 && !empty)
+            return fail(PA_ERR_INVALID_ARG, "num_tokens is 0 but the batch has query rows");
+        g_last_error[0] = 0;
+        return PA_OK;
+    }
+    hipStream_t s = (hipStream_t)stream;
+    if (a.c.dtype == PA_BF16) {
+        a.knew = key;
+        a.vnew = value;
+        a.slots = slot_mapping;
+        return launch_status(pa::launch_prefill_bf16(a, s));
+    }
+    // float32 correctness path: the store, then the attention, on the same stream
+    pa::StoreArgs sa;
+    sa.c = a.c;
+    sa.key = key;
+    sa.value = value;
+    sa.slots = slot_mapping;
+    sa.num_tokens = num_tokens;
+    hipError_t e = pa::launch_store(sa, s);
+    if (e != hipSuccess) return launch_status(e);
+    return launch_status(pa::launch_prefill_f32(a, s));
 }
 
 size_t pa_decode_workspace_size(const pa_cache_desc* cache, int32_t num_seqs, int32_t num_heads,
@@ -207,17 +266,21 @@ size_t pa_decode_workspace_size(const pa_cache_desc* cache, int32_t num_seqs, in
     return (size_t)c.nw * 2 * num_heads * ((size_t)cache->head_size + 2) * sizeof(float);
 }
 
-int pa_decode(const pa_cache_desc* cache, void* out, const void* query, const int32_t* block_table,
-              int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t num_seqs,
-              int32_t max_seq_len, int32_t num_heads, float scale, int32_t sliding_window,
-              int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream) {
-    pa::DecodeArgs a;
+// Validation and launch planning shared by pa_decode and pa_decode_with_store; *empty is
+// set when there is nothing to launch.
+static int decode_args(const pa_cache_desc* cache, void* out, const void* query, const int32_t* block_table,
+                       int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t num_seqs,
+                       int32_t max_seq_len, int32_t num_heads, float scale, int32_t sliding_window,
+                       int32_t partition_size, void* workspace, size_t workspace_bytes,
+                       pa::DecodeArgs* a_out, bool* empty) {
+    pa::DecodeArgs& a = *a_out;
+    *empty = false;
     int st = check_cache(cache, &a.c);
     if (st) return st;
     if ((st = check_heads(a.c, num_heads))) return st;
     if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs must be >= 0 (got %d)", num_seqs);
     if (max_seq_len < 0) return fail(PA_ERR_INVALID_ARG, "max_seq_len must be >= 0");
-    if (num_seqs == 0) { g_last_error[0] = 0; return PA_OK; }
+    if (num_seqs == 0) { *empty = true; return PA_OK; }
     if (!out || !query || !block_table || !seq_lens)
         return fail(PA_ERR_INVALID_ARG, "out, query, block_table and seq_lens must be non-NULL");
     if (max_blocks_per_seq < 1) return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq must be >= 1");
@@ -238,13 +301,12 @@ int pa_decode(const pa_cache_desc* cache, void* out, const void* query, const in
     a.num_heads = num_heads;
     a.group = num_heads / a.c.num_kv_heads;
     a.scale = scale;
-    a.window = sliding_window > 0 ? sliding_window : 0;
-    hipStream_t s = (hipStream_t)stream;
+    a.window = win;
     a.nw = 1;
     a.min_steps = 1;
     a.ws_o = nullptr;
     a.ws_ml = nullptr;
-    if (a.c.dtype == PA_F32) return launch_status(pa::launch_decode_f32(a, s));
+    if (a.c.dtype == PA_F32) return PA_OK;
     if (a.c.num_kv_heads > 65535) return fail(PA_ERR_INVALID_ARG, "num_kv_heads too large");
     const size_t need = pa_decode_workspace_size(cache, num_seqs, num_heads, max_seq_len, sliding_window, partition_size);
     if (need > 0 && (!workspace || workspace_bytes < need))
@@ -257,7 +319,45 @@ int pa_decode(const pa_cache_desc* cache, void* out, const void* query, const in
         a.ws_o = (float*)workspace;
         a.ws_ml = a.ws_o + (size_t)c.nw * 2 * num_heads * a.c.head_size;
     }
-    return launch_status(pa::launch_decode_bf16(a, s));
+    return PA_OK;
+}
+
+int pa_decode(const pa_cache_desc* cache, void* out, const void* query, const int32_t* block_table,
+              int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t num_seqs,
+              int32_t max_seq_len, int32_t num_heads, float scale, int32_t sliding_window,
+              int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream) {
+    pa::DecodeArgs a;
+    bool empty;
+    int st = decode_args(cache, out, query, block_table, max_blocks_per_seq, seq_lens, num_seqs, max_seq_len,
+                         num_heads, scale, sliding_window, partition_size, workspace, workspace_bytes, &a, &empty);
+    if (st) return st;
+    if (empty) { g_last_error[0] = 0; return PA_OK; }
+    hipStream_t s = (hipStream_t)stream;
+    return launch_status(a.c.dtype == PA_F32 ? pa::launch_decode_f32(a, s) : pa::launch_decode_bf16(a, s));
+}
+
+int pa_decode_with_store(const pa_cache_desc* cache, void* out, const void* query, const void* key,
+                         const void* value, const int32_t* slot_mapping, const int32_t* block_table,
+                         int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t num_seqs,
+                         int32_t max_seq_len, int32_t num_heads, float scale, int32_t sliding_window,
+                         int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream) {
+    pa::DecodeArgs a;
+    bool empty;
+    int st = decode_args(cache, out, query, block_table, max_blocks_per_seq, seq_lens, num_seqs, max_seq_len,
+                         num_heads, scale, sliding_window, partition_size, workspace, workspace_bytes, &a, &empty);
+    if (st) return st;
+    if (empty) { g_last_error[0] = 0; return PA_OK; }
+    if (!key || !value || !slot_mapping) return fail(PA_ERR_INVALID_ARG, "key, value and slot_mapping must be non-NULL");
+    hipStream_t s = (hipStream_t)stream;
+    pa::StoreArgs sa;
+    sa.c = a.c;
+    sa.key = key;
+    sa.value = value;
+    sa.slots = slot_mapping;
+    sa.num_tokens = num_seqs;
+    hipError_t e = pa::launch_store(sa, s);
+    if (e != hipSuccess) return launch_status(e);
+    return launch_status(a.c.dtype == PA_F32 ? pa::launch_decode_f32(a, s) : pa::launch_decode_bf16(a, s));
 }
 
 }  // extern "C"

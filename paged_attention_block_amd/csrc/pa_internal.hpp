@@ -90,6 +90,13 @@ struct PrefillArgs {
     int32_t group;       // num_heads / num_kv_heads
     float scale;
     int32_t window;
+    // fused store (null when the call only attends): the new tokens' keys and values,
+    // [tokens][Hkv][D] in query-row order, and their slots.  Keys at positions >= seqlen_k -
+    // seqlen_q of a sequence are its new tokens: they are read from here, and written to the
+    // cache at their slots by the kernel.
+    const void* knew;
+    const void* vnew;
+    const int32_t* slots;
 };
 
 struct DecodeArgs {

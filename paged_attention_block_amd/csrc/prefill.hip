@@ -56,6 +56,14 @@ __device__ __forceinline__ void copy_to_lds16(const void* base, uint32_t voff, u
                  : "memory", "m0");
 }
 
+// the same copy from a per-lane 64-bit address
+__device__ __forceinline__ void copy_to_lds16_lane(const void* gptr, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(gptr), "s"(lds)
+                 : "memory", "m0");
+}
+
 // s_waitcnt vmcnt(n) for a wave-uniform n (the count is an instruction immediate; counts
 // above 23 wait for everything, which is always safe)
 __device__ __forceinline__ void wait_vmcnt(int n) {
@@ -238,25 +246,70 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const PrefillArgs 
         my_copies += (copier && ig < IPG) ? 2 : 0;
     }
 
-    // byte offset in a plane of the first token row of this wave's group of the tile at k0
-    // (KV head 0).  A group with no live key takes the rows of the tile's first live group
-    // instead, so no block-table entry outside the live range is read.
-    auto group_base = [&](int k0) -> int64_t {
+    // Source of this wave's 16-key group of the tile at k0 (wave-uniform).  A group with no
+    // live key takes the rows of the tile's first live group instead, so no block-table entry
+    // outside the live range is read.  Keys below `off` come from the cache through the block
+    // table; with a fused store, keys from `off` on are the sequence's new tokens and come
+    // from the caller's key/value rows (same row layout as a cache plane).  A group that
+    // straddles `off` or runs past the last key is copied with per-lane addresses, clamped to
+    // the sequence's rows (rows past the last key are zeroed after the copy).
+    const char* knew = (const char*)a.knew;
+    const char* vnew = (const char*)a.vnew;
+    const bool fused = knew != nullptr;
+    struct GroupSrc {
+        const char* k;   // uniform base (non-mixed) of the group's first row, KV head 0
+        const char* v;
+        int64_t gb;      // cache offset of the group's block rows (mixed groups)
+        int j0;          // first key of the group copied
+        bool mixed;
+    };
+    auto group_src = [&](int k0) -> GroupSrc {
+        GroupSrc r;
         const int j0 = k0 + 16 * cga;
         const bool live = (j0 <= wg_hi) && (j0 + 15 >= wg_lo);
-        const int src = live ? j0 : (max(k0, wg_lo) & ~15);
-        const int blk = table[src >> shift];
-        return ((int64_t)blk * BS + (src & (BS - 1))) * RB;
+        r.j0 = live ? j0 : (max(k0, wg_lo) & ~15);
+        r.mixed = fused && r.j0 + 15 >= off && (r.j0 < off || r.j0 + 15 > sk - 1);
+        r.gb = 0;
+        if (!fused || r.j0 < off) {
+            const int blk = table[r.j0 >> shift];
+            r.gb = ((int64_t)blk * BS + (r.j0 & (BS - 1))) * RB;
+            r.k = kplane + r.gb;
+            r.v = kplane + vdelta + r.gb;
+        } else {
+            const int64_t row = (int64_t)q0 + r.j0 - off;
+            r.k = knew + row * RB;
+            r.v = vnew + row * RB;
+        }
+        return r;
     };
-    // copy this wave's share of one plane of a tile (group base gbase) into LDS buffer dst
-    auto issue = [&](const char* plane, int64_t gbase, const uint32_t (&cg)[IPG], char* dst) {
+    // copy this wave's share of one plane of a tile into LDS buffer dst
+    auto issue = [&](const GroupSrc& gs, bool vplane_, const uint32_t (&cg)[IPG], char* dst) {
         if (!copier) return;
-        const char* src = plane + gbase;
         const uint32_t lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)dst;
+        if (!gs.mixed) {
+            const char* src = vplane_ ? gs.v : gs.k;
 #pragma unroll
-        for (int jj = 0; jj < IPG; ++jj) {
-            const int ig = csub + nsub * jj;
-            if (ig < IPG) copy_to_lds16(src, cg[jj], lds + 1024u * (uint32_t)(IPG * cga + ig));
+            for (int jj = 0; jj < IPG; ++jj) {
+                const int ig = csub + nsub * jj;
+                if (ig < IPG) copy_to_lds16(src, cg[jj], lds + 1024u * (uint32_t)(IPG * cga + ig));
+            }
+        } else {
+#pragma unroll
+            for (int jj = 0; jj < IPG; ++jj) {
+                const int ig = csub + nsub * jj;
+                if (ig < IPG) {
+                    const int row = RPI * ig + crow;
+                    const int key = gs.j0 + row;
+                    const char* p;
+                    if (key < off) {
+                        p = kplane + (vplane_ ? vdelta : 0) + gs.gb + cg[jj];
+                    } else {
+                        const int64_t rn = (int64_t)q0 + min(key, sk - 1) - off;
+                        p = (vplane_ ? vnew : knew) + rn * RB + (cg[jj] - (uint32_t)row * (uint32_t)RB);
+                    }
+                    copy_to_lds16_lane(p, lds + 1024u * (uint32_t)(IPG * cga + ig));
+                }
+            }
         }
     };
     // after this wave's copies of a plane of the tile at k0 landed: zero the rows it copied
@@ -273,7 +326,6 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const PrefillArgs 
             }
         }
     };
-    const char* vplane = kplane + vdelta;
 
     // LDS operand addresses of this lane: K row 16*ga + col, chunk (4t + grp) swizzled by
     // the row, and (16*ga + col) & KSW == col & KSW, so only the 16*ga row offset depends on ga
@@ -388,6 +440,41 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const PrefillArgs 
         }
     };
 
+    // ---------------------------------------------------------------- fused store
+    // A new token's K/V rows reach LDS in the tiles around the diagonal of the q-tile that
+    // holds its query row.  In those steps the workgroup that holds the pair (row block, head
+    // 0) of the row writes the row (KV head g's part, both planes) from LDS to its cache slot
+    // (negative slots skipped): no extra global read, and the stores overlap the math.  The
+    // attention never reads these cache rows (it takes new keys from the caller's rows).
+    // the q-tile's slots, staged in LDS once (a global load inside the loop would make the
+    // compiler wait for every copy in flight); filled right after the first tile's copies are
+    // issued, so its wait overlaps theirs
+    __shared__ int lds_slots[128];
+    auto stage_slots = [&]() {
+        for (int i = tid; i < 32 * pg.rb; i += blockDim.x)
+            lds_slots[i] = i0 + i < sq ? a.slots[q0 + i0 + i] : -1;
+    };
+    auto store_new_rows = [&](int k0, const char* kc, const char* vc) {
+        const int ks = max(k0, off + wg_row0);
+        const int ke = min(k0 + BN, off + wg_row_end);
+        if (ks >= ke) return;
+        constexpr int CH = D * 2 / 16;  // 16-byte chunks per row and plane
+        for (int idx = tid; idx < (ke - ks) * CH; idx += blockDim.x) {
+            const int key = ks + idx / CH;
+            const int c = idx % CH;
+            const int i = key - off;                           // query row of the token
+            if (((i - i0) / 32 * G) / 4 != jw) continue;       // another workgroup's row block
+            const int slot = lds_slots[i - i0];
+            if (slot < 0) continue;
+            const int r = key - k0;                            // row in the tile
+            const u32x4 kx = *(const u32x4*)(kc + r * D * 2 + ((c ^ (r & KSW)) * 16));
+            const u32x4 vx = *(const u32x4*)(vc + r * D * 2 + ((c ^ ((2 * r) & VSW)) * 16));
+            const int64_t dst = ((int64_t)slot * Hkv + g) * D * 2 + c * 16;
+            *(u32x4*)((char*)a.c.kv + dst) = kx;
+            *(u32x4*)((char*)a.c.kv + vdelta + dst) = vx;
+        }
+    };
+
     // ---------------------------------------------------------------- main loop
     // A ring of NBUF buffer pairs: while tile kt computes, the copies of tiles kt+1 ..
     // kt+NBUF-1 are in flight.  Tile kt sits in buffer (kt - kt_begin) % NBUF; the loop body
@@ -416,10 +503,11 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const PrefillArgs 
         // barrier: that would also wait for the copies of the later tiles
         lds_barrier();
         if (kt + NBUF - 1 < kt_end) {
-            const int64_t gb = group_base(k0 + (NBUF - 1) * BN);
-            issue(kplane, gb, cgk, kbuf(std::integral_constant<int, jn>{}));
-            issue(vplane, gb, cgv, vbuf(std::integral_constant<int, jn>{}));
+            const GroupSrc gs = group_src(k0 + (NBUF - 1) * BN);
+            issue(gs, false, cgk, kbuf(std::integral_constant<int, jn>{}));
+            issue(gs, true, cgv, vbuf(std::integral_constant<int, jn>{}));
         }
+        if (fused) store_new_rows(k0, kc, vc);
         if (wave_active && k0 <= wv_hi && k0 + BN - 1 >= wv_lo) {
             f32x4 sacc[NGA][NBR];
             u32x4 pk[NCC][NBR];
@@ -433,20 +521,21 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const PrefillArgs 
         const int kt_begin = wg_lo / BN;
         const int kt_end = wg_hi / BN + 1;
         {
-            int64_t gb = group_base(kt_begin * BN);
-            issue(kplane, gb, cgk, lds_k0);
-            issue(vplane, gb, cgv, lds_v0);
+            GroupSrc gs = group_src(kt_begin * BN);
+            issue(gs, false, cgk, lds_k0);
+            issue(gs, true, cgv, lds_v0);
             if (NBUF > 2 && kt_begin + 1 < kt_end) {
-                gb = group_base((kt_begin + 1) * BN);
-                issue(kplane, gb, cgk, lds_k1);
-                issue(vplane, gb, cgv, lds_v1);
+                gs = group_src((kt_begin + 1) * BN);
+                issue(gs, false, cgk, lds_k1);
+                issue(gs, true, cgv, lds_v1);
             }
             if (NBUF > 3 && kt_begin + 2 < kt_end) {
-                gb = group_base((kt_begin + 2) * BN);
-                issue(kplane, gb, cgk, lds_k2);
-                issue(vplane, gb, cgv, lds_v2);
+                gs = group_src((kt_begin + 2) * BN);
+                issue(gs, false, cgk, lds_k2);
+                issue(gs, true, cgv, lds_v2);
             }
         }
+        if (fused) stage_slots();
         for (int kt = kt_begin; kt < kt_end; kt += NBUF) {
             step(kt, kt_end, std::integral_constant<int, 0>{});
             if (kt + 1 < kt_end) step(kt + 1, kt_end, std::integral_constant<int, 1>{});

@@ -83,6 +83,21 @@ class GpuRun:
                                 wl.sliding_window, partition_size=partition_size)
         raise TypeError(op)
 
+    def run_with_store(self, store, op, partition_size: int = 0):
+        """The store of ``op``'s rows of ``store`` and the attention ``op``, as one call."""
+        wl, d = self.wl, self.dev
+        k = store.key[op.out_rows].to(d)
+        v = store.value[op.out_rows].to(d)
+        sl = self.i32(store.slot_mapping[op.out_rows])
+        if isinstance(op, W.PrefillOp):
+            return pa.pa_prefill_varlen_with_store(op.query.to(d), k, v, sl, self.cache, self.i32(op.block_table),
+                                                   self.i32(op.cu_seqlens_q), self.i32(op.cu_seqlens_k),
+                                                   op.max_seqlen_q, op.max_seqlen_k, wl.scale, wl.num_kv_heads,
+                                                   wl.sliding_window)
+        return pa.pa_decode_with_store(op.query.to(d), k, v, sl, self.cache, self.i32(op.block_table),
+                                       self.i32(op.seq_lens), op.max_seq_len, wl.scale, wl.num_kv_heads,
+                                       wl.sliding_window, partition_size=partition_size)
+
 
 def oracle_attention(wl: W.Workload, op, cache_vals: np.ndarray, picks=None) -> np.ndarray:
     """Oracle output for a prefill/decode op; ``picks`` = list of (row, head) to sample."""

@@ -35,7 +35,7 @@ def _gpu():
     torch.cuda.synchronize()
 
 
-@functools.lru_cache(maxsize=2)
+@functools.lru_cache(maxsize=3)
 def _config(n):
     return W.config(n)
 
@@ -66,6 +66,42 @@ def _check_phase(run: GpuRun, ops, cache_ref_bits, *, picks_rng=None, partition_
                 sel = np.stack([got[r, h] for r, h in picks])
                 err = assert_close(sel, ref, wl.dtype, f"{label} {name} (sampled {len(picks)})")
             say(f"[{label}] {name} max abs err {err:.3e}")
+    return cache_ref_bits
+
+
+def _check_phase_with_store(run: GpuRun, ops, cache_ref_bits, *, picks_rng=None, partition_size=0, label=""):
+    """Like _check_phase, but each attention op runs fused with the store of its own rows of
+    the phase's StoreOp (pa_*_with_store); the oracle is the store followed by the op."""
+    wl = run.wl
+    store = None
+    for op in ops:
+        name = type(op).__name__
+        if isinstance(op, W.CopyOp):
+            run.run(op)
+            cache_ref_bits = oracle.copy_blocks(cache_ref_bits, op.pairs)
+            continue
+        if isinstance(op, W.StoreOp):
+            store = op
+            continue
+        say(f"[{label}] {name} with store")
+        out = run.run_with_store(store, op, partition_size=partition_size)
+        torch.cuda.synchronize()
+        rows = op.out_rows
+        cache_ref_bits = oracle.store_kv(cache_ref_bits, bits(store.key[rows]), bits(store.value[rows]),
+                                         store.slot_mapping[rows])
+        host = run.cache.cpu()
+        np.testing.assert_array_equal(bits(host), cache_ref_bits)
+        vals = host_values(host)
+        got = out.float().cpu().numpy()
+        if picks_rng is None:
+            ref = oracle_attention(wl, op, vals)
+            err = assert_close(got, ref, wl.dtype, f"{label} {name}")
+        else:
+            picks = sample_picks(op, wl.num_heads, picks_rng)
+            ref = oracle_attention(wl, op, vals, picks)
+            sel = np.stack([got[r, h] for r, h in picks])
+            err = assert_close(sel, ref, wl.dtype, f"{label} {name} (sampled {len(picks)})")
+        say(f"[{label}] {name} with store: max abs err {err:.3e}")
     return cache_ref_bits
 
 
@@ -327,3 +363,48 @@ def test_config5_mixed_step():
     wl = _config(5)
     run = GpuRun(wl, DEV)
     _check_phase(run, wl.phases[0], bits(wl.kv_cache), picks_rng=np.random.default_rng(5), label="config5")
+
+
+# ----------------------------------------------------------------------------- store fused into the call
+
+
+@pytest.mark.parametrize("name", sorted(PREFILL_CASES))
+def test_small_prefill_with_store(name):
+    """pa_prefill_varlen_with_store = pa_store_kv + pa_prefill_varlen: every output and the whole
+    cache, bit for bit.  The chunked cases put the new keys' first row off a 16-key group
+    boundary and their last row before a group's end (the per-lane copy path)."""
+    H, Hkv, D, BS, win, dt, spec = PREFILL_CASES[name]
+    seqs = [W.SeqSpec(c, [q], ["prefill"]) for c, q in spec]
+    wl = W.build(name, 100, seqs, num_heads=H, num_kv_heads=Hkv, head_size=D, block_size=BS,
+                 dtype=dt, sliding_window=win)
+    run = GpuRun(wl, DEV)
+    _check_phase_with_store(run, wl.phases[0], bits(wl.kv_cache), label=name + "/fused")
+
+
+@pytest.mark.parametrize("name", ["g4_d128", "g5_d128_window", "f32_d64"])
+def test_small_decode_with_store(name):
+    H, Hkv, D, BS, win, dt, ctxs = DECODE_CASES[name]
+    seqs = [W.SeqSpec(c, [1], ["decode"]) for c in ctxs]
+    wl = W.build(name, 200, seqs, num_heads=H, num_kv_heads=Hkv, head_size=D, block_size=BS,
+                 dtype=dt, sliding_window=win)
+    run = GpuRun(wl, DEV)
+    _check_phase_with_store(run, wl.phases[0], bits(wl.kv_cache), partition_size=64, label=name + "/fused")
+
+
+def test_config1_fp32_all_phases_with_store():
+    wl = _config(1)
+    run = GpuRun(wl, DEV)
+    ref = bits(wl.kv_cache)
+    for i, ph in enumerate(wl.phases):
+        ref = _check_phase_with_store(run, ph, ref, label=f"config1 phase {i} fused")
+
+
+@pytest.mark.parametrize("n", [3, 4, 5])
+def test_config_with_store_sampled(n):
+    """Configs 3-5 with every store fused into its attention call (config 4: both phases)."""
+    wl = _config(n)
+    run = GpuRun(wl, DEV)
+    ref = bits(wl.kv_cache)
+    for i, ph in enumerate(wl.phases):
+        ref = _check_phase_with_store(run, ph, ref, picks_rng=np.random.default_rng(100 + n),
+                                      label=f"config{n} phase {i} fused")
