@@ -5,6 +5,7 @@ import this package.  It holds no C sources, so there is nothing to compile for 
 """
 
 from .paged_attention import (  # noqa: F401
+    alibi_bias,
     allowed_mask,
     attention_probs,
     attention_rows,

@@ -30,6 +30,13 @@ Every function takes numpy arrays and follows the pages' statement of the proble
   allowed key is written as zeros (vLLM learning book, section 5, the profile-run
   ``output.fill_(0)``; the pages leave the empty row otherwise undefined).
 
+* ALiBi (optional ``alibi_slopes[num_heads]``): the score of query head ``h`` at position
+  ``p`` for key ``j`` gets ``slope[h] * (j - p)`` added after the scale, before the softmax
+  and the mask (vllm-npu 0.4.2 diff, ``torch_sdpa.py`` and ``xformers.py``
+  ``_make_alibi_bias``: the bias matrix ``bias[i, j] = j - i`` times the per-head slope,
+  added to the scores together with the causal ``-inf`` triangle).  Positions are the
+  absolute ones of the mask above, so chunked prefill and decode use the same rule.
+
 Decode is the same definition with one query per sequence and ``seqlen_k = seq_lens[s]``
 (MinivLLM API docs, section paged_attention_decode: one query, ``context_lens`` valid
 keys).  All floating-point work is fp64.
@@ -46,6 +53,7 @@ __all__ = [
     "allowed_mask",
     "kv_head_of",
     "gather_kv",
+    "alibi_bias",
     "attention_probs",
     "attention_rows",
     "prefill_varlen",
@@ -145,6 +153,12 @@ def gather_kv(kv_cache: np.ndarray, table_row: np.ndarray, positions, kv_head: i
     return k, v
 
 
+def alibi_bias(slope, key_pos, query_pos):
+    """ALiBi bias ``slope * (j - p)`` for key positions ``j`` and query positions ``p``
+    (numpy broadcasting; vllm-npu 0.4.2 diff, ``_make_alibi_bias``)."""
+    return slope * (key_pos - query_pos)
+
+
 def _locate(cu_seqlens_q: np.ndarray, token: int) -> int:
     """Sequence that owns packed query ``token`` (zero-length sequences own nothing)."""
     s = int(np.searchsorted(cu_seqlens_q, token, side="right")) - 1
@@ -153,11 +167,11 @@ def _locate(cu_seqlens_q: np.ndarray, token: int) -> int:
 
 
 def attention_probs(query, kv_cache, block_table, cu_seqlens_q, cu_seqlens_k, scale,
-                    num_kv_heads, sliding_window, token, head):
+                    num_kv_heads, sliding_window, token, head, alibi_slopes=None):
     """Softmax weights of packed query ``token``, head ``head`` over keys ``[0, seqlen_k)``.
 
     Masked keys get weight exactly 0.  Returns ``(probs, seq)``; ``probs`` is all zeros
-    for a row with no allowed key.
+    for a row with no allowed key.  ``alibi_slopes`` adds ``slope[head] * (j - p)``.
     """
     s = _locate(cu_seqlens_q, token)
     seqlen_q = int(cu_seqlens_q[s + 1] - cu_seqlens_q[s])
@@ -170,13 +184,16 @@ def attention_probs(query, kv_cache, block_table, cu_seqlens_q, cu_seqlens_k, sc
         return probs, s
     k, _ = gather_kv(kv_cache, block_table[s], range(lo, hi + 1), g)
     z = float(scale) * (k @ np.asarray(query[token, head], dtype=np.float64))
+    if alibi_slopes is not None:
+        p = seqlen_k - seqlen_q + row
+        z = z + alibi_bias(float(alibi_slopes[head]), np.arange(lo, hi + 1, dtype=np.float64), p)
     w = np.exp(z - z.max())
     probs[lo:hi + 1] = w / w.sum()
     return probs, s
 
 
 def attention_rows(query, kv_cache, block_table, cu_seqlens_q, cu_seqlens_k, scale,
-                   num_kv_heads, sliding_window, picks) -> np.ndarray:
+                   num_kv_heads, sliding_window, picks, alibi_slopes=None) -> np.ndarray:
     """Output rows ``out[token, head, :]`` (fp64) for each ``(token, head)`` in ``picks``.
 
     The definition, one row at a time: softmax weights from ``attention_probs`` times the
@@ -187,7 +204,8 @@ def attention_rows(query, kv_cache, block_table, cu_seqlens_q, cu_seqlens_k, sca
     num_heads = query.shape[1]
     for token, head in picks:
         probs, s = attention_probs(query, kv_cache, block_table, cu_seqlens_q, cu_seqlens_k,
-                                   scale, num_kv_heads, sliding_window, int(token), int(head))
+                                   scale, num_kv_heads, sliding_window, int(token), int(head),
+                                   alibi_slopes)
         nz = np.nonzero(probs)[0]
         if len(nz) == 0:
             rows.append(np.zeros(query.shape[2], dtype=np.float64))
@@ -200,7 +218,7 @@ def attention_rows(query, kv_cache, block_table, cu_seqlens_q, cu_seqlens_k, sca
 
 
 def prefill_varlen(query, kv_cache, block_table, cu_seqlens_q, cu_seqlens_k, scale,
-                   num_kv_heads, sliding_window=0) -> np.ndarray:
+                   num_kv_heads, sliding_window=0, alibi_slopes=None) -> np.ndarray:
     """Every output row of varlen paged attention, ``[total_q, num_heads, head_size]`` fp64.
 
     Same definition as ``attention_rows``, evaluated per (sequence, KV head) over the
@@ -231,6 +249,11 @@ def prefill_varlen(query, kv_cache, block_table, cu_seqlens_q, cu_seqlens_k, sca
             heads = [h for h in range(num_heads) if kv_head_of(h, num_heads, num_kv_heads) == g]
             qg = q[q0:q0 + seqlen_q, heads, :].transpose(1, 0, 2)   # [group, seqlen_q, D]
             z = float(scale) * (qg @ k.T)                           # [group, seqlen_q, n]
+            if alibi_slopes is not None:
+                pos = seqlen_k - seqlen_q + np.arange(seqlen_q, dtype=np.float64)   # query positions
+                keys = np.arange(lo, hi + 1, dtype=np.float64)
+                sl = np.asarray(alibi_slopes, dtype=np.float64)[heads]
+                z = z + alibi_bias(sl[:, None, None], keys[None, None, :], pos[None, :, None])
             z = np.where(mask[None], z, -np.inf)
             zmax = np.where(live_rows[None, :, None], z.max(axis=2, keepdims=True), 0.0)
             w = np.where(mask[None], np.exp(z - zmax), 0.0)
@@ -241,7 +264,7 @@ def prefill_varlen(query, kv_cache, block_table, cu_seqlens_q, cu_seqlens_k, sca
 
 
 def decode(query, kv_cache, block_table, seq_lens, scale, num_kv_heads,
-           sliding_window=0) -> np.ndarray:
+           sliding_window=0, alibi_slopes=None) -> np.ndarray:
     """Paged decode, ``[num_seqs, num_heads, head_size]`` fp64: one query per sequence.
 
     MinivLLM API docs, section paged_attention_decode: sequence ``s`` attends its
@@ -252,4 +275,4 @@ def decode(query, kv_cache, block_table, seq_lens, scale, num_kv_heads,
     cu_q = np.arange(len(seq_lens) + 1, dtype=np.int64)
     cu_k = np.concatenate([[0], np.cumsum(seq_lens)])
     return prefill_varlen(query, kv_cache, block_table, cu_q, cu_k, scale, num_kv_heads,
-                          sliding_window)
+                          sliding_window, alibi_slopes)

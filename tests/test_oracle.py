@@ -348,3 +348,100 @@ def test_scale_enters_once_as_final_factor():
     b = oracle.prefill_varlen(c["q"], c["cache"], c["table"], c["cu_q"], c["cu_k"], 0.5, 2, 0)
     np.testing.assert_allclose(a, b, rtol=1e-13, atol=1e-13)
     assert math.isclose(1 / math.sqrt(64), 0.125)
+
+
+# ----------------------------------------------------------------------------- ALiBi pins
+
+
+def _alibi_slopes(H):
+    # the geometric slopes of the ALiBi paper for a power-of-two head count: 2^(-8 i / H)
+    return np.array([2.0 ** (-8.0 * (i + 1) / H) for i in range(H)])
+
+
+def _pages_alibi_attention(q, k, v, slopes, scale, hf_style=False):
+    """Square causal prompt on contiguous K/V with the pages' bias construction: the
+    position differences bias[i, j] = j - i (or HF's j, which the pages say gives the same
+    result), times each head's slope, plus the -inf strict upper triangle, added to
+    scale * q.K^T; then softmax and the value rows.  q [L, H, D], k/v [L, H, D]."""
+    L, H, _ = q.shape
+    pos = np.arange(L, dtype=np.float64)
+    bias = np.broadcast_to(pos[None, :], (L, L)).copy() if hf_style else pos[None, :] - pos[:, None]
+    bias = bias[None] * slopes[:, None, None]                              # [H, L, L]
+    inf_mask = np.triu(np.full((L, L), -np.inf), k=1)
+    z = scale * np.einsum("ihd,jhd->hij", q, k) + bias + inf_mask[None]
+    w = np.exp(z - z.max(axis=2, keepdims=True))
+    w /= w.sum(axis=2, keepdims=True)
+    return np.einsum("hij,jhd->ihd", w, v)
+
+
+def test_alibi_matches_the_pages_bias_construction():
+    H, Hkv, D, BS = 8, 2, 16, 4
+    specs = [(9, 9), (14, 14), (1, 1)]
+    c = _random_case(40, specs, H, Hkv, D, BS)
+    slopes = _alibi_slopes(H)
+    out = oracle.prefill_varlen(c["q"], c["cache"], c["table"], c["cu_q"], c["cu_k"], 0.25, Hkv, 0,
+                                alibi_slopes=slopes)
+    for s, (sq, sk) in enumerate(specs):
+        q = c["q"][c["cu_q"][s]:c["cu_q"][s + 1]]
+        k = np.repeat(c["ks"][s], H // Hkv, axis=1)
+        v = np.repeat(c["vs"][s], H // Hkv, axis=1)
+        for hf in (False, True):
+            ref = _pages_alibi_attention(q, k, v, slopes, 0.25, hf_style=hf)
+            np.testing.assert_allclose(out[c["cu_q"][s]:c["cu_q"][s + 1]], ref, rtol=1e-11, atol=1e-12)
+
+
+def test_alibi_zero_slopes_is_plain_attention():
+    specs = [(3, 10), (6, 6), (1, 13)]
+    c = _random_case(41, specs, 4, 2, 8, 4)
+    for w in (0, 3):
+        a = oracle.prefill_varlen(c["q"], c["cache"], c["table"], c["cu_q"], c["cu_k"], 0.5, 2, w)
+        b = oracle.prefill_varlen(c["q"], c["cache"], c["table"], c["cu_q"], c["cu_k"], 0.5, 2, w,
+                                  alibi_slopes=np.zeros(4))
+        np.testing.assert_array_equal(a, b)
+
+
+def test_alibi_closed_forms():
+    """q = 0: the weights are exp(slope * (j - p)), a geometric sequence over the allowed
+    keys j in [lo, p], so out = sum_j r^(p-j) v_j / sum_j r^(p-j) with r = exp(-slope); a
+    huge slope leaves only the query's own key.  Chunked rows and a window included."""
+    H, Hkv, D, BS = 4, 2, 8, 4
+    specs = [(3, 10), (6, 6), (1, 13)]
+    slopes = np.array([0.3, 1.1, 0.05, 2.0])
+    for w in (0, 4):
+        c = _random_case(42 + w, specs, H, Hkv, D, BS)
+        out = oracle.prefill_varlen(np.zeros_like(c["q"]), c["cache"], c["table"], c["cu_q"], c["cu_k"],
+                                    1.0, Hkv, w, alibi_slopes=slopes)
+        for s, (sq, sk) in enumerate(specs):
+            for i in range(sq):
+                lo, hi = oracle.key_range(i, sq, sk, w)
+                p = sk - sq + i
+                assert hi == p
+                for h in range(H):
+                    r = math.exp(-slopes[h])
+                    n = p - lo + 1
+                    wts = r ** np.arange(n - 1, -1, -1)          # keys lo..p: r^(p-j)
+                    denom = (1 - r ** n) / (1 - r)                # geometric series
+                    exp = (wts[:, None] * c["vs"][s][lo:p + 1, h // (H // Hkv)]).sum(axis=0) / denom
+                    np.testing.assert_allclose(out[c["cu_q"][s] + i, h], exp, rtol=1e-12, atol=1e-13)
+        big = oracle.prefill_varlen(c["q"], c["cache"], c["table"], c["cu_q"], c["cu_k"], 0.1, Hkv, w,
+                                    alibi_slopes=np.full(H, 1e4))
+        for s, (sq, sk) in enumerate(specs):
+            for i in range(sq):
+                p = sk - sq + i
+                for h in range(H):
+                    np.testing.assert_allclose(big[c["cu_q"][s] + i, h], c["vs"][s][p, h // (H // Hkv)],
+                                               rtol=0, atol=1e-12)
+
+
+def test_alibi_decode_and_rows_agree_with_prefill():
+    specs = [(1, 7), (1, 1), (1, 20)]
+    c = _random_case(43, specs, 4, 2, 8, 4)
+    slopes = np.array([0.5, 0.25, 0.125, 0.0625])
+    lens = np.array([sk for _, sk in specs])
+    d = oracle.decode(c["q"], c["cache"], c["table"], lens, 0.4, 2, 5, alibi_slopes=slopes)
+    p = oracle.prefill_varlen(c["q"], c["cache"], c["table"], c["cu_q"], c["cu_k"], 0.4, 2, 5, alibi_slopes=slopes)
+    np.testing.assert_array_equal(d, p)
+    picks = [(t, h) for t in range(3) for h in range(4)]
+    rows = oracle.attention_rows(c["q"], c["cache"], c["table"], c["cu_q"], c["cu_k"], 0.4, 2, 5, picks,
+                                 alibi_slopes=slopes)
+    np.testing.assert_allclose(rows, np.stack([p[t, h] for t, h in picks]), rtol=1e-12, atol=1e-13)

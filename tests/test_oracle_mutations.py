@@ -24,6 +24,8 @@ PIN_FUNCS = [
     lambda gd: pins.test_block_size_invariance(),
     lambda gd: pins.test_gqa_equals_explicitly_duplicated_kv_heads(),
     lambda gd: pins.test_store_worked_example(gd),
+    lambda gd: pins.test_alibi_matches_the_pages_bias_construction(),
+    lambda gd: pins.test_alibi_closed_forms(),
 ]
 
 
@@ -69,6 +71,14 @@ def _store_offset_swapped(kv_cache, key, value, slot_mapping):
     return out
 
 
+def _alibi_sign_flipped(slope, key_pos, query_pos):
+    return slope * (query_pos - key_pos)
+
+
+def _alibi_half_slope(slope, key_pos, query_pos):
+    return 0.5 * slope * (key_pos - query_pos)
+
+
 _orig_gather = pa.gather_kv
 
 MUTATIONS = {
@@ -79,6 +89,8 @@ MUTATIONS = {
     "k_v_planes_swapped": ("gather_kv", _gather_swapped_planes),
     "block_offset_reversed": ("gather_kv", _gather_wrong_offset),
     "store_block_offset_swapped": ("store_kv", _store_offset_swapped),
+    "alibi_sign_flipped": ("alibi_bias", _alibi_sign_flipped),
+    "alibi_half_slope": ("alibi_bias", _alibi_half_slope),
 }
 
 
