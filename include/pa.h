@@ -108,7 +108,10 @@ int pa_copy_blocks(const pa_cache_desc* cache, const int32_t* block_pairs, int32
  *                 key range are never read and may be -1)
  *   cu_seqlens_q, cu_seqlens_k  [num_seqs + 1] int32, non-decreasing, starting at 0
  *   max_seqlen_q  >= every seqlen_q (sizes the grid); max_seqlen_k >= every seqlen_k
- *   scale         final multiplier of q.K^T (e.g. 1/sqrt(head_size))
+ *   scale         final multiplier of q.K^T (e.g. 1/sqrt(head_size)), >= 0
+ *   alibi_slopes  NULL, or [num_heads] float32 ALiBi slopes: the score of query head h at
+ *                 position p for key j gets alibi_slopes[h] * (j - p) added after the scale
+ *                 (vllm-npu 0.4.2 diff, torch_sdpa.py / xformers.py, _make_alibi_bias)
  * Keys must already be stored (pa_store_kv first).  The K/V tiles are read only inside
  * each row's live range, so cache slots outside it may hold anything, NaN included.
  */
@@ -116,7 +119,8 @@ int pa_prefill_varlen(const pa_cache_desc* cache, void* out, const void* query,
                       const int32_t* block_table, int32_t max_blocks_per_seq,
                       const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
                       int32_t num_seqs, int32_t max_seqlen_q, int32_t max_seqlen_k,
-                      int32_t num_heads, float scale, int32_t sliding_window, void* stream);
+                      int32_t num_heads, float scale, int32_t sliding_window,
+                      const float* alibi_slopes, void* stream);
 
 /*
  * pa_prefill_varlen_with_store — pa_store_kv of the batch's new tokens, then
@@ -143,7 +147,7 @@ int pa_prefill_varlen_with_store(const pa_cache_desc* cache, void* out, const vo
                                  int32_t max_blocks_per_seq, const int32_t* cu_seqlens_q,
                                  const int32_t* cu_seqlens_k, int32_t num_seqs, int32_t max_seqlen_q,
                                  int32_t max_seqlen_k, int32_t num_heads, float scale,
-                                 int32_t sliding_window, void* stream);
+                                 int32_t sliding_window, const float* alibi_slopes, void* stream);
 
 /*
  * pa_decode_workspace_size — bytes of device workspace pa_decode needs for these sizes
@@ -172,6 +176,8 @@ size_t pa_decode_workspace_size(const pa_cache_desc* cache, int32_t num_seqs,
  *   out, query   [num_seqs][num_heads][head_size], contiguous, cache dtype
  *   block_table  [num_seqs][max_blocks_per_seq] int32
  *   seq_lens     [num_seqs] int32, each in [0, max_seq_len]
+ *   alibi_slopes NULL, or [num_heads] float32 ALiBi slopes (as pa_prefill_varlen, with the
+ *                query at position seq_lens[s] - 1)
  *   workspace    device buffer of >= pa_decode_workspace_size(...) bytes (may be NULL when
  *                that is 0); its contents need no initialisation
  * A sequence with seq_lens[s] == 0 gets a zero output row.
@@ -180,8 +186,8 @@ int pa_decode(const pa_cache_desc* cache, void* out, const void* query,
               const int32_t* block_table, int32_t max_blocks_per_seq,
               const int32_t* seq_lens, int32_t num_seqs, int32_t max_seq_len,
               int32_t num_heads, float scale, int32_t sliding_window,
-              int32_t partition_size, void* workspace, size_t workspace_bytes,
-              void* stream);
+              const float* alibi_slopes, int32_t partition_size, void* workspace,
+              size_t workspace_bytes, void* stream);
 
 /*
  * pa_decode_with_store — pa_store_kv of each sequence's new token, then pa_decode, as one
@@ -194,8 +200,8 @@ int pa_decode_with_store(const pa_cache_desc* cache, void* out, const void* quer
                          const void* value, const int32_t* slot_mapping, const int32_t* block_table,
                          int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t num_seqs,
                          int32_t max_seq_len, int32_t num_heads, float scale, int32_t sliding_window,
-                         int32_t partition_size, void* workspace, size_t workspace_bytes,
-                         void* stream);
+                         const float* alibi_slopes, int32_t partition_size, void* workspace,
+                         size_t workspace_bytes, void* stream);
 
 /* Fixed text for a status code. */
 const char* pa_status_string(int status);

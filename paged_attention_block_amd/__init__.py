@@ -66,13 +66,13 @@ def load() -> ctypes.CDLL:
     D = ctypes.POINTER(_CacheDesc)
     lib.pa_store_kv.argtypes = [D, P, P, P, I32, P]
     lib.pa_copy_blocks.argtypes = [D, P, I32, P]
-    lib.pa_prefill_varlen.argtypes = [D, P, P, P, I32, P, P, I32, I32, I32, I32, F32, I32, P]
+    lib.pa_prefill_varlen.argtypes = [D, P, P, P, I32, P, P, I32, I32, I32, I32, F32, I32, P, P]
     lib.pa_decode_workspace_size.argtypes = [D, I32, I32, I32, I32, I32]
     lib.pa_decode_workspace_size.restype = SZ
-    lib.pa_decode.argtypes = [D, P, P, P, I32, P, I32, I32, I32, F32, I32, I32, P, SZ, P]
+    lib.pa_decode.argtypes = [D, P, P, P, I32, P, I32, I32, I32, F32, I32, P, I32, P, SZ, P]
     lib.pa_prefill_varlen_with_store.argtypes = [D, P, P, P, P, P, I32, P, I32, P, P, I32, I32, I32, I32,
-                                                 F32, I32, P]
-    lib.pa_decode_with_store.argtypes = [D, P, P, P, P, P, P, I32, P, I32, I32, I32, F32, I32, I32, P, SZ, P]
+                                                 F32, I32, P, P]
+    lib.pa_decode_with_store.argtypes = [D, P, P, P, P, P, P, I32, P, I32, I32, I32, F32, I32, P, I32, P, SZ, P]
     for name in ("pa_store_kv", "pa_copy_blocks", "pa_prefill_varlen", "pa_decode",
                  "pa_prefill_varlen_with_store", "pa_decode_with_store"):
         getattr(lib, name).restype = ctypes.c_int
@@ -102,6 +102,16 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
 
 def _stream(t: torch.Tensor) -> Optional[int]:
     return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _alibi(slopes: Optional[torch.Tensor], query: torch.Tensor, dev) -> Optional[int]:
+    """Device pointer of optional ALiBi slopes (float32 [num_heads], contiguous)."""
+    if slopes is None:
+        return None
+    _need(slopes, "alibi_slopes", torch.float32, dev, 1)
+    if slopes.shape[0] != query.shape[1]:
+        raise ValueError(f"alibi_slopes must be [{query.shape[1]}]")
+    return _ptr(slopes)
 
 
 def _desc(kv_cache: torch.Tensor) -> _CacheDesc:
@@ -157,8 +167,10 @@ def pa_copy_blocks(kv_cache: torch.Tensor, block_pairs: torch.Tensor) -> None:
 def pa_prefill_varlen(query: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
                       cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor, max_seqlen_q: int,
                       max_seqlen_k: int, scale: float, num_kv_heads: int, sliding_window: int = 0,
-                      out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Varlen causal attention of packed ``query [Tq, H, D]`` over the cached keys."""
+                      out: Optional[torch.Tensor] = None,
+                      alibi_slopes: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Varlen causal attention of packed ``query [Tq, H, D]`` over the cached keys
+    (``alibi_slopes``: optional float32 ``[H]`` ALiBi slopes on the cache's device)."""
     lib = load()
     desc = _desc(kv_cache)
     dev = kv_cache.device
@@ -182,7 +194,8 @@ def pa_prefill_varlen(query: torch.Tensor, kv_cache: torch.Tensor, block_table: 
     _check(lib.pa_prefill_varlen(ctypes.byref(desc), _ptr(out), _ptr(query), _ptr(block_table),
                                  block_table.shape[1], _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
                                  num_seqs, int(max_seqlen_q), int(max_seqlen_k), query.shape[1],
-                                 float(scale), int(sliding_window), _stream(kv_cache)),
+                                 float(scale), int(sliding_window), _alibi(alibi_slopes, query, dev),
+                                 _stream(kv_cache)),
            "pa_prefill_varlen")
     return out
 
@@ -204,7 +217,8 @@ def pa_decode_workspace_size(kv_cache: torch.Tensor, num_seqs: int, num_heads: i
 def pa_decode(query: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
               seq_lens: torch.Tensor, max_seq_len: int, scale: float, num_kv_heads: int,
               sliding_window: int = 0, out: Optional[torch.Tensor] = None,
-              workspace: Optional[torch.Tensor] = None, partition_size: int = 0) -> torch.Tensor:
+              workspace: Optional[torch.Tensor] = None, partition_size: int = 0,
+              alibi_slopes: Optional[torch.Tensor] = None) -> torch.Tensor:
     """One query per sequence (``query [B, H, D]``) over its ``seq_lens[s]`` cached keys.
 
     ``workspace`` is a device byte buffer of at least ``pa_decode_workspace_size(...)``
@@ -239,7 +253,8 @@ def pa_decode(query: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Te
     with (torch.cuda.device(dev) if dev.type == "cuda" else contextlib.nullcontext()):
         _check(lib.pa_decode(ctypes.byref(desc), _ptr(out), _ptr(query), _ptr(block_table),
                              block_table.shape[1], _ptr(seq_lens), num_seqs, int(max_seq_len),
-                             query.shape[1], float(scale), int(sliding_window), int(partition_size),
+                             query.shape[1], float(scale), int(sliding_window),
+                             _alibi(alibi_slopes, query, dev), int(partition_size),
                              _ptr(workspace), ws_bytes, _stream(kv_cache)), "pa_decode")
     return out
 
@@ -260,7 +275,8 @@ def pa_prefill_varlen_with_store(query: torch.Tensor, key: torch.Tensor, value: 
                                  block_table: torch.Tensor, cu_seqlens_q: torch.Tensor,
                                  cu_seqlens_k: torch.Tensor, max_seqlen_q: int, max_seqlen_k: int,
                                  scale: float, num_kv_heads: int, sliding_window: int = 0,
-                                 out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                                 out: Optional[torch.Tensor] = None,
+                                 alibi_slopes: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Store the batch's new tokens (``key``/``value [Tq, Hkv, D]`` at ``slot_mapping``) and run
     the varlen causal attention of ``query [Tq, H, D]`` in one call (one kernel for bf16)."""
     lib = load()
@@ -288,7 +304,8 @@ def pa_prefill_varlen_with_store(query: torch.Tensor, key: torch.Tensor, value: 
                                             _ptr(slot_mapping), query.shape[0], _ptr(block_table),
                                             block_table.shape[1], _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
                                             num_seqs, int(max_seqlen_q), int(max_seqlen_k), query.shape[1],
-                                            float(scale), int(sliding_window), _stream(kv_cache)),
+                                            float(scale), int(sliding_window), _alibi(alibi_slopes, query, dev),
+                                            _stream(kv_cache)),
            "pa_prefill_varlen_with_store")
     return out
 
@@ -297,7 +314,8 @@ def pa_decode_with_store(query: torch.Tensor, key: torch.Tensor, value: torch.Te
                          slot_mapping: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
                          seq_lens: torch.Tensor, max_seq_len: int, scale: float, num_kv_heads: int,
                          sliding_window: int = 0, out: Optional[torch.Tensor] = None,
-                         workspace: Optional[torch.Tensor] = None, partition_size: int = 0) -> torch.Tensor:
+                         workspace: Optional[torch.Tensor] = None, partition_size: int = 0,
+                         alibi_slopes: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Store each sequence's new token (``key``/``value [B, Hkv, D]`` at ``slot_mapping``) and
     decode ``query [B, H, D]`` over the ``seq_lens[s]`` keys that include it, in one call."""
     lib = load()
@@ -331,6 +349,7 @@ def pa_decode_with_store(query: torch.Tensor, key: torch.Tensor, value: torch.Te
         _check(lib.pa_decode_with_store(ctypes.byref(desc), _ptr(out), _ptr(query), _ptr(key), _ptr(value),
                                         _ptr(slot_mapping), _ptr(block_table), block_table.shape[1],
                                         _ptr(seq_lens), num_seqs, int(max_seq_len), query.shape[1],
-                                        float(scale), int(sliding_window), int(partition_size),
-                                        _ptr(workspace), ws_bytes, _stream(kv_cache)), "pa_decode_with_store")
+                                        float(scale), int(sliding_window), _alibi(alibi_slopes, query, dev),
+                                        int(partition_size), _ptr(workspace), ws_bytes, _stream(kv_cache)),
+               "pa_decode_with_store")
     return out

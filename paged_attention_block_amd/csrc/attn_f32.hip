@@ -4,7 +4,9 @@
 // simple: one wavefront per (query row, head); lane l owns dims l and l + 64.  For each key
 // in the row's live range the wave reads the K row through the block table, reduces q.k
 // across lanes, updates the online-softmax state (MinivLLM API docs, "Attention":
-// online softmax) and accumulates p * V.  No float32 input ever passes through a bf16 or
+// online softmax) and accumulates p * V.  With ALiBi slopes the score of key j at query
+// position p gets slope * (j - p) added after the scale (vllm-npu 0.4.2 diff, torch_sdpa.py,
+// _make_alibi_bias).  No float32 input ever passes through a bf16 or
 // reduced-precision matrix instruction.
 #include <math.h>
 
@@ -26,11 +28,11 @@ __global__ __launch_bounds__(64) void attn_rows_f32_kernel(
     int num_kv_heads, float* __restrict__ out, const float* __restrict__ q,
     const int32_t* __restrict__ table, int max_blocks, const int32_t* __restrict__ cu_q,
     const int32_t* __restrict__ cu_k, const int32_t* __restrict__ seq_lens, int max_seqlen_q,
-    int num_heads, int group, float scale, int window, int mode) {
+    int num_heads, int group, float scale, int window, const float* __restrict__ alibi, int mode) {
     constexpr int R = D / 64;
     const int lane = threadIdx.x;
     const int h = blockIdx.y;
-    int s, token, lo, hi;
+    int s, token, lo, hi, pos;
     if (mode == 0) {
         s = blockIdx.x / max_seqlen_q;
         const int row = blockIdx.x % max_seqlen_q;
@@ -40,6 +42,7 @@ __global__ __launch_bounds__(64) void attn_rows_f32_kernel(
         const int sk = cu_k[s + 1] - cu_k[s];
         const int p = sk - sq + row;
         token = q0 + row;
+        pos = p;
         hi = min(p, sk - 1);
         lo = window > 0 ? max(0, p - window + 1) : 0;
     } else {
@@ -47,8 +50,10 @@ __global__ __launch_bounds__(64) void attn_rows_f32_kernel(
         token = s;
         const int n = seq_lens[s];
         hi = n - 1;
+        pos = n - 1;
         lo = window > 0 ? max(0, n - window) : 0;
     }
+    const float slope = alibi ? alibi[h] : 0.f;  // ALiBi: slope * (j - pos) after the scale
     const int g = h / group;
     float qv[R], o[R];
     for (int r = 0; r < R; ++r) {
@@ -63,7 +68,7 @@ __global__ __launch_bounds__(64) void attn_rows_f32_kernel(
         const float* v = k + plane_elems;
         float part = 0.f;
         for (int r = 0; r < R; ++r) part = fmaf(qv[r], k[lane + 64 * r], part);
-        const float z = wave_sum_f32(part) * scale;
+        const float z = fmaf(wave_sum_f32(part), scale, slope * (float)(j - pos));
         const float m_new = fmaxf(m, z);
         const float alpha = expf(m - m_new);
         const float pj = expf(z - m_new);
@@ -83,13 +88,13 @@ hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t st) {
                            c.plane_elems, c.block_size, c.block_shift, c.num_kv_heads,
                            (float*)a.out, (const float*)a.q, a.table, a.max_blocks, a.cu_q, a.cu_k,
                            (const int32_t*)nullptr, a.max_seqlen_q, a.num_heads, a.group, a.scale,
-                           a.window, 0);
+                           a.window, a.alibi, 0);
     else
         hipLaunchKernelGGL(attn_rows_f32_kernel<64>, grid, dim3(64), 0, st, (const float*)c.kv,
                            c.plane_elems, c.block_size, c.block_shift, c.num_kv_heads,
                            (float*)a.out, (const float*)a.q, a.table, a.max_blocks, a.cu_q, a.cu_k,
                            (const int32_t*)nullptr, a.max_seqlen_q, a.num_heads, a.group, a.scale,
-                           a.window, 0);
+                           a.window, a.alibi, 0);
     return hipGetLastError();
 }
 
@@ -101,13 +106,13 @@ hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t st) {
                            c.plane_elems, c.block_size, c.block_shift, c.num_kv_heads,
                            (float*)a.out, (const float*)a.q, a.table, a.max_blocks,
                            (const int32_t*)nullptr, (const int32_t*)nullptr, a.seq_lens, 1,
-                           a.num_heads, a.group, a.scale, a.window, 1);
+                           a.num_heads, a.group, a.scale, a.window, a.alibi, 1);
     else
         hipLaunchKernelGGL(attn_rows_f32_kernel<64>, grid, dim3(64), 0, st, (const float*)c.kv,
                            c.plane_elems, c.block_size, c.block_shift, c.num_kv_heads,
                            (float*)a.out, (const float*)a.q, a.table, a.max_blocks,
                            (const int32_t*)nullptr, (const int32_t*)nullptr, a.seq_lens, 1,
-                           a.num_heads, a.group, a.scale, a.window, 1);
+                           a.num_heads, a.group, a.scale, a.window, a.alibi, 1);
     return hipGetLastError();
 }
 

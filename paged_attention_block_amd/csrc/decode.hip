@@ -80,8 +80,11 @@ __device__ __forceinline__ void load_step(int k0, int kb, int ke, const int32_t*
 }
 
 // Online-softmax update of one 32-key step (scores by MFMA, P packed to bf16, PV by MFMA).
-template <int D>
+// With ALiBi, sl2 = this lane's head slope in log2 units and pos the query's position: the
+// score of key j gets sl2 * (j - pos) added after the scale.
+template <int D, bool ALIBI>
 __device__ __forceinline__ void compute_step(int k0, int kb, int ke, int grp, float c_log2,
+                                             float sl2, int pos,
                                              const bf16x8 (&qf)[D / 32], u32x4 (&kr)[2][D / 32],
                                              typename VRow<D>::T (&vr)[8], f32x4 (&oacc)[D / 16],
                                              float& m_run, float& l_run) {
@@ -111,17 +114,25 @@ __device__ __forceinline__ void compute_step(int k0, int kb, int ke, int grp, fl
             vr[j] = ok ? vr[j] : (VT)(0u);
         }
     }
+    float cs = c_log2;  // accumulator -> log2 units (1 once ALiBi has folded it in)
+    if constexpr (ALIBI) {
+        const float base = sl2 * (float)(k0 + 4 * grp - pos);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            sc[j] = fmaf(sc[j], c_log2, fmaf(sl2, (float)(16 * (j >> 2) + (j & 3)), base));
+        cs = 1.f;
+    }
     float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
                      fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
     mx = group4_max(mx);
-    const float m_new = fmaxf(m_run, mx * c_log2);
+    const float m_new = fmaxf(m_run, mx * cs);
     const float msub = m_new == -INFINITY ? 0.f : m_new;
     const float alpha = __builtin_amdgcn_exp2f(m_run - msub);
     float pr[8];
     float psum = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        pr[j] = __builtin_amdgcn_exp2f(fmaf(sc[j], c_log2, -msub));
+        pr[j] = __builtin_amdgcn_exp2f(fmaf(sc[j], cs, -msub));
         psum += pr[j];
     }
     l_run = l_run * alpha + psum;
@@ -189,7 +200,7 @@ __device__ inline int chunk_begin(int w, int S, int nw) { return (int)(((int64_t
 // the chunk that holds step t, 0 <= t < S
 __device__ inline int chunk_of(int t, int S, int nw) { return (int)(((int64_t)(t + 1) * nw - 1) / S); }
 
-template <int D>
+template <int D, bool ALIBI>
 __global__ __launch_bounds__(512) void decode_bf16_kernel(const DecodeArgs a) {
     constexpr int KS = D / 32;   // k-slices of q.K^T
     constexpr int DPL = D / 16;  // dims per lane chunk of a V row = PV MFMAs per step
@@ -223,6 +234,7 @@ __global__ __launch_bounds__(512) void decode_bf16_kernel(const DecodeArgs a) {
     const char* __restrict__ kplane = (const char*)a.c.kv;
     const char* __restrict__ vplane = kplane + a.c.plane_elems * 2;
     const float c_log2 = a.scale * 1.4426950408889634f;
+    const float sl2 = ALIBI && head_ok ? a.alibi[head] * 1.4426950408889634f : 0.f;  // ALiBi slope, log2 units
     // per-lane byte offsets from a group's first row: K rows (key col, dims 8*grp of each
     // 32-dim slice), V rows (key 4*grp + j%4, dims DPL*col)
     const int64_t row_elems = (int64_t)Hkv * D;
@@ -302,12 +314,12 @@ __global__ __launch_bounds__(512) void decode_bf16_kernel(const DecodeArgs a) {
                 __syncthreads();
                 const int n1 = k0 + 32 < ke ? k0 + 32 : k0;
                 load_step<D>(n1, kb, ke, table, shift, BS, row_elems, g, kplane, vplane, k_off, v_off, row_bytes, kB, vB);
-                compute_step<D>(k0, kb, ke, grp, c_log2, qf, kA, vA, oacc, m_run, l_run);
+                compute_step<D, ALIBI>(k0, kb, ke, grp, c_log2, sl2, n - 1, qf, kA, vA, oacc, m_run, l_run);
                 k0 += 32;
                 if (k0 >= ke) break;
                 const int n2 = k0 + 32 < ke ? k0 + 32 : k0;
                 load_step<D>(n2, kb, ke, table, shift, BS, row_elems, g, kplane, vplane, k_off, v_off, row_bytes, kA, vA);
-                compute_step<D>(k0, kb, ke, grp, c_log2, qf, kB, vB, oacc, m_run, l_run);
+                compute_step<D, ALIBI>(k0, kb, ke, grp, c_log2, sl2, n - 1, qf, kB, vB, oacc, m_run, l_run);
                 k0 += 32;
                 if (k0 >= ke) break;
             }
@@ -457,8 +469,8 @@ int decode_resident_slots(int head_size, int num_kv_heads) {
         hipError_t e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
         if (e == hipSuccess)
             e = head_size == 128
-                    ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_bf16_kernel<128>, 64 * waves, 0)
-                    : hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_bf16_kernel<64>, 64 * waves, 0);
+                    ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_bf16_kernel<128, false>, 64 * waves, 0)
+                    : hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_bf16_kernel<64, false>, 64 * waves, 0);
         if (e != hipSuccess || ncu <= 0 || nb <= 0) {
             (void)hipGetLastError();
             return 256;
@@ -473,10 +485,13 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t st) {
     const int hkv = a.c.num_kv_heads;
     const dim3 grid(a.nw, (hkv + 7) / 8);
     const dim3 block(64 * (hkv < 8 ? hkv : 8));
-    if (a.c.head_size == 128)
-        hipLaunchKernelGGL(decode_bf16_kernel<128>, grid, block, 0, st, a);
-    else
-        hipLaunchKernelGGL(decode_bf16_kernel<64>, grid, block, 0, st, a);
+    if (a.c.head_size == 128) {
+        if (a.alibi) hipLaunchKernelGGL((decode_bf16_kernel<128, true>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((decode_bf16_kernel<128, false>), grid, block, 0, st, a);
+    } else {
+        if (a.alibi) hipLaunchKernelGGL((decode_bf16_kernel<64, true>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((decode_bf16_kernel<64, false>), grid, block, 0, st, a);
+    }
     if (a.nw > 1) {
         const dim3 mg(a.num_seqs, (a.num_heads + 3) / 4);
         const bool many = a.nw > 8 * a.num_seqs;  // more than ~8 pieces per sequence

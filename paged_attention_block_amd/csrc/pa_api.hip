@@ -162,8 +162,8 @@ static int prefill_args(const pa_cache_desc* cache, void* out, const void* query
                         const int32_t* block_table, int32_t max_blocks_per_seq,
                         const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
                         int32_t num_seqs, int32_t max_seqlen_q, int32_t max_seqlen_k,
-                        int32_t num_heads, float scale, int32_t sliding_window, pa::PrefillArgs* pa_out,
-                        bool* empty) {
+                        int32_t num_heads, float scale, int32_t sliding_window, const float* alibi_slopes,
+                        pa::PrefillArgs* pa_out, bool* empty) {
     pa::PrefillArgs& a = *pa_out;
     *empty = false;
     int st = check_cache(cache, &a.c);
@@ -177,7 +177,7 @@ static int prefill_args(const pa_cache_desc* cache, void* out, const void* query
     if (max_blocks_per_seq < 1) return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq must be >= 1");
     if ((int64_t)max_seqlen_k > (int64_t)max_blocks_per_seq * a.c.block_size)
         return fail(PA_ERR_INVALID_ARG, "max_seqlen_k %d exceeds max_blocks_per_seq * block_size", max_seqlen_k);
-    if (!(scale == scale)) return fail(PA_ERR_INVALID_ARG, "scale is NaN");
+    if (!(scale >= 0.f)) return fail(PA_ERR_INVALID_ARG, "scale must be >= 0 (got %g)", (double)scale);
     if (a.c.dtype == PA_F32 && (int64_t)num_seqs * max_seqlen_q >= (int64_t(1) << 31))
         return fail(PA_ERR_INVALID_ARG, "num_seqs * max_seqlen_q too large");
     if ((int64_t)num_seqs * num_heads * ((max_seqlen_q + 31) / 32) >= (int64_t(1) << 30))
@@ -197,6 +197,7 @@ static int prefill_args(const pa_cache_desc* cache, void* out, const void* query
     a.knew = nullptr;
     a.vnew = nullptr;
     a.slots = nullptr;
+    a.alibi = alibi_slopes;
     return PA_OK;
 }
 
@@ -204,11 +205,13 @@ int pa_prefill_varlen(const pa_cache_desc* cache, void* out, const void* query,
                       const int32_t* block_table, int32_t max_blocks_per_seq,
                       const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
                       int32_t num_seqs, int32_t max_seqlen_q, int32_t max_seqlen_k,
-                      int32_t num_heads, float scale, int32_t sliding_window, void* stream) {
+                      int32_t num_heads, float scale, int32_t sliding_window,
+                      const float* alibi_slopes, void* stream) {
     pa::PrefillArgs a;
     bool empty;
     int st = prefill_args(cache, out, query, block_table, max_blocks_per_seq, cu_seqlens_q, cu_seqlens_k,
-                          num_seqs, max_seqlen_q, max_seqlen_k, num_heads, scale, sliding_window, &a, &empty);
+                          num_seqs, max_seqlen_q, max_seqlen_k, num_heads, scale, sliding_window,
+                          alibi_slopes, &a, &empty);
     if (st) return st;
     if (empty) { g_last_error[0] = 0; return PA_OK; }
     hipStream_t s = (hipStream_t)stream;
@@ -221,11 +224,12 @@ int pa_prefill_varlen_with_store(const pa_cache_desc* cache, void* out, const vo
                                  int32_t max_blocks_per_seq, const int32_t* cu_seqlens_q,
                                  const int32_t* cu_seqlens_k, int32_t num_seqs, int32_t max_seqlen_q,
                                  int32_t max_seqlen_k, int32_t num_heads, float scale,
-                                 int32_t sliding_window, void* stream) {
+                                 int32_t sliding_window, const float* alibi_slopes, void* stream) {
     pa::PrefillArgs a;
     bool empty;
     int st = prefill_args(cache, out, query, block_table, max_blocks_per_seq, cu_seqlens_q, cu_seqlens_k,
-                          num_seqs, max_seqlen_q, max_seqlen_k, num_heads, scale, sliding_window, &a, &empty);
+                          num_seqs, max_seqlen_q, max_seqlen_k, num_heads, scale, sliding_window,
+                          alibi_slopes, &a, &empty);
     if (st) return st;
     if (num_tokens < 0) return fail(PA_ERR_INVALID_ARG, "num_tokens must be >= 0 (got %d)", num_tokens);
     if (num_tokens > 0 && (!key || !value || !slot_mapping))
@@ -271,8 +275,8 @@ size_t pa_decode_workspace_size(const pa_cache_desc* cache, int32_t num_seqs, in
 static int decode_args(const pa_cache_desc* cache, void* out, const void* query, const int32_t* block_table,
                        int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t num_seqs,
                        int32_t max_seq_len, int32_t num_heads, float scale, int32_t sliding_window,
-                       int32_t partition_size, void* workspace, size_t workspace_bytes,
-                       pa::DecodeArgs* a_out, bool* empty) {
+                       const float* alibi_slopes, int32_t partition_size, void* workspace,
+                       size_t workspace_bytes, pa::DecodeArgs* a_out, bool* empty) {
     pa::DecodeArgs& a = *a_out;
     *empty = false;
     int st = check_cache(cache, &a.c);
@@ -288,7 +292,7 @@ static int decode_args(const pa_cache_desc* cache, void* out, const void* query,
         return fail(PA_ERR_INVALID_ARG, "max_seq_len %d exceeds max_blocks_per_seq * block_size", max_seq_len);
     if (partition_size < 0 || partition_size % 32 != 0)
         return fail(PA_ERR_INVALID_ARG, "partition_size must be 0 or a positive multiple of 32 (got %d)", partition_size);
-    if (!(scale == scale)) return fail(PA_ERR_INVALID_ARG, "scale is NaN");
+    if (!(scale >= 0.f)) return fail(PA_ERR_INVALID_ARG, "scale must be >= 0 (got %g)", (double)scale);
     const int32_t win = sliding_window > 0 ? sliding_window : 0;
     if ((int64_t)num_seqs * ((max_keys_of(max_seq_len, win) + 31) / 32 + 1) > 0x7fffffff)
         return fail(PA_ERR_INVALID_ARG, "num_seqs * max_seq_len too large");
@@ -302,6 +306,7 @@ static int decode_args(const pa_cache_desc* cache, void* out, const void* query,
     a.group = num_heads / a.c.num_kv_heads;
     a.scale = scale;
     a.window = win;
+    a.alibi = alibi_slopes;
     a.nw = 1;
     a.min_steps = 1;
     a.ws_o = nullptr;
@@ -325,11 +330,13 @@ static int decode_args(const pa_cache_desc* cache, void* out, const void* query,
 int pa_decode(const pa_cache_desc* cache, void* out, const void* query, const int32_t* block_table,
               int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t num_seqs,
               int32_t max_seq_len, int32_t num_heads, float scale, int32_t sliding_window,
-              int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream) {
+              const float* alibi_slopes, int32_t partition_size, void* workspace,
+              size_t workspace_bytes, void* stream) {
     pa::DecodeArgs a;
     bool empty;
     int st = decode_args(cache, out, query, block_table, max_blocks_per_seq, seq_lens, num_seqs, max_seq_len,
-                         num_heads, scale, sliding_window, partition_size, workspace, workspace_bytes, &a, &empty);
+                         num_heads, scale, sliding_window, alibi_slopes, partition_size, workspace,
+                         workspace_bytes, &a, &empty);
     if (st) return st;
     if (empty) { g_last_error[0] = 0; return PA_OK; }
     hipStream_t s = (hipStream_t)stream;
@@ -340,11 +347,13 @@ int pa_decode_with_store(const pa_cache_desc* cache, void* out, const void* quer
                          const void* value, const int32_t* slot_mapping, const int32_t* block_table,
                          int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t num_seqs,
                          int32_t max_seq_len, int32_t num_heads, float scale, int32_t sliding_window,
-                         int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream) {
+                         const float* alibi_slopes, int32_t partition_size, void* workspace,
+                         size_t workspace_bytes, void* stream) {
     pa::DecodeArgs a;
     bool empty;
     int st = decode_args(cache, out, query, block_table, max_blocks_per_seq, seq_lens, num_seqs, max_seq_len,
-                         num_heads, scale, sliding_window, partition_size, workspace, workspace_bytes, &a, &empty);
+                         num_heads, scale, sliding_window, alibi_slopes, partition_size, workspace,
+                         workspace_bytes, &a, &empty);
     if (st) return st;
     if (empty) { g_last_error[0] = 0; return PA_OK; }
     if (!key || !value || !slot_mapping) return fail(PA_ERR_INVALID_ARG, "key, value and slot_mapping must be non-NULL");

@@ -97,6 +97,7 @@ struct PrefillArgs {
     const void* knew;
     const void* vnew;
     const int32_t* slots;
+    const float* alibi;  // [num_heads] ALiBi slopes, or null
 };
 
 struct DecodeArgs {
@@ -113,6 +114,7 @@ struct DecodeArgs {
     int32_t window;
     int32_t nw;          // chunk workgroups per group of 8 KV heads (grid x)
     int32_t min_steps;   // fewest 32-key steps per chunk
+    const float* alibi;  // [num_heads] ALiBi slopes, or null
     float* ws_o;         // [nw][2][H][D] unnormalised partial outputs (first, last segment)
     float* ws_ml;        // [nw][2][H][2] running max (log2 units) and sum
 };

@@ -99,7 +99,7 @@ struct PrefillGrid {
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-template <int D, int NBR, int BN, int NBUF>
+template <int D, int NBR, int BN, int NBUF, bool ALIBI>
 __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const PrefillArgs a, const PrefillGrid pg) {
     constexpr int NGA = BN / 16;      // 16-key groups per K/V tile
     constexpr int NCC = BN / 32;      // 32-key chunks per K/V tile (PV MFMA k-steps)
@@ -178,6 +178,9 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const PrefillArgs 
     const int wv_p_min = off + r0;
 
     const float c_log2 = a.scale * 1.4426950408889634f;
+    // ALiBi slope of this wave's head in log2 units (the bias slope * (j - p) is added to the
+    // scaled score before the softmax)
+    const float sl2 = ALIBI && wave_ok ? a.alibi[h] * 1.4426950408889634f : 0.f;
     const int BS = a.c.block_size;
     const int shift = a.c.block_shift;
     const char* __restrict__ kplane = (const char*)a.c.kv;
@@ -371,6 +374,20 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const PrefillArgs 
                         sacc[ga][nb][r] = (key > prow[nb] || key < plo[nb]) ? -INFINITY : sacc[ga][nb][r];
                 }
         }
+        // cs: factor from the accumulator to log2 units (1 once ALiBi has folded it in)
+        float cs = c_log2;
+        if constexpr (ALIBI) {
+#pragma unroll
+            for (int nb = 0; nb < NBR; ++nb) {
+                const float base = sl2 * (float)(k0 + 4 * grp - prow[nb]);
+#pragma unroll
+                for (int ga = 0; ga < NGA; ++ga)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        sacc[ga][nb][r] = fmaf(sacc[ga][nb][r], c_log2, fmaf(sl2, (float)(16 * ga + r), base));
+            }
+            cs = 1.f;
+        }
 #pragma unroll
         for (int nb = 0; nb < NBR; ++nb) {
             // three-operand chain: one v_max3 per two scores
@@ -382,7 +399,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const PrefillArgs 
             // The reference maximum moves only when the tile's maximum exceeds it by more
             // than 8 (log2 units): P = exp2(s - m) then stays below 2^8, and O and l are
             // rescaled only on those rare moves instead of on every increase.
-            const float mt = mx * c_log2;
+            const float mt = mx * cs;
             const bool move = mt > m_run[nb] + 8.f;
             const float m_new = move ? mt : m_run[nb];
             alpha[nb] = (move && m_run[nb] != -INFINITY) ? __builtin_amdgcn_exp2f(m_run[nb] - m_new) : 1.f;
@@ -392,7 +409,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const PrefillArgs 
 #pragma unroll
             for (int ga = 0; ga < NGA; ++ga)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) pv[ga][r] = __builtin_amdgcn_exp2f(fmaf(sacc[ga][nb][r], c_log2, -msub));
+                for (int r = 0; r < 4; ++r) pv[ga][r] = __builtin_amdgcn_exp2f(fmaf(sacc[ga][nb][r], cs, -msub));
             float ps = 0.f;
 #pragma unroll
             for (int ga = 0; ga < NGA; ++ga) ps += (pv[ga][0] + pv[ga][1]) + (pv[ga][2] + pv[ga][3]);
@@ -580,10 +597,14 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t st) {
     pg.n_tiles = (a.max_seqlen_q + 32 * pg.rb - 1) / (32 * pg.rb) * pg.wgs_per_tile;
     const int64_t nsg_pad = ((int64_t)pg.n_sg + 7) / 8 * 8;
     const dim3 grid((unsigned)(nsg_pad * pg.n_tiles));
-    if (a.c.head_size == 128)
-        hipLaunchKernelGGL((prefill_bf16_kernel<128, 2, kPrefillBN, kPrefillNBUF>), grid, dim3(256), 0, st, a, pg);
-    else
-        hipLaunchKernelGGL((prefill_bf16_kernel<64, 2, kPrefillBN, kPrefillNBUF>), grid, dim3(256), 0, st, a, pg);
+    const bool alibi = a.alibi != nullptr;
+    if (a.c.head_size == 128) {
+        if (alibi) hipLaunchKernelGGL((prefill_bf16_kernel<128, 2, kPrefillBN, kPrefillNBUF, true>), grid, dim3(256), 0, st, a, pg);
+        else hipLaunchKernelGGL((prefill_bf16_kernel<128, 2, kPrefillBN, kPrefillNBUF, false>), grid, dim3(256), 0, st, a, pg);
+    } else {
+        if (alibi) hipLaunchKernelGGL((prefill_bf16_kernel<64, 2, kPrefillBN, kPrefillNBUF, true>), grid, dim3(256), 0, st, a, pg);
+        else hipLaunchKernelGGL((prefill_bf16_kernel<64, 2, kPrefillBN, kPrefillNBUF, false>), grid, dim3(256), 0, st, a, pg);
+    }
     return hipGetLastError();
 }
 

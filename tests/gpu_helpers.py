@@ -60,6 +60,10 @@ class GpuRun:
         self.wl = wl
         self.dev = device
         self.cache = wl.kv_cache.to(device)
+        self.alibi = None        # optional np.ndarray [num_heads] ALiBi slopes
+
+    def _slopes(self):
+        return None if self.alibi is None else torch.from_numpy(np.asarray(self.alibi, np.float32)).to(self.dev)
 
     def i32(self, a: np.ndarray) -> torch.Tensor:
         return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(self.dev)
@@ -76,11 +80,12 @@ class GpuRun:
             return pa.pa_prefill_varlen(op.query.to(self.dev), self.cache, self.i32(op.block_table),
                                         self.i32(op.cu_seqlens_q), self.i32(op.cu_seqlens_k),
                                         op.max_seqlen_q, op.max_seqlen_k, wl.scale, wl.num_kv_heads,
-                                        wl.sliding_window)
+                                        wl.sliding_window, alibi_slopes=self._slopes())
         if isinstance(op, W.DecodeOp):
             return pa.pa_decode(op.query.to(self.dev), self.cache, self.i32(op.block_table),
                                 self.i32(op.seq_lens), op.max_seq_len, wl.scale, wl.num_kv_heads,
-                                wl.sliding_window, partition_size=partition_size)
+                                wl.sliding_window, partition_size=partition_size,
+                                alibi_slopes=self._slopes())
         raise TypeError(op)
 
     def run_with_store(self, store, op, partition_size: int = 0):
@@ -93,14 +98,16 @@ class GpuRun:
             return pa.pa_prefill_varlen_with_store(op.query.to(d), k, v, sl, self.cache, self.i32(op.block_table),
                                                    self.i32(op.cu_seqlens_q), self.i32(op.cu_seqlens_k),
                                                    op.max_seqlen_q, op.max_seqlen_k, wl.scale, wl.num_kv_heads,
-                                                   wl.sliding_window)
+                                                   wl.sliding_window, alibi_slopes=self._slopes())
         return pa.pa_decode_with_store(op.query.to(d), k, v, sl, self.cache, self.i32(op.block_table),
                                        self.i32(op.seq_lens), op.max_seq_len, wl.scale, wl.num_kv_heads,
-                                       wl.sliding_window, partition_size=partition_size)
+                                       wl.sliding_window, partition_size=partition_size,
+                                       alibi_slopes=self._slopes())
 
 
-def oracle_attention(wl: W.Workload, op, cache_vals: np.ndarray, picks=None) -> np.ndarray:
-    """Oracle output for a prefill/decode op; ``picks`` = list of (row, head) to sample."""
+def oracle_attention(wl: W.Workload, op, cache_vals: np.ndarray, picks=None, alibi=None) -> np.ndarray:
+    """Oracle output for a prefill/decode op; ``picks`` = list of (row, head) to sample;
+    ``alibi`` = optional ALiBi slopes [num_heads]."""
     q = host_values(op.query)
     if isinstance(op, W.PrefillOp):
         cu_q, cu_k = op.cu_seqlens_q, op.cu_seqlens_k
@@ -109,9 +116,9 @@ def oracle_attention(wl: W.Workload, op, cache_vals: np.ndarray, picks=None) -> 
         cu_k = np.concatenate([[0], np.cumsum(op.seq_lens)])
     if picks is None:
         return oracle.prefill_varlen(q, cache_vals, op.block_table, cu_q, cu_k, wl.scale,
-                                     wl.num_kv_heads, wl.sliding_window)
+                                     wl.num_kv_heads, wl.sliding_window, alibi)
     return oracle.attention_rows(q, cache_vals, op.block_table, cu_q, cu_k, wl.scale,
-                                 wl.num_kv_heads, wl.sliding_window, picks)
+                                 wl.num_kv_heads, wl.sliding_window, picks, alibi)
 
 
 def sample_picks(op, num_heads: int, rng: np.random.Generator, n_random: int = 96):

@@ -48,8 +48,8 @@ def test_status_strings(lib):
 def test_zero_work_is_ok_without_launch(lib):
     assert lib.pa_store_kv(desc(), None, None, None, 0, None) == 0
     assert lib.pa_copy_blocks(desc(), None, 0, None) == 0
-    assert lib.pa_prefill_varlen(desc(), None, None, None, 1, None, None, 0, 0, 0, 8, 1.0, 0, None) == 0
-    assert lib.pa_decode(desc(), None, None, None, 1, None, 0, 0, 8, 1.0, 0, 0, None, 0, None) == 0
+    assert lib.pa_prefill_varlen(desc(), None, None, None, 1, None, None, 0, 0, 0, 8, 1.0, 0, None, None) == 0
+    assert lib.pa_decode(desc(), None, None, None, 1, None, 0, 0, 8, 1.0, 0, None, 0, None, 0, None) == 0
 
 
 @pytest.mark.parametrize("kw,status,needle", [
@@ -85,7 +85,7 @@ def test_prefill_argument_checks(lib):
     def call(d=None, **k):
         a = args(**k)
         return lib.pa_prefill_varlen(d or desc(), a["out"], a["q"], a["tab"], a["mb"], a["cuq"], a["cuk"],
-                                     a["b"], a["msq"], a["msk"], a["h"], a["scale"], a["w"], None)
+                                     a["b"], a["msq"], a["msk"], a["h"], a["scale"], a["w"], None, None)
     assert call(h=7) == 1 and b"multiple" in lib.pa_last_error()
     assert call(h=0) == 1
     assert call(h=2 * 17) == 2 and b"16" in lib.pa_last_error()          # group 17 > 16 for bf16
@@ -93,6 +93,7 @@ def test_prefill_argument_checks(lib):
     assert call(mb=0) == 1
     assert call(msk=65) == 1 and b"max_blocks_per_seq" in lib.pa_last_error()
     assert call(scale=float("nan")) == 1
+    assert call(scale=-0.5) == 1 and b"scale" in lib.pa_last_error()   # the kernels assume scale >= 0
     assert call(d=desc(bs=8)) == 2                                      # bf16 needs block_size >= 16
     assert call(b=-1) == 1
 
@@ -104,12 +105,12 @@ def test_decode_argument_and_workspace_checks(lib):
     need = lib.pa_decode_workspace_size(d, 64, 32, 4097, 0, 128)
     assert need == -(-64 * 129 // 4) * 2 * 32 * (128 + 2) * 4
     # too small a workspace is rejected before any launch
-    assert lib.pa_decode(d, FAKE, FAKE, FAKE, 300, FAKE, 64, 4097, 32, 0.1, 0, 128, FAKE, need - 1, None) == 3
-    assert lib.pa_decode(d, FAKE, FAKE, FAKE, 300, FAKE, 64, 4097, 32, 0.1, 0, 128, None, need, None) == 3
-    assert lib.pa_decode(d, FAKE, FAKE, FAKE, 300, FAKE, 64, 4097, 32, 0.1, 0, 48, FAKE, need, None) == 1
-    assert lib.pa_decode(d, FAKE, FAKE, FAKE, 300, FAKE, 64, 4097, 32, 0.1, 0, -32, FAKE, need, None) == 1
-    assert lib.pa_decode(d, FAKE, FAKE, FAKE, 200, FAKE, 64, 4097, 32, 0.1, 0, 128, FAKE, need, None) == 1
-    assert lib.pa_decode(d, None, FAKE, FAKE, 300, FAKE, 64, 4097, 32, 0.1, 0, 128, FAKE, need, None) == 1
+    assert lib.pa_decode(d, FAKE, FAKE, FAKE, 300, FAKE, 64, 4097, 32, 0.1, 0, None, 128, FAKE, need - 1, None) == 3
+    assert lib.pa_decode(d, FAKE, FAKE, FAKE, 300, FAKE, 64, 4097, 32, 0.1, 0, None, 128, None, need, None) == 3
+    assert lib.pa_decode(d, FAKE, FAKE, FAKE, 300, FAKE, 64, 4097, 32, 0.1, 0, None, 48, FAKE, need, None) == 1
+    assert lib.pa_decode(d, FAKE, FAKE, FAKE, 300, FAKE, 64, 4097, 32, 0.1, 0, None, -32, FAKE, need, None) == 1
+    assert lib.pa_decode(d, FAKE, FAKE, FAKE, 200, FAKE, 64, 4097, 32, 0.1, 0, None, 128, FAKE, need, None) == 1
+    assert lib.pa_decode(d, None, FAKE, FAKE, 300, FAKE, 64, 4097, 32, 0.1, 0, None, 128, FAKE, need, None) == 1
     # a batch that fits one chunk needs no workspace; float32 never needs one
     assert lib.pa_decode_workspace_size(d, 1, 32, 100, 0, 128) == 0
     assert lib.pa_decode_workspace_size(d, 64, 32, 0, 0, 0) == 0
@@ -128,3 +129,21 @@ def test_decode_auto_chunks_without_device(lib):
     # 4 sequences of at most 100 keys: 16 steps -> 4 chunks; one sequence: 4 steps -> 1 chunk
     assert lib.pa_decode_workspace_size(d8, 4, 32, 100, 0, 0) == 4 * 2 * 32 * 130 * 4
     assert lib.pa_decode_workspace_size(d8, 1, 32, 100, 0, 0) == 0
+
+
+def test_fused_store_entry_points_check_arguments(lib):
+    d = desc(nb=64, bs=16, hkv=2, d=128)
+    # prefill with store: key/value/slot_mapping required once there are rows
+    args = (d, FAKE, FAKE, None, FAKE, FAKE, 40, FAKE, 4, FAKE, FAKE, 2, 20, 30, 8, 0.1, 0, None, None)
+    assert lib.pa_prefill_varlen_with_store(*args) == 1 and b"key" in lib.pa_last_error()
+    args = (d, FAKE, FAKE, FAKE, FAKE, FAKE, -1, FAKE, 4, FAKE, FAKE, 2, 20, 30, 8, 0.1, 0, None, None)
+    assert lib.pa_prefill_varlen_with_store(*args) == 1
+    args = (d, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, 4, FAKE, FAKE, 2, 20, 30, 8, 0.1, 0, None, None)
+    assert lib.pa_prefill_varlen_with_store(*args) == 1                  # rows but no tokens
+    args = (d, None, None, None, None, None, 0, None, 1, None, None, 0, 0, 0, 8, 0.1, 0, None, None)
+    assert lib.pa_prefill_varlen_with_store(*args) == 0                  # empty batch
+    # decode with store
+    args = (d, FAKE, FAKE, None, FAKE, FAKE, FAKE, 4, FAKE, 3, 60, 8, 0.1, 0, None, 0, FAKE, 1 << 20, None)
+    assert lib.pa_decode_with_store(*args) == 1 and b"key" in lib.pa_last_error()
+    args = (d, None, None, None, None, None, None, 1, None, 0, 0, 8, 0.1, 0, None, 0, None, 0, None)
+    assert lib.pa_decode_with_store(*args) == 0                          # no sequences

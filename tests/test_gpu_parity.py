@@ -58,11 +58,11 @@ def _check_phase(run: GpuRun, ops, cache_ref_bits, *, picks_rng=None, partition_
             vals = host_values(run.cache.cpu())
             got = out.float().cpu().numpy()
             if picks_rng is None:
-                ref = oracle_attention(wl, op, vals)
+                ref = oracle_attention(wl, op, vals, alibi=run.alibi)
                 err = assert_close(got, ref, wl.dtype, f"{label} {name}")
             else:
                 picks = sample_picks(op, wl.num_heads, picks_rng)
-                ref = oracle_attention(wl, op, vals, picks)
+                ref = oracle_attention(wl, op, vals, picks, alibi=run.alibi)
                 sel = np.stack([got[r, h] for r, h in picks])
                 err = assert_close(sel, ref, wl.dtype, f"{label} {name} (sampled {len(picks)})")
             say(f"[{label}] {name} max abs err {err:.3e}")
@@ -94,11 +94,11 @@ def _check_phase_with_store(run: GpuRun, ops, cache_ref_bits, *, picks_rng=None,
         vals = host_values(host)
         got = out.float().cpu().numpy()
         if picks_rng is None:
-            ref = oracle_attention(wl, op, vals)
+            ref = oracle_attention(wl, op, vals, alibi=run.alibi)
             err = assert_close(got, ref, wl.dtype, f"{label} {name}")
         else:
             picks = sample_picks(op, wl.num_heads, picks_rng)
-            ref = oracle_attention(wl, op, vals, picks)
+            ref = oracle_attention(wl, op, vals, picks, alibi=run.alibi)
             sel = np.stack([got[r, h] for r, h in picks])
             err = assert_close(sel, ref, wl.dtype, f"{label} {name} (sampled {len(picks)})")
         say(f"[{label}] {name} with store: max abs err {err:.3e}")
@@ -408,3 +408,47 @@ def test_config_with_store_sampled(n):
     for i, ph in enumerate(wl.phases):
         ref = _check_phase_with_store(run, ph, ref, picks_rng=np.random.default_rng(100 + n),
                                       label=f"config{n} phase {i} fused")
+
+
+# ----------------------------------------------------------------------------- ALiBi
+
+
+def _slopes(H):
+    """The ALiBi paper's geometric slopes (2^(-8 i / H) for H a power of two, and for other
+    counts the same formula), scaled by 4 so that the bias matters at these lengths."""
+    return 4.0 * np.array([2.0 ** (-8.0 * (i + 1) / H) for i in range(H)])
+
+
+@pytest.mark.parametrize("name", ["g4_d128_causal", "g4_d128_chunked_window", "g5_d128_window17",
+                                  "g8_d64", "g1_d128_rows128", "f32_d64", "f32_d128_window"])
+@pytest.mark.parametrize("fused", [False, True])
+def test_small_prefill_alibi(name, fused):
+    H, Hkv, D, BS, win, dt, spec = PREFILL_CASES[name]
+    seqs = [W.SeqSpec(c, [q], ["prefill"]) for c, q in spec]
+    wl = W.build(name, 100, seqs, num_heads=H, num_kv_heads=Hkv, head_size=D, block_size=BS,
+                 dtype=dt, sliding_window=win)
+    run = GpuRun(wl, DEV)
+    run.alibi = _slopes(H)
+    check = _check_phase_with_store if fused else _check_phase
+    check(run, wl.phases[0], bits(wl.kv_cache), label=f"{name}/alibi{'/fused' if fused else ''}")
+
+
+@pytest.mark.parametrize("name", ["g4_d128", "g5_d128_window", "g16_d128", "f32_d64"])
+@pytest.mark.parametrize("part", [0, 64])
+def test_small_decode_alibi(name, part):
+    H, Hkv, D, BS, win, dt, ctxs = DECODE_CASES[name]
+    seqs = [W.SeqSpec(c, [1], ["decode"]) for c in ctxs]
+    wl = W.build(name, 200, seqs, num_heads=H, num_kv_heads=Hkv, head_size=D, block_size=BS,
+                 dtype=dt, sliding_window=win)
+    run = GpuRun(wl, DEV)
+    run.alibi = _slopes(H)
+    _check_phase(run, wl.phases[0], bits(wl.kv_cache), partition_size=part, label=f"{name}/alibi/p{part}")
+
+
+@pytest.mark.parametrize("n", [2, 3])
+def test_config_alibi_sampled(n):
+    wl = _config(n)
+    run = GpuRun(wl, DEV)
+    run.alibi = _slopes(wl.num_heads) / 16.0     # long contexts: a gentler bias keeps many keys alive
+    _check_phase(run, wl.phases[0], bits(wl.kv_cache), picks_rng=np.random.default_rng(200 + n),
+                 label=f"config{n}/alibi")
