@@ -106,7 +106,7 @@ def copy_bytes(op, wl) -> float:
 class Step:
     """Device-resident inputs of one phase and a callable that runs it."""
 
-    def __init__(self, wl, ops, dev, partition_size=0, fused=False):
+    def __init__(self, wl, ops, dev, partition_size=0, fused=False, alibi=False):
         """fused: every attention op runs as its *_with_store call on its own rows of the
         phase's store (the separate store op is dropped)."""
         import numpy as np
@@ -116,6 +116,9 @@ class Step:
         self.wl, self.ops, self.dev = wl, ops, dev
         i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)  # noqa: E731
         self.cache = wl.kv_cache.to(dev)
+        # ALiBi: the ALiBi paper's geometric slopes 2^(-8 i / H)
+        self.slopes = (torch.tensor([2.0 ** (-8.0 * (i + 1) / wl.num_heads) for i in range(wl.num_heads)],
+                                    dtype=torch.float32, device=dev) if alibi else None)
         self.prepared = []
         store = next((op for op in ops if type(op).__name__ == "StoreOp"), None)
         for op in ops:
@@ -155,18 +158,21 @@ class Step:
         elif name == "PrefillOp" and d.get("fused"):
             pa.pa_prefill_varlen_with_store(d["q"], d["nk"], d["nv"], d["nslots"], self.cache, d["table"],
                                             d["cuq"], d["cuk"], op.max_seqlen_q, op.max_seqlen_k, wl.scale,
-                                            wl.num_kv_heads, wl.sliding_window, out=d["out"])
+                                            wl.num_kv_heads, wl.sliding_window, out=d["out"],
+                                            alibi_slopes=self.slopes)
         elif name == "PrefillOp":
             pa.pa_prefill_varlen(d["q"], self.cache, d["table"], d["cuq"], d["cuk"], op.max_seqlen_q,
-                                 op.max_seqlen_k, wl.scale, wl.num_kv_heads, wl.sliding_window, out=d["out"])
+                                 op.max_seqlen_k, wl.scale, wl.num_kv_heads, wl.sliding_window, out=d["out"],
+                                 alibi_slopes=self.slopes)
         elif name == "DecodeOp" and d.get("fused"):
             pa.pa_decode_with_store(d["q"], d["nk"], d["nv"], d["nslots"], self.cache, d["table"], d["lens"],
                                     op.max_seq_len, wl.scale, wl.num_kv_heads, wl.sliding_window,
-                                    out=d["out"], workspace=d["ws"], partition_size=d["part"])
+                                    out=d["out"], workspace=d["ws"], partition_size=d["part"],
+                                    alibi_slopes=self.slopes)
         elif name == "DecodeOp":
             pa.pa_decode(d["q"], self.cache, d["table"], d["lens"], op.max_seq_len, wl.scale,
                          wl.num_kv_heads, wl.sliding_window, out=d["out"], workspace=d["ws"],
-                         partition_size=d["part"])
+                         partition_size=d["part"], alibi_slopes=self.slopes)
 
     def time(self, steps: int, warmup: int, flush_bytes: int = 0):
         """Mean step time, mean HIP-event duration of every op, and wall time per step
@@ -319,11 +325,12 @@ def _workload(n):
     return W.config(n)
 
 
-def bench_workload(name, steps, warmup, dev, with_cpu, partition_size=0, flush_mb=1024, fused=False):
+def bench_workload(name, steps, warmup, dev, with_cpu, partition_size=0, flush_mb=1024, fused=False,
+                   alibi=False):
     import workloads as W
     wl = _workload(WORKLOAD_CONFIG[name])
     phase = wl.phases[-1] if name == "chunked_decode" else wl.phases[0]
-    step = Step(wl, phase, dev, partition_size, fused)
+    step = Step(wl, phase, dev, partition_size, fused, alibi)
     step_t, per_op, wall = step.time(steps, warmup, flush_mb * 1024 * 1024)
     ops = [d["op"] for d in step.prepared]
     res = {"workload": W.CONFIG_NAMES[WORKLOAD_CONFIG[name]], "ms_per_step": round(step_t * 1e3, 4),
@@ -347,14 +354,14 @@ def bench_workload(name, steps, warmup, dev, with_cpu, partition_size=0, flush_m
                 "bytes": b + sb, "tokens_per_s": round(len(op.seq_lens) / t, 1),
                 "partition_size": d["part"] or "auto",
                 "roofline": roofline((b + sb) / t / 1e9, HBM_PEAK_GBS, "GB/s", "hbm",
-                                     read_traffic("decode") if name == "decode" and not fused else None)}
+                                     read_traffic("decode") if name == "decode" and not fused and not alibi else None)}
         elif n == "PrefillOp":
             f = prefill_flops(op, wl)
             total_flops += f
             res["ops"]["prefill_with_store" if fused else "prefill"] = {
                 "ms": round(t * 1e3, 4), "TFLOP/s": round(f / t / 1e12, 2), "flops": f,
                 "roofline": roofline(f / t / 1e12, BF16_PEAK_TFLOPS, "TFLOP/s", "mfma",
-                                     read_traffic("prefill") if name == "prefill" and not fused else None)}
+                                     read_traffic("prefill") if name == "prefill" and not fused and not alibi else None)}
         elif n == "StoreOp":
             b = store_bytes(op, wl)
             total_bytes += b
@@ -442,6 +449,11 @@ def main() -> int:
                                         "step_GB/s" if name == "decode" else "step_TFLOP/s":
                                         r["step_GB/s"] if name == "decode" else r["step_TFLOP/s"],
                                         "ops": r["ops"]}
+        # the same two steps with ALiBi slopes
+        line["alibi"] = {}
+        for name in ("decode", "prefill"):
+            r = bench_workload(name, 20, 5, dev, False, flush_mb=args.flush_mb, alibi=True)
+            line["alibi"][name] = {"workload": r["workload"], "ms_per_step": r["ms_per_step"], "ops": r["ops"]}
         # the other two workloads, every op with its roofline (no CPU baseline): chunked prefill
         # with a 4096-key window and the decode after it (config 4), and the mixed step
         # copy_blocks -> store -> prefill -> decode (config 5)
