@@ -9,11 +9,15 @@ from .paged_attention import (  # noqa: F401
     allowed_mask,
     attention_probs,
     attention_rows,
+    cascade_decode,
+    cascade_split,
     copy_blocks,
     decode,
     gather_kv,
     key_range,
     kv_head_of,
+    merge_partials,
+    partial_attention,
     prefill_varlen,
     store_kv,
 )

@@ -40,6 +40,15 @@ Every function takes numpy arrays and follows the pages' statement of the proble
 Decode is the same definition with one query per sequence and ``seqlen_k = seq_lens[s]``
 (MinivLLM API docs, section paged_attention_decode: one query, ``context_lens`` valid
 keys).  All floating-point work is fp64.
+
+* Cascade (shared-prefix) decode: when the sequences of a batch share their first
+  ``common_prefix_len`` keys through the same physical blocks, attention is taken in two
+  parts, the shared prefix for all queries at once and then each sequence's own keys, and
+  the parts are combined; the result equals plain decode (vLLM learning book, section 8
+  Cascade Attention, the self-check question 4, and the cascade fields of section 4
+  FlashAttentionMetadata).  The pages do not write out the
+  combination; the one that makes the two parts equal to a softmax over their union is the
+  log-sum-exp weighting of ``merge_partials``.
 """
 
 from __future__ import annotations
@@ -58,6 +67,10 @@ __all__ = [
     "attention_rows",
     "prefill_varlen",
     "decode",
+    "partial_attention",
+    "merge_partials",
+    "cascade_split",
+    "cascade_decode",
 ]
 
 
@@ -276,3 +289,85 @@ def decode(query, kv_cache, block_table, seq_lens, scale, num_kv_heads,
     cu_k = np.concatenate([[0], np.cumsum(seq_lens)])
     return prefill_varlen(query, kv_cache, block_table, cu_q, cu_k, scale, num_kv_heads,
                           sliding_window, alibi_slopes)
+
+
+# ----------------------------------------------------------------------------- cascade
+
+
+def partial_attention(q_row, k, v, scale):
+    """Attention of one query over one part of its keys: ``(o, lse)``.
+
+    ``o = softmax(scale * k q) v`` over the part's rows and ``lse = log sum exp(scale * k q)``;
+    a part with no key gives ``(0, -inf)``.
+    """
+    if len(k) == 0:
+        return np.zeros(v.shape[1], dtype=np.float64), -np.inf
+    z = float(scale) * (k @ np.asarray(q_row, dtype=np.float64))
+    zmax = z.max()
+    w = np.exp(z - zmax)
+    return (w / w.sum()) @ v, zmax + np.log(w.sum())
+
+
+def merge_partials(parts):
+    """Combine ``[(o_i, lse_i)]`` of disjoint key sets into the attention over their union.
+
+    A softmax over the union weights part ``i`` by ``exp(lse_i)`` relative to the others:
+    ``o = sum_i exp(lse_i - L) o_i`` with ``L = log sum_i exp(lse_i)``.  All parts empty gives
+    the zero row of an empty softmax.
+    """
+    lses = np.array([lse for _, lse in parts], dtype=np.float64)
+    if not np.isfinite(lses).any():
+        return np.zeros_like(parts[0][0])
+    top = lses[np.isfinite(lses)].max()
+    w = np.exp(lses - top)
+    w = w / w.sum()
+    return sum(wi * o for wi, (o, _) in zip(w, parts))
+
+
+def cascade_split(seq_len, common_prefix_len):
+    """Key positions of the shared part and of the sequence's own part: ``[0, P)`` and
+    ``[P, seq_len)`` (vLLM learning book, self-check question 4: the shared segment, then each
+    request's later segment)."""
+    return range(0, common_prefix_len), range(common_prefix_len, seq_len)
+
+
+def cascade_decode(query, kv_cache, block_table, seq_lens, scale, num_kv_heads,
+                   common_prefix_len) -> np.ndarray:
+    """Shared-prefix decode, ``[num_seqs, num_heads, head_size]`` fp64.
+
+    vLLM learning book, section 8 (Cascade Attention) and self-check question 4: (1) every
+    query of the batch attends the one shared prefix, read once through the first
+    sequence's block table; (2) each query attends its own sequence's keys after the prefix;
+    (3) the two parts are combined (``merge_partials``).  The prefix is a whole number of
+    blocks (the scheduler counts common prefix blocks), every sequence holds at least the
+    prefix, and every block-table row starts with the same prefix blocks; anything else
+    raises ``ValueError``.  No sliding window and no ALiBi (every prefix key is visible to
+    every query with the same weight rule).
+    """
+    q = np.asarray(query, dtype=np.float64)
+    seq_lens = np.asarray(seq_lens, dtype=np.int64)
+    num_seqs, num_heads, head_size = q.shape
+    block_size = kv_cache.shape[2]
+    P = int(common_prefix_len)
+    if P < 0 or P % block_size != 0:
+        raise ValueError("common_prefix_len must be a non-negative multiple of block_size")
+    nb = P // block_size
+    if num_seqs and (seq_lens < P).any():
+        raise ValueError("every sequence must hold the whole common prefix")
+    for s in range(num_seqs):
+        if not np.array_equal(block_table[s, :nb], block_table[0, :nb]):
+            raise ValueError(f"sequence {s} does not share the prefix blocks")
+    out = np.zeros((num_seqs, num_heads, head_size), dtype=np.float64)
+    for h in range(num_heads):
+        g = kv_head_of(h, num_heads, num_kv_heads)
+        # (1) the shared part, for every query at once
+        pre_pos, _ = cascade_split(P, P)
+        kp, vp = gather_kv(kv_cache, block_table[0], pre_pos, g)
+        shared = [partial_attention(q[s, h], kp, vp, scale) for s in range(num_seqs)]
+        for s in range(num_seqs):
+            # (2) the sequence's own part, (3) the combination
+            _, own_pos = cascade_split(int(seq_lens[s]), P)
+            ko, vo = gather_kv(kv_cache, block_table[s], own_pos, g)
+            own = partial_attention(q[s, h], ko, vo, scale)
+            out[s, h] = merge_partials([shared[s], own])
+    return out

@@ -445,3 +445,70 @@ def test_alibi_decode_and_rows_agree_with_prefill():
     rows = oracle.attention_rows(c["q"], c["cache"], c["table"], c["cu_q"], c["cu_k"], 0.4, 2, 5, picks,
                                  alibi_slopes=slopes)
     np.testing.assert_allclose(rows, np.stack([p[t, h] for t, h in picks]), rtol=1e-12, atol=1e-13)
+
+
+# ----------------------------------------------------------------------------- cascade pins
+
+
+def _shared_prefix_case(seed, lens, P, H, Hkv, D, BS):
+    """Sequences whose first ``P`` keys are the same rows, paged with the prefix blocks shared:
+    every block-table row starts with the first sequence's prefix blocks."""
+    rng = np.random.default_rng(seed)
+    kp = rng.standard_normal((P, Hkv, D)); vp = rng.standard_normal((P, Hkv, D))
+    ks = [np.concatenate([kp, rng.standard_normal((n - P, Hkv, D))]) for n in lens]
+    vs = [np.concatenate([vp, rng.standard_normal((n - P, Hkv, D))]) for n in lens]
+    cache, table = paged_from_contiguous(ks, vs, BS, rng, extra_blocks=2)
+    table[1:, :P // BS] = table[0, :P // BS]
+    q = rng.standard_normal((len(lens), H, D))
+    return q, cache, table, ks, vs
+
+
+@pytest.mark.parametrize("P,lens", [(8, [8, 9, 21, 30]), (12, [40, 12, 13]), (0, [5, 17]), (16, [16])])
+def test_cascade_equals_dense_attention_and_plain_decode(P, lens):
+    # vLLM learning book, section 8: the cascade split is mathematically equivalent to plain
+    # attention; checked against torch SDPA on the contiguous keys and against plain decode
+    H, Hkv, D, BS = 6, 2, 8, 4
+    q, cache, table, ks, vs = _shared_prefix_case(80 + P, lens, P, H, Hkv, D, BS)
+    out = oracle.cascade_decode(q, cache, table, np.array(lens), 0.4, Hkv, P)
+    for s, n in enumerate(lens):
+        k = np.repeat(ks[s], H // Hkv, axis=1); v = np.repeat(vs[s], H // Hkv, axis=1)
+        ref = _sdpa(q[s:s + 1], k, v, np.ones((1, n), dtype=bool), 0.4)
+        np.testing.assert_allclose(out[s], ref[0], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(out, oracle.decode(q, cache, table, np.array(lens), 0.4, Hkv),
+                               rtol=1e-12, atol=1e-12)
+
+
+def test_cascade_uniform_weights_closed_form():
+    # q = 0 gives every key the same weight: each output is the mean of all n value rows,
+    # so the prefix part must count P / n of it and the own part (n - P) / n
+    H, Hkv, D, BS, P = 4, 4, 8, 4, 12
+    lens = [13, 20, 40]
+    q, cache, table, ks, vs = _shared_prefix_case(91, lens, P, H, Hkv, D, BS)
+    out = oracle.cascade_decode(np.zeros_like(q), cache, table, np.array(lens), 0.7, Hkv, P)
+    for s in range(len(lens)):
+        np.testing.assert_allclose(out[s], vs[s].mean(axis=0), rtol=1e-13, atol=1e-13)
+
+
+def test_merge_partials_of_any_split_is_the_whole_softmax():
+    rng = np.random.default_rng(92)
+    k = rng.standard_normal((11, 8)); v = rng.standard_normal((11, 8)); q = rng.standard_normal(8)
+    z = 0.6 * (k @ q)
+    whole = (np.exp(z - z.max()) / np.exp(z - z.max()).sum()) @ v
+    for cuts in ([0, 4, 11], [0, 0, 7, 11], [0, 1, 2, 11, 11]):
+        parts = [oracle.partial_attention(q, k[a:b], v[a:b], 0.6) for a, b in zip(cuts[:-1], cuts[1:])]
+        np.testing.assert_allclose(oracle.merge_partials(parts), whole, rtol=1e-13, atol=1e-13)
+    empty = oracle.partial_attention(q, k[:0], v[:0], 0.6)
+    assert empty[1] == -np.inf and not empty[0].any()
+    assert not oracle.merge_partials([empty, empty]).any()
+
+
+def test_cascade_rejects_what_is_not_a_shared_prefix():
+    H, Hkv, D, BS, P = 4, 2, 8, 4, 8
+    q, cache, table, _, _ = _shared_prefix_case(93, [9, 12], P, H, Hkv, D, BS)
+    with pytest.raises(ValueError):
+        oracle.cascade_decode(q, cache, table, np.array([9, 12]), 0.5, Hkv, 6)      # not whole blocks
+    with pytest.raises(ValueError):
+        oracle.cascade_decode(q, cache, table, np.array([9, 12]), 0.5, Hkv, 12)     # 9 < 12
+    bad = table.copy(); bad[1, 1] = table[1, 2]
+    with pytest.raises(ValueError):
+        oracle.cascade_decode(q, cache, bad, np.array([9, 12]), 0.5, Hkv, P)        # block not shared

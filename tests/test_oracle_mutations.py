@@ -26,6 +26,9 @@ PIN_FUNCS = [
     lambda gd: pins.test_store_worked_example(gd),
     lambda gd: pins.test_alibi_matches_the_pages_bias_construction(),
     lambda gd: pins.test_alibi_closed_forms(),
+    lambda gd: pins.test_cascade_equals_dense_attention_and_plain_decode(8, [8, 9, 21, 30]),
+    lambda gd: pins.test_cascade_uniform_weights_closed_form(),
+    lambda gd: pins.test_merge_partials_of_any_split_is_the_whole_softmax(),
 ]
 
 
@@ -79,6 +82,15 @@ def _alibi_half_slope(slope, key_pos, query_pos):
     return 0.5 * slope * (key_pos - query_pos)
 
 
+def _merge_equal_weights(parts):
+    live = [o for o, lse in parts if np.isfinite(lse)]
+    return sum(live) / len(live) if live else np.zeros_like(parts[0][0])
+
+
+def _split_overlapping(seq_len, common_prefix_len):
+    return range(0, common_prefix_len), range(max(0, common_prefix_len - 1), seq_len)
+
+
 _orig_gather = pa.gather_kv
 
 MUTATIONS = {
@@ -91,6 +103,8 @@ MUTATIONS = {
     "store_block_offset_swapped": ("store_kv", _store_offset_swapped),
     "alibi_sign_flipped": ("alibi_bias", _alibi_sign_flipped),
     "alibi_half_slope": ("alibi_bias", _alibi_half_slope),
+    "cascade_merge_equal_weights": ("merge_partials", _merge_equal_weights),
+    "cascade_parts_overlap": ("cascade_split", _split_overlapping),
 }
 
 

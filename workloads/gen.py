@@ -28,7 +28,7 @@ import torch
 
 __all__ = [
     "SeqSpec", "StoreOp", "CopyOp", "PrefillOp", "DecodeOp", "Workload",
-    "cu_seqlens", "slot_mapping", "build", "config", "CONFIG_NAMES",
+    "cu_seqlens", "slot_mapping", "build", "config", "CONFIG_NAMES", "shared_prefix_decode",
 ]
 
 
@@ -127,18 +127,25 @@ def _gauss(rng: np.random.Generator, shape, dtype: torch.dtype) -> torch.Tensor:
 def build(name: str, seed: int, seqs: List[SeqSpec], *, num_heads: int, num_kv_heads: int,
           head_size: int, block_size: int, dtype: torch.dtype, sliding_window: int = 0,
           scale: Optional[float] = None, num_blocks: Optional[int] = None,
-          copy_fraction: float = 0.0, rng: Optional[np.random.Generator] = None) -> Workload:
+          copy_fraction: float = 0.0, rng: Optional[np.random.Generator] = None,
+          shared_prefix: int = 0) -> Workload:
     """Draw the inputs of every phase of ``seqs`` (see the module docstring for the order).
 
     The pool is ``ceil(1.1 * total blocks)`` physical blocks unless ``num_blocks`` is given;
     sequences take blocks in order from one seeded permutation of the pool, and block-table
-    rows are padded with -1.
+    rows are padded with -1.  ``shared_prefix`` (a multiple of ``block_size``, at most every
+    ``ctx0``): the first that many keys of every sequence are the first sequence's, through
+    the same physical blocks (a prefix-cache hit shared by the batch); the other sequences
+    take blocks only for the rest.
     """
     rng = np.random.default_rng(seed) if rng is None else rng
     nphase = max(len(s.q) for s in seqs) if seqs else 0
     n_final = [s.ctx0 + sum(s.q) for s in seqs]
     nblk = [math.ceil(n / block_size) for n in n_final]
-    total = sum(nblk)
+    assert shared_prefix % block_size == 0 and all(s.ctx0 >= shared_prefix for s in seqs)
+    n_shared = shared_prefix // block_size
+    own = [nb - (n_shared if i > 0 else 0) for i, nb in enumerate(nblk)]
+    total = sum(own)
     if num_blocks is None:
         num_blocks = max(1, math.ceil(1.1 * total))
     assert num_blocks >= total, "pool too small"
@@ -147,8 +154,10 @@ def build(name: str, seed: int, seqs: List[SeqSpec], *, num_heads: int, num_kv_h
     tables = np.full((len(seqs), width), -1, dtype=np.int32)
     cursor = 0
     for i, nb in enumerate(nblk):
-        tables[i, :nb] = perm[cursor:cursor + nb]
-        cursor += nb
+        if i > 0 and n_shared:
+            tables[i, :n_shared] = tables[0, :n_shared]
+        tables[i, nb - own[i]:nb] = perm[cursor:cursor + own[i]]
+        cursor += own[i]
     allocated = perm[:cursor]
     free = perm[cursor:]
 
@@ -256,3 +265,19 @@ def config(n: int) -> Workload:
         return build("config5", n, seqs, num_heads=64, num_kv_heads=8, head_size=128, block_size=16,
                      dtype=torch.bfloat16, copy_fraction=0.01, rng=rng)
     raise ValueError(f"no config {n}")
+
+
+def shared_prefix_decode(seed: int = 6, num_seqs: int = 64, prefix: int = 1024, lo: int = 1024,
+                         hi: int = 4096, num_heads: int = 32, num_kv_heads: int = 8,
+                         head_size: int = 128, block_size: int = 16,
+                         dtype: torch.dtype = torch.bfloat16) -> Workload:
+    """One decode step of ``num_seqs`` sequences that share their first ``prefix`` keys (one
+    system prompt, served from the prefix cache): contexts U[lo, hi] (at least ``prefix``),
+    the GQA decode shape otherwise.  The vLLM learning book (self-check question 4) names a
+    shared prefix of at least 256 tokens and at least two requests as the usual trigger."""
+    rng = np.random.default_rng(seed)
+    ctx = rng.integers(max(lo, prefix), hi + 1, size=num_seqs)
+    seqs = [SeqSpec(int(c), [1], ["decode"]) for c in ctx]
+    return build(f"shared_prefix{prefix}_b{num_seqs}", seed, seqs, num_heads=num_heads,
+                 num_kv_heads=num_kv_heads, head_size=head_size, block_size=block_size, dtype=dtype,
+                 rng=rng, shared_prefix=prefix)
