@@ -18,12 +18,17 @@ Default run (one JSON line on stdout):
     its mean duration, timed with HIP events on the stream the library launches on.
   * ``cpu_baseline``: the fp64 numpy oracle on the host, on a bounded sample of the same
     workload, in the same unit.
+  * ``shared_prefix``: decode of 64 sequences that share a 1024-key prefix (contexts
+    U[1024, 4096], same heads), as plain decode and as cascade decode (the shared prefix
+    attended once for all queries).
 
 Algorithmic work (not the work the kernels actually do):
   decode bytes  = sum_s keys(s) * Hkv * D * 2 (K and V) * 2 B + q + out + 4 B per block-table
                   entry read and per seq_len
   prefill FLOPs = sum over (query row, allowed key, head) of 4 * D
   store bytes   = 2 * T * Hkv * D * 2 B read + the same written + 4 B per slot
+  cascade bytes = decode bytes with the shared prefix's K/V and block-table entries counted
+                  once for the batch
 
 Usage: python bench.py [--steps K] [--warmup W] [--workload decode|prefill|chunked|mixed]
 """
@@ -75,6 +80,23 @@ def decode_bytes(op, wl) -> float:
     return float(total)
 
 
+def cascade_bytes(op, wl, prefix: int) -> float:
+    """Decode bytes when the first ``prefix`` keys of every sequence are one shared prefix,
+    read once: the prefix K/V and table entries once, each sequence's own keys and entries."""
+    import numpy as np
+    elt = 2 if wl.dtype.itemsize == 2 else 4
+    row = wl.num_kv_heads * wl.head_size * elt
+    total = 2 * prefix * row + 4 * (prefix // wl.block_size)
+    for n in op.seq_lens.astype(np.int64):
+        own = int(n) - prefix
+        total += 2 * own * row
+        if own > 0:
+            total += 4 * ((int(n) - 1) // wl.block_size - prefix // wl.block_size + 1)
+    b = len(op.seq_lens)
+    total += 2 * b * wl.num_heads * wl.head_size * elt + 4 * b
+    return float(total)
+
+
 def prefill_flops(op, wl) -> float:
     import numpy as np
     cu_q, cu_k = op.cu_seqlens_q.astype(np.int64), op.cu_seqlens_k.astype(np.int64)
@@ -106,9 +128,10 @@ def copy_bytes(op, wl) -> float:
 class Step:
     """Device-resident inputs of one phase and a callable that runs it."""
 
-    def __init__(self, wl, ops, dev, partition_size=0, fused=False, alibi=False):
+    def __init__(self, wl, ops, dev, partition_size=0, fused=False, alibi=False, cascade=0):
         """fused: every attention op runs as its *_with_store call on its own rows of the
-        phase's store (the separate store op is dropped)."""
+        phase's store (the separate store op is dropped).  cascade > 0: decode runs as
+        pa_cascade_decode over a shared prefix of that many keys."""
         import numpy as np
         import torch
         import paged_attention_block_amd as pa
@@ -142,8 +165,13 @@ class Step:
                 d.update(q=op.query.to(dev), table=i32(op.block_table), lens=i32(op.seq_lens))
                 d["out"] = torch.empty_like(d["q"])
                 d["part"] = partition_size
-                need = pa.pa_decode_workspace_size(self.cache, len(op.seq_lens), wl.num_heads,
-                                                   op.max_seq_len, wl.sliding_window, d["part"])
+                d["cascade"] = cascade
+                if cascade:
+                    need = pa.pa_cascade_decode_workspace_size(self.cache, len(op.seq_lens), wl.num_heads,
+                                                               op.max_seq_len, cascade, d["part"])
+                else:
+                    need = pa.pa_decode_workspace_size(self.cache, len(op.seq_lens), wl.num_heads,
+                                                       op.max_seq_len, wl.sliding_window, d["part"])
                 d["ws"] = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
             self.prepared.append(d)
         self.names = [type(d["op"]).__name__ for d in self.prepared]
@@ -169,6 +197,10 @@ class Step:
                                     op.max_seq_len, wl.scale, wl.num_kv_heads, wl.sliding_window,
                                     out=d["out"], workspace=d["ws"], partition_size=d["part"],
                                     alibi_slopes=self.slopes)
+        elif name == "DecodeOp" and d.get("cascade"):
+            pa.pa_cascade_decode(d["q"], self.cache, d["table"], d["lens"], op.max_seq_len, wl.scale,
+                                 wl.num_kv_heads, d["cascade"], out=d["out"], workspace=d["ws"],
+                                 partition_size=d["part"])
         elif name == "DecodeOp":
             pa.pa_decode(d["q"], self.cache, d["table"], d["lens"], op.max_seq_len, wl.scale,
                          wl.num_kv_heads, wl.sliding_window, out=d["out"], workspace=d["ws"],
@@ -319,21 +351,27 @@ def roofline(achieved, peak, unit, bound, traffic=None):
             "frac": round(achieved / peak, 4), "traffic": traffic}
 
 
+SHARED_PREFIX = 1024
+SHARED_PREFIX_NAME = ("shared-prefix decode: B 64, prefix 1024 keys shared, ctx U[1024,4096], H 32/8, "
+                      "D 128, bs 16, bf16")
+
+
 @functools.lru_cache(maxsize=1)
 def _workload(n):
     import workloads as W
-    return W.config(n)
+    return W.shared_prefix_decode(prefix=SHARED_PREFIX) if n == "shared_prefix" else W.config(n)
 
 
 def bench_workload(name, steps, warmup, dev, with_cpu, partition_size=0, flush_mb=1024, fused=False,
-                   alibi=False):
+                   alibi=False, cascade=False):
     import workloads as W
-    wl = _workload(WORKLOAD_CONFIG[name])
+    wl = _workload("shared_prefix" if name == "shared_prefix" else WORKLOAD_CONFIG[name])
     phase = wl.phases[-1] if name == "chunked_decode" else wl.phases[0]
-    step = Step(wl, phase, dev, partition_size, fused, alibi)
+    step = Step(wl, phase, dev, partition_size, fused, alibi, SHARED_PREFIX if cascade else 0)
     step_t, per_op, wall = step.time(steps, warmup, flush_mb * 1024 * 1024)
     ops = [d["op"] for d in step.prepared]
-    res = {"workload": W.CONFIG_NAMES[WORKLOAD_CONFIG[name]], "ms_per_step": round(step_t * 1e3, 4),
+    wname = SHARED_PREFIX_NAME if name == "shared_prefix" else W.CONFIG_NAMES[WORKLOAD_CONFIG[name]]
+    res = {"workload": wname, "ms_per_step": round(step_t * 1e3, 4),
            "wall_ms_per_step": round(wall * 1e3, 4), "cache_eviction_MiB_per_step": flush_mb, "ops": {}}
     total_bytes, total_flops = 0.0, 0.0
     for op, t, d in zip(ops, per_op, step.prepared):
@@ -346,7 +384,15 @@ def bench_workload(name, steps, warmup, dev, with_cpu, partition_size=0, flush_m
             elt = 2 if wl.dtype.itemsize == 2 else 4
             sb = float(2 * 2 * rows * wl.num_kv_heads * wl.head_size * elt + 4 * rows)
             total_bytes += sb
-        if n == "DecodeOp":
+        if n == "DecodeOp" and cascade:
+            b = cascade_bytes(op, wl, SHARED_PREFIX)
+            total_bytes += b
+            res["ops"]["cascade_decode"] = {
+                "ms": round(t * 1e3, 4), "GB/s": round(b / t / 1e9, 1), "bytes": b,
+                "plain_decode_bytes": decode_bytes(op, wl), "tokens_per_s": round(len(op.seq_lens) / t, 1),
+                "partition_size": d["part"] or "auto",
+                "roofline": roofline(b / t / 1e9, HBM_PEAK_GBS, "GB/s", "hbm")}
+        elif n == "DecodeOp":
             b = decode_bytes(op, wl)
             total_bytes += b
             res["ops"]["decode_with_store" if fused else "decode"] = {
@@ -457,6 +503,12 @@ def main() -> int:
         # the other two workloads, every op with its roofline (no CPU baseline): chunked prefill
         # with a 4096-key window and the decode after it (config 4), and the mixed step
         # copy_blocks -> store -> prefill -> decode (config 5)
+        # a batch sharing a 1024-key prefix: plain decode, then cascade decode
+        line["shared_prefix"] = {}
+        for kind, casc in (("decode", False), ("cascade", True)):
+            r = bench_workload("shared_prefix", 20, 5, dev, False, flush_mb=args.flush_mb, cascade=casc)
+            line["shared_prefix"][kind] = {"workload": r["workload"], "ms_per_step": r["ms_per_step"],
+                                           "ops": r["ops"]}
         line["secondary"] = {}
         for name in ("chunked", "chunked_decode", "mixed"):
             r = bench_workload(name, 10, 3, dev, False, flush_mb=args.flush_mb)

@@ -8,6 +8,7 @@
  *   pa_decode          grouped-query decode, one query per sequence, split-K
  *   pa_prefill_varlen_with_store, pa_decode_with_store
  *                      the store of the new tokens and the attention in one call
+ *   pa_cascade_decode  decode of a batch that shares a prefix of cached blocks
  *
  * Conventions shared by every entry point
  *   - All tensor arguments are DEVICE pointers, caller-allocated and caller-owned; the
@@ -171,15 +172,15 @@ size_t pa_decode_workspace_size(const pa_cache_desc* cache, int32_t num_seqs,
  * chunks, one per workgroup; a sequence cut by chunk boundaries leaves a partial softmax
  * state per piece in the workspace, merged afterwards with a log-sum-exp rescale.
  * partition_size 0 = automatic (as many chunks as the device runs at once, of at least
- * 256 keys); otherwise a multiple of 32: chunks of at least that many keys.
+ * 128 keys); otherwise a multiple of 32: chunks of at least that many keys.
  *
  *   out, query   [num_seqs][num_heads][head_size], contiguous, cache dtype
  *   block_table  [num_seqs][max_blocks_per_seq] int32
  *   seq_lens     [num_seqs] int32, each in [0, max_seq_len]
  *   alibi_slopes NULL, or [num_heads] float32 ALiBi slopes (as pa_prefill_varlen, with the
  *                query at position seq_lens[s] - 1)
- *   workspace    device buffer of >= pa_decode_workspace_size(...) bytes (may be NULL when
- *                that is 0); its contents need no initialisation
+ *   workspace    16-byte aligned device buffer of >= pa_decode_workspace_size(...) bytes
+ *                (may be NULL when that is 0); its contents need no initialisation
  * A sequence with seq_lens[s] == 0 gets a zero output row.
  */
 int pa_decode(const pa_cache_desc* cache, void* out, const void* query,
@@ -202,6 +203,41 @@ int pa_decode_with_store(const pa_cache_desc* cache, void* out, const void* quer
                          int32_t max_seq_len, int32_t num_heads, float scale, int32_t sliding_window,
                          const float* alibi_slopes, int32_t partition_size, void* workspace,
                          size_t workspace_bytes, void* stream);
+
+/*
+ * pa_cascade_decode_workspace_size — bytes of device workspace pa_cascade_decode needs
+ * (the split of the own keys as pa_decode_workspace_size, plus the prefix pass's states:
+ * num_seqs * num_heads * (head_size + 2) floats per prefix chunk).  0 for float32 caches.
+ */
+size_t pa_cascade_decode_workspace_size(const pa_cache_desc* cache, int32_t num_seqs,
+                                        int32_t num_heads, int32_t max_seq_len,
+                                        int32_t common_prefix_len, int32_t partition_size);
+
+/*
+ * pa_cascade_decode — decode of a batch whose sequences share their first common_prefix_len
+ * keys through the same physical blocks (a prefix-cache hit, such as one system prompt).
+ *
+ * vLLM learning book, "05. Attention Backends", section 8 (Cascade Attention), the cascade
+ * fields of section 4 (use_cascade, common_prefix_len) and self-check question 4: attention
+ * over the shared prefix is taken once for all queries of the batch, whose K/V is then read
+ * once instead of once per sequence; each sequence then attends only its own keys, and the
+ * two parts are combined by log-sum-exp.  The result equals pa_decode without a window or
+ * ALiBi (up to rounding).
+ *
+ *   common_prefix_len  a multiple of block_size, at most max_seq_len; 0 runs pa_decode
+ *   (other arguments as pa_decode; bf16 caches only: a float32 cache is PA_ERR_UNSUPPORTED)
+ * Preconditions on device data (not checked): every seq_lens[s] >= common_prefix_len, and
+ * entries [0, common_prefix_len / block_size) of every block-table row are the same
+ * physical blocks; the prefix is read through row 0.
+ * Runs the prefix kernel, then the partition (+ merge) kernels of pa_decode on the keys
+ * after the prefix, whose first piece of each sequence starts from the prefix's state.
+ */
+int pa_cascade_decode(const pa_cache_desc* cache, void* out, const void* query,
+                      const int32_t* block_table, int32_t max_blocks_per_seq,
+                      const int32_t* seq_lens, int32_t num_seqs, int32_t max_seq_len,
+                      int32_t num_heads, float scale, int32_t common_prefix_len,
+                      int32_t partition_size, void* workspace, size_t workspace_bytes,
+                      void* stream);
 
 /* Fixed text for a status code. */
 const char* pa_status_string(int status);

@@ -22,6 +22,7 @@ import torch
 __all__ = [
     "PaError", "lib_path", "load", "pa_store_kv", "pa_copy_blocks", "pa_prefill_varlen",
     "pa_decode", "pa_decode_workspace_size", "pa_prefill_varlen_with_store", "pa_decode_with_store",
+    "pa_cascade_decode", "pa_cascade_decode_workspace_size",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -73,8 +74,11 @@ def load() -> ctypes.CDLL:
     lib.pa_prefill_varlen_with_store.argtypes = [D, P, P, P, P, P, I32, P, I32, P, P, I32, I32, I32, I32,
                                                  F32, I32, P, P]
     lib.pa_decode_with_store.argtypes = [D, P, P, P, P, P, P, I32, P, I32, I32, I32, F32, I32, P, I32, P, SZ, P]
+    lib.pa_cascade_decode_workspace_size.argtypes = [D, I32, I32, I32, I32, I32]
+    lib.pa_cascade_decode_workspace_size.restype = SZ
+    lib.pa_cascade_decode.argtypes = [D, P, P, P, I32, P, I32, I32, I32, F32, I32, I32, P, SZ, P]
     for name in ("pa_store_kv", "pa_copy_blocks", "pa_prefill_varlen", "pa_decode",
-                 "pa_prefill_varlen_with_store", "pa_decode_with_store"):
+                 "pa_prefill_varlen_with_store", "pa_decode_with_store", "pa_cascade_decode"):
         getattr(lib, name).restype = ctypes.c_int
     lib.pa_status_string.argtypes = [ctypes.c_int]
     lib.pa_status_string.restype = ctypes.c_char_p
@@ -256,6 +260,59 @@ def pa_decode(query: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Te
                              query.shape[1], float(scale), int(sliding_window),
                              _alibi(alibi_slopes, query, dev), int(partition_size),
                              _ptr(workspace), ws_bytes, _stream(kv_cache)), "pa_decode")
+    return out
+
+
+def pa_cascade_decode_workspace_size(kv_cache: torch.Tensor, num_seqs: int, num_heads: int,
+                                     max_seq_len: int, common_prefix_len: int,
+                                     partition_size: int = 0) -> int:
+    """Workspace bytes ``pa_cascade_decode`` needs, asked on the cache's device."""
+    lib = load()
+    desc = _desc(kv_cache)
+    with (torch.cuda.device(kv_cache.device) if kv_cache.is_cuda else contextlib.nullcontext()):
+        return int(lib.pa_cascade_decode_workspace_size(ctypes.byref(desc), num_seqs, num_heads, max_seq_len,
+                                                        common_prefix_len, partition_size))
+
+
+def pa_cascade_decode(query: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
+                      seq_lens: torch.Tensor, max_seq_len: int, scale: float, num_kv_heads: int,
+                      common_prefix_len: int, out: Optional[torch.Tensor] = None,
+                      workspace: Optional[torch.Tensor] = None, partition_size: int = 0) -> torch.Tensor:
+    """Decode of a batch whose block-table rows all start with the same
+    ``common_prefix_len / block_size`` physical blocks: the shared prefix is attended once
+    for every query, then each sequence's own keys (arguments otherwise as ``pa_decode``)."""
+    lib = load()
+    desc = _desc(kv_cache)
+    dev = kv_cache.device
+    if num_kv_heads != kv_cache.shape[3]:
+        raise ValueError(f"num_kv_heads {num_kv_heads} != cache's {kv_cache.shape[3]}")
+    _need(query, "query", kv_cache.dtype, dev, 3)
+    _need(block_table, "block_table", torch.int32, dev, 2)
+    _need(seq_lens, "seq_lens", torch.int32, dev, 1)
+    num_seqs = query.shape[0]
+    if seq_lens.shape[0] != num_seqs or block_table.shape[0] < num_seqs:
+        raise ValueError("seq_lens must be [num_seqs] and block_table [num_seqs, max_blocks]")
+    if query.shape[2] != kv_cache.shape[4]:
+        raise ValueError("query head_size does not match the cache")
+    if out is None:
+        out = torch.empty_like(query)
+    else:
+        _need(out, "out", kv_cache.dtype, dev, 3)
+        if out.shape != query.shape:
+            raise ValueError("out must match query's shape")
+    need = pa_cascade_decode_workspace_size(kv_cache, num_seqs, query.shape[1], int(max_seq_len),
+                                            int(common_prefix_len), int(partition_size))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if workspace is not None and workspace.device != dev:
+        raise ValueError("workspace must be on the cache's device")
+    with (torch.cuda.device(dev) if dev.type == "cuda" else contextlib.nullcontext()):
+        _check(lib.pa_cascade_decode(ctypes.byref(desc), _ptr(out), _ptr(query), _ptr(block_table),
+                                     block_table.shape[1], _ptr(seq_lens), num_seqs, int(max_seq_len),
+                                     query.shape[1], float(scale), int(common_prefix_len),
+                                     int(partition_size), _ptr(workspace), ws_bytes, _stream(kv_cache)),
+               "pa_cascade_decode")
     return out
 
 

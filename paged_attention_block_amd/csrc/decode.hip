@@ -187,7 +187,7 @@ __device__ inline void decode_chunking(const DecodeArgs& a, int lane, int s_befo
     int tot = 0, pre = 0;
     for (int c = 0; c < a.num_seqs; c += 64) {
         const int sl = c + lane;
-        const int st = sl < a.num_seqs ? decode_steps(a.seq_lens[sl], a.window) : 0;
+        const int st = sl < a.num_seqs ? decode_steps(a.seq_lens[sl], a.window, a.key_start) : 0;
         tot += st;
         pre += sl < s_before ? st : 0;
     }
@@ -200,7 +200,47 @@ __device__ inline int chunk_begin(int w, int S, int nw) { return (int)(((int64_t
 // the chunk that holds step t, 0 <= t < S
 __device__ inline int chunk_of(int t, int S, int nw) { return (int)(((int64_t)(t + 1) * nw - 1) / S); }
 
-template <int D, bool ALIBI>
+// Shared-prefix decode: fold the prefix chunks' states of query head `head` of sequence s
+// into the running state (m_run, l_run, oacc) of this lane by log-sum-exp.  The sums go to
+// the grp 0 lanes only: the partition kernel adds its per-lane partial sums over the four
+// lane groups at the end.
+template <int D>
+__device__ __forceinline__ void fold_prefix(const DecodeArgs& a, int s, int head, int grp,
+                                            f32x4 (&oacc)[D / 16], float& m_run, float& l_run) {
+    constexpr int DPL = D / 16;
+    const int64_t per_chunk = (int64_t)a.num_seqs * a.num_heads;
+    const int64_t row = (int64_t)s * a.num_heads + head;
+    float M = m_run;
+    for (int c = 0; c < a.prefix_chunks; ++c) M = fmaxf(M, a.pre_ml[(c * per_chunk + row) * 2]);
+    const float msub = M == -INFINITY ? 0.f : M;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - msub);
+    float l = l_run * alpha;
+#pragma unroll
+    for (int t = 0; t < DPL; ++t) oacc[t] *= alpha;
+    for (int c = 0; c < a.prefix_chunks; ++c) {
+        const f32x2 ml = *(const f32x2*)(a.pre_ml + (c * per_chunk + row) * 2);
+        const float w = __builtin_amdgcn_exp2f(ml[0] - msub);
+        if (grp == 0) l = fmaf(w, ml[1], l);
+        const float* po = a.pre_o + (c * per_chunk + row) * D;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int d0 = DPL * (4 * grp + r);
+#pragma unroll
+            for (int t = 0; t < DPL; t += 4) {
+                const f32x4 x = *(const f32x4*)(po + d0 + t);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) oacc[t + i][r] = fmaf(w, x[i], oacc[t + i][r]);
+            }
+        }
+    }
+    m_run = M;
+    l_run = l;
+}
+
+// CASCADE: shared-prefix decode.  Every sequence's steps then start at key_start, the first
+// piece of a sequence folds the prefix's state into its own, and a sequence with no own key
+// writes the prefix's result.
+template <int D, bool ALIBI, bool CASCADE>
 __global__ __launch_bounds__(512) void decode_bf16_kernel(const DecodeArgs a) {
     constexpr int KS = D / 32;   // k-slices of q.K^T
     constexpr int DPL = D / 16;  // dims per lane chunk of a V row = PV MFMAs per step
@@ -247,7 +287,7 @@ __global__ __launch_bounds__(512) void decode_bf16_kernel(const DecodeArgs a) {
         if (carry > r1 || (carry == r1 && !last_chunk)) break;
         const int sl = c + lane;
         const int n_l = sl < a.num_seqs ? a.seq_lens[sl] : 0;
-        const int st_l = decode_steps(n_l, a.window);
+        const int st_l = decode_steps(n_l, a.window, a.key_start);
         const int incl = wave_incl_scan(st_l, lane) + carry;
         const int off_l = incl - st_l;
         // sequences of this chunk: those whose steps meet [r0, r1); a sequence with no
@@ -265,8 +305,22 @@ __global__ __launch_bounds__(512) void decode_bf16_kernel(const DecodeArgs a) {
             const int steps = __builtin_amdgcn_readlane(st_l, l);
             const int off = __builtin_amdgcn_readlane(off_l, l);
             __bf16* out_row = (__bf16*)a.out + ((int64_t)s * H + head) * D;
-            if (steps == 0) {  // zero-length sequence: zero output row
-                if (head_ok) {
+            if (steps == 0) {  // no key of its own: the prefix's result, or a zero row
+                if constexpr (CASCADE) {
+                    f32x4 oacc[DPL];
+#pragma unroll
+                    for (int t = 0; t < DPL; ++t) oacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    float m_run = -INFINITY, l_run = 0.f;
+                    fold_prefix<D>(a, s, head_ok ? head : g * G, grp, oacc, m_run, l_run);
+                    const float l_tot = group4_sum(l_run);
+                    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+                    if (head_ok) {
+                        for (int r = 0; r < 4; ++r) {
+                            const int d0 = DPL * (4 * grp + r);
+                            for (int t = 0; t < DPL; ++t) out_row[d0 + t] = (__bf16)(oacc[t][r] * inv);
+                        }
+                    }
+                } else if (head_ok) {
                     for (int r = 0; r < 4; ++r) {
                         const int d0 = DPL * (4 * grp + r);
                         for (int t = 0; t < DPL; ++t) out_row[d0 + t] = (__bf16)0.f;
@@ -276,7 +330,7 @@ __global__ __launch_bounds__(512) void decode_bf16_kernel(const DecodeArgs a) {
             }
             const int ls = max(r0 - off, 0);
             const int le = min(r1 - off, steps);
-            const int lo = decode_lo(n, a.window);
+            const int lo = decode_lo(n, a.window, a.key_start);
             const int base = decode_base(lo);
             const int step_begin = base + 32 * ls;             // multiple of 32
             const int kb = step_begin > lo ? step_begin : lo;  // first live key of the segment
@@ -324,6 +378,9 @@ __global__ __launch_bounds__(512) void decode_bf16_kernel(const DecodeArgs a) {
                 if (k0 >= ke) break;
             }
 
+            if constexpr (CASCADE) {  // the sequence's first piece also holds the prefix
+                if (ls == 0) fold_prefix<D>(a, s, head_ok ? head : g * G, grp, oacc, m_run, l_run);
+            }
             const float l_tot = group4_sum(l_run);
             if (head_ok) {
                 if (ls == 0 && le == steps) {  // the whole sequence: normalised output
@@ -353,6 +410,134 @@ __global__ __launch_bounds__(512) void decode_bf16_kernel(const DecodeArgs a) {
     }
 }
 
+// Shared-prefix pass.  The rows of KV head g are its (sequence, query head) pairs,
+// r = s*G + (head - g*G); a wave takes 16 of them as the 16 MFMA columns that the partition
+// kernel gives to the query heads of one group, so each K/V row it loads serves 16 queries
+// (the prefix is the same keys for every sequence: this is a dense contraction).
+// Workgroup = (KV head g, prefix chunk c, row group rg): its 8 waves split the chunk's 32-key
+// steps, then combine their states by log-sum-exp through LDS in three halving rounds, and
+// wave 0 writes the chunk's state.  Workgroup ids are dealt to the 8 XCDs in turn; they are
+// mapped so that all row groups of one (g, c) run on the same XCD, where the chunk's K/V is
+// read from HBM once and from that XCD's L2 by the other row groups.
+template <int D>
+__global__ __launch_bounds__(512) void cascade_prefix_kernel(const DecodeArgs a, int row_groups) {
+    constexpr int KS = D / 32;
+    constexpr int DPL = D / 16;
+    typedef typename VRow<D>::T VT;
+    __shared__ float red[4][4 * DPL + 2][64];
+    const int lane = threadIdx.x & 63;
+    const int col = lane & 15;
+    const int grp = lane >> 4;
+    const int wave = threadIdx.x >> 6;
+    const int Hkv = a.c.num_kv_heads;
+    const int k = blockIdx.x >> 3;
+    const int u = (blockIdx.x & 7) + 8 * (k / row_groups);
+    const int rg = k % row_groups;
+    if (u >= Hkv * a.prefix_chunks) return;  // whole workgroup, before any barrier
+    const int g = u % Hkv;
+    const int c = u / Hkv;
+    const int G = a.group;
+    const int H = a.num_heads;
+    const int row = 16 * rg + col;
+    const bool row_ok = row < a.num_seqs * G;
+    const int s = row_ok ? row / G : 0;
+    const int head = g * G + (row_ok ? row % G : 0);
+    const int P = a.key_start;
+    const int Ps = (P + 31) >> 5;
+    const int cb = (int)((int64_t)c * Ps / a.prefix_chunks);
+    const int ce = (int)((int64_t)(c + 1) * Ps / a.prefix_chunks);
+    const int st0 = cb + (ce - cb) * wave / 8;
+    const int st1 = cb + (ce - cb) * (wave + 1) / 8;
+    const int kb = 32 * st0;
+    const int ke = min(P, 32 * st1);
+
+    const int BS = a.c.block_size;
+    const int shift = a.c.block_shift;
+    const char* __restrict__ kplane = (const char*)a.c.kv;
+    const char* __restrict__ vplane = kplane + a.c.plane_elems * 2;
+    const float c_log2 = a.scale * 1.4426950408889634f;
+    const int64_t row_elems = (int64_t)Hkv * D;
+    const uint32_t row_bytes = (uint32_t)(row_elems * 2);
+    const uint32_t k_off = (uint32_t)col * row_bytes + 16u * grp;
+    const uint32_t v_off = (uint32_t)(4 * grp) * row_bytes + 2u * DPL * col;
+
+    bf16x8 qf[KS];
+    {
+        const u32x4* qrow = (const u32x4*)((const __bf16*)a.q + ((int64_t)s * H + head) * D);
+#pragma unroll
+        for (int t = 0; t < KS; ++t) {
+            const u32x4 x = qrow[4 * t + grp];
+            qf[t] = __builtin_bit_cast(bf16x8, row_ok ? x : (u32x4)(0u));
+        }
+    }
+    f32x4 oacc[DPL];
+#pragma unroll
+    for (int t = 0; t < DPL; ++t) oacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY;
+    float l_run = 0.f;
+    if (st1 > st0) {
+        // the waves read different keys, so they run free (no barrier in the walk)
+        u32x4 kA[2][KS], kB[2][KS];
+        VT vA[8], vB[8];
+        int k0 = kb;
+        load_step<D>(k0, kb, ke, a.table, shift, BS, row_elems, g, kplane, vplane, k_off, v_off, row_bytes, kA, vA);
+        while (true) {
+            const int n1 = k0 + 32 < ke ? k0 + 32 : k0;
+            load_step<D>(n1, kb, ke, a.table, shift, BS, row_elems, g, kplane, vplane, k_off, v_off, row_bytes, kB, vB);
+            compute_step<D, false>(k0, kb, ke, grp, c_log2, 0.f, 0, qf, kA, vA, oacc, m_run, l_run);
+            k0 += 32;
+            if (k0 >= ke) break;
+            const int n2 = k0 + 32 < ke ? k0 + 32 : k0;
+            load_step<D>(n2, kb, ke, a.table, shift, BS, row_elems, g, kplane, vplane, k_off, v_off, row_bytes, kA, vA);
+            compute_step<D, false>(k0, kb, ke, grp, c_log2, 0.f, 0, qf, kB, vB, oacc, m_run, l_run);
+            k0 += 32;
+            if (k0 >= ke) break;
+        }
+    }
+    // waves [half, 2*half) hand their states to waves [0, half)
+#pragma unroll
+    for (int half = 4; half >= 1; half >>= 1) {
+        if (wave >= half && wave < 2 * half) {
+            float (*slot)[64] = red[wave - half];
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int t = 0; t < DPL; ++t) slot[r * DPL + t][lane] = oacc[t][r];
+            slot[4 * DPL][lane] = m_run;
+            slot[4 * DPL + 1][lane] = l_run;
+        }
+        __syncthreads();
+        if (wave < half) {
+            float (*slot)[64] = red[wave];
+            const float mo = slot[4 * DPL][lane];
+            const float M = fmaxf(m_run, mo);
+            const float msub = M == -INFINITY ? 0.f : M;
+            const float a0 = __builtin_amdgcn_exp2f(m_run - msub);
+            const float a1 = __builtin_amdgcn_exp2f(mo - msub);
+            l_run = fmaf(l_run, a0, slot[4 * DPL + 1][lane] * a1);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int t = 0; t < DPL; ++t) oacc[t][r] = fmaf(oacc[t][r], a0, slot[r * DPL + t][lane] * a1);
+            m_run = M;
+        }
+        __syncthreads();
+    }
+    if (wave != 0) return;
+    const float l_tot = group4_sum(l_run);
+    if (!row_ok) return;
+    const int64_t st = ((int64_t)c * a.num_seqs + s) * H + head;
+    float* po = a.pre_o + st * D;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int d0 = DPL * (4 * grp + r);
+#pragma unroll
+        for (int t = 0; t < DPL; t += 4)
+            *(f32x4*)(po + d0 + t) = f32x4{oacc[t][r], oacc[t + 1][r], oacc[t + 2][r], oacc[t + 3][r]};
+    }
+    if (grp == 0) *(f32x2*)(a.pre_ml + st * 2) = f32x2{m_run, l_tot};
+}
+
 // Merge of the pieces of a sequence cut by chunk boundaries (log-sum-exp rescale by
 // exp2(m_p - max m)): a workgroup of MW waves per (sequence, four query heads); in each wave
 // lanes 16h .. 16h+15 take query head 4*blockIdx.y + h, D/16 dims each.  Wave w folds pieces
@@ -369,7 +554,7 @@ __global__ __launch_bounds__(64 * MW) void decode_merge_kernel(const DecodeArgs 
     const int wv_id = threadIdx.x >> 6;
     int S, nw, off;
     decode_chunking(a, lane, s, S, nw, off);
-    const int steps = decode_steps(a.seq_lens[s], a.window);
+    const int steps = decode_steps(a.seq_lens[s], a.window, a.key_start);
     if (steps == 0) return;
     const int w_lo = chunk_of(off, S, nw);
     const int np = chunk_of(off + steps - 1, S, nw) - w_lo + 1;
@@ -469,8 +654,8 @@ int decode_resident_slots(int head_size, int num_kv_heads) {
         hipError_t e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
         if (e == hipSuccess)
             e = head_size == 128
-                    ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_bf16_kernel<128, false>, 64 * waves, 0)
-                    : hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_bf16_kernel<64, false>, 64 * waves, 0);
+                    ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_bf16_kernel<128, false, false>, 64 * waves, 0)
+                    : hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_bf16_kernel<64, false, false>, 64 * waves, 0);
         if (e != hipSuccess || ncu <= 0 || nb <= 0) {
             (void)hipGetLastError();
             return 256;
@@ -481,17 +666,16 @@ int decode_resident_slots(int head_size, int num_kv_heads) {
     return cus[dev] * per_cu[dev][di][waves];
 }
 
-hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t st) {
+// Partition kernel (+ merge kernel when the batch is cut into more than one chunk).
+template <bool ALIBI, bool CASCADE>
+static void launch_partition_merge(const DecodeArgs& a, hipStream_t st) {
     const int hkv = a.c.num_kv_heads;
     const dim3 grid(a.nw, (hkv + 7) / 8);
     const dim3 block(64 * (hkv < 8 ? hkv : 8));
-    if (a.c.head_size == 128) {
-        if (a.alibi) hipLaunchKernelGGL((decode_bf16_kernel<128, true>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((decode_bf16_kernel<128, false>), grid, block, 0, st, a);
-    } else {
-        if (a.alibi) hipLaunchKernelGGL((decode_bf16_kernel<64, true>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((decode_bf16_kernel<64, false>), grid, block, 0, st, a);
-    }
+    if (a.c.head_size == 128)
+        hipLaunchKernelGGL((decode_bf16_kernel<128, ALIBI, CASCADE>), grid, block, 0, st, a);
+    else
+        hipLaunchKernelGGL((decode_bf16_kernel<64, ALIBI, CASCADE>), grid, block, 0, st, a);
     if (a.nw > 1) {
         const dim3 mg(a.num_seqs, (a.num_heads + 3) / 4);
         const bool many = a.nw > 8 * a.num_seqs;  // more than ~8 pieces per sequence
@@ -503,6 +687,23 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t st) {
             else hipLaunchKernelGGL((decode_merge_kernel<64, 1>), mg, dim3(64), 0, st, a);
         }
     }
+}
+
+hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t st) {
+    if (a.alibi) launch_partition_merge<true, false>(a, st);
+    else launch_partition_merge<false, false>(a, st);
+    return hipGetLastError();
+}
+
+hipError_t launch_cascade_decode_bf16(const DecodeArgs& a, hipStream_t st) {
+    const int row_groups = (a.num_seqs * a.group + 15) / 16;
+    const int units = a.c.num_kv_heads * a.prefix_chunks;
+    const dim3 grid((unsigned)(8LL * row_groups * ((units + 7) / 8)));
+    if (a.c.head_size == 128)
+        hipLaunchKernelGGL((cascade_prefix_kernel<128>), grid, dim3(512), 0, st, a, row_groups);
+    else
+        hipLaunchKernelGGL((cascade_prefix_kernel<64>), grid, dim3(512), 0, st, a, row_groups);
+    launch_partition_merge<false, true>(a, st);
     return hipGetLastError();
 }
 

@@ -107,10 +107,46 @@ Chunks decode_chunks(int32_t num_seqs, int32_t head_size, int32_t num_kv_heads, 
 }
 
 // Largest key span a sequence's steps cover: its live keys [lo, n) plus the < 32 keys
-// between lo and the 32-aligned start of its first step.
-int32_t max_keys_of(int32_t max_seq_len, int32_t window) {
+// between lo and the 32-aligned start of its first step.  start > 0: the keys after a
+// shared prefix of that length.
+int32_t max_keys_of(int32_t max_seq_len, int32_t window, int32_t start = 0) {
+    if (start > 0) return max_seq_len > pa::decode_base(start) ? max_seq_len - pa::decode_base(start) : 0;
     if (window > 0 && max_seq_len > window) return max_seq_len < window + 31 ? max_seq_len : window + 31;
     return max_seq_len;
+}
+
+// Key chunks of a shared prefix of P keys: about one 8-wave prefix workgroup per compute
+// unit over the (KV head, 16-row group) pairs, each wave keeping at least two 32-key steps.
+int32_t cascade_prefix_chunks(int32_t num_seqs, int32_t group, int32_t num_kv_heads, int32_t P) {
+    const int64_t steps = (P + 31) / 32;
+    const int64_t units = (((int64_t)num_seqs * group + 15) / 16) * num_kv_heads;
+    int64_t nc = (256 + units - 1) / units;
+    const int64_t most = steps / 16 > 1 ? steps / 16 : 1;
+    if (nc > most) nc = most;
+    if (nc > 64) nc = 64;
+    return (int32_t)(nc < 1 ? 1 : nc);
+}
+
+// Workspace bytes of a decode launch: partial states of the chunk split (none with a
+// single chunk or a float32 cache), then, with a shared prefix, the prefix chunks' states.
+struct DecodePlan {
+    Chunks c;
+    int32_t prefix_chunks;
+    size_t chunk_bytes;
+    size_t prefix_bytes;
+};
+DecodePlan decode_plan(const pa_cache_desc* cache, int32_t num_seqs, int32_t num_heads, int32_t max_seq_len,
+                       int32_t window, int32_t key_start, int32_t partition_size) {
+    DecodePlan p = {{1, 1}, 0, 0, 0};
+    if (cache->dtype != PA_BF16) return p;
+    p.c = decode_chunks(num_seqs, cache->head_size, cache->num_kv_heads,
+                        max_keys_of(max_seq_len, window > 0 ? window : 0, key_start), partition_size);
+    if (p.c.nw > 1) p.chunk_bytes = (size_t)p.c.nw * 2 * num_heads * ((size_t)cache->head_size + 2) * sizeof(float);
+    if (key_start > 0) {
+        p.prefix_chunks = cascade_prefix_chunks(num_seqs, num_heads / cache->num_kv_heads, cache->num_kv_heads, key_start);
+        p.prefix_bytes = (size_t)p.prefix_chunks * num_seqs * num_heads * ((size_t)cache->head_size + 2) * sizeof(float);
+    }
+    return p;
 }
 
 }  // namespace
@@ -262,12 +298,17 @@ int pa_prefill_varlen_with_store(const pa_cache_desc* cache, void* out, const vo
 size_t pa_decode_workspace_size(const pa_cache_desc* cache, int32_t num_seqs, int32_t num_heads,
                                 int32_t max_seq_len, int32_t sliding_window, int32_t partition_size) {
     if (!cache || num_seqs <= 0 || num_heads <= 0 || max_seq_len <= 0 || partition_size < 0) return 0;
-    if (cache->dtype != PA_BF16) return 0;  // the float32 path needs no workspace
-    const Chunks c = decode_chunks(num_seqs, cache->head_size, cache->num_kv_heads,
-                                   max_keys_of(max_seq_len, sliding_window > 0 ? sliding_window : 0),
-                                   partition_size);
-    if (c.nw <= 1) return 0;
-    return (size_t)c.nw * 2 * num_heads * ((size_t)cache->head_size + 2) * sizeof(float);
+    if (cache->num_kv_heads <= 0 || num_heads % cache->num_kv_heads != 0) return 0;
+    return decode_plan(cache, num_seqs, num_heads, max_seq_len, sliding_window, 0, partition_size).chunk_bytes;
+}
+
+size_t pa_cascade_decode_workspace_size(const pa_cache_desc* cache, int32_t num_seqs, int32_t num_heads,
+                                        int32_t max_seq_len, int32_t common_prefix_len,
+                                        int32_t partition_size) {
+    if (!cache || num_seqs <= 0 || num_heads <= 0 || max_seq_len <= 0 || partition_size < 0) return 0;
+    if (cache->num_kv_heads <= 0 || num_heads % cache->num_kv_heads != 0 || common_prefix_len < 0) return 0;
+    const DecodePlan p = decode_plan(cache, num_seqs, num_heads, max_seq_len, 0, common_prefix_len, partition_size);
+    return p.chunk_bytes + p.prefix_bytes;
 }
 
 // Validation and launch planning shared by pa_decode and pa_decode_with_store; *empty is
@@ -276,7 +317,7 @@ static int decode_args(const pa_cache_desc* cache, void* out, const void* query,
                        int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t num_seqs,
                        int32_t max_seq_len, int32_t num_heads, float scale, int32_t sliding_window,
                        const float* alibi_slopes, int32_t partition_size, void* workspace,
-                       size_t workspace_bytes, pa::DecodeArgs* a_out, bool* empty) {
+                       size_t workspace_bytes, pa::DecodeArgs* a_out, bool* empty, int32_t key_start = 0) {
     pa::DecodeArgs& a = *a_out;
     *empty = false;
     int st = check_cache(cache, &a.c);
@@ -294,7 +335,7 @@ static int decode_args(const pa_cache_desc* cache, void* out, const void* query,
         return fail(PA_ERR_INVALID_ARG, "partition_size must be 0 or a positive multiple of 32 (got %d)", partition_size);
     if (!(scale >= 0.f)) return fail(PA_ERR_INVALID_ARG, "scale must be >= 0 (got %g)", (double)scale);
     const int32_t win = sliding_window > 0 ? sliding_window : 0;
-    if ((int64_t)num_seqs * ((max_keys_of(max_seq_len, win) + 31) / 32 + 1) > 0x7fffffff)
+    if ((int64_t)num_seqs * ((max_keys_of(max_seq_len, win, key_start) + 31) / 32 + 1) > 0x7fffffff)
         return fail(PA_ERR_INVALID_ARG, "num_seqs * max_seq_len too large");
     a.out = out;
     a.q = query;
@@ -311,18 +352,28 @@ static int decode_args(const pa_cache_desc* cache, void* out, const void* query,
     a.min_steps = 1;
     a.ws_o = nullptr;
     a.ws_ml = nullptr;
+    a.key_start = key_start;
+    a.prefix_chunks = 0;
+    a.pre_o = nullptr;
+    a.pre_ml = nullptr;
     if (a.c.dtype == PA_F32) return PA_OK;
     if (a.c.num_kv_heads > 65535) return fail(PA_ERR_INVALID_ARG, "num_kv_heads too large");
-    const size_t need = pa_decode_workspace_size(cache, num_seqs, num_heads, max_seq_len, sliding_window, partition_size);
+    const DecodePlan p = decode_plan(cache, num_seqs, num_heads, max_seq_len, win, key_start, partition_size);
+    const size_t need = p.chunk_bytes + p.prefix_bytes;
     if (need > 0 && (!workspace || workspace_bytes < need))
         return fail(PA_ERR_WORKSPACE, "decode needs %zu workspace bytes, got %zu", need, workspace ? workspace_bytes : 0);
-    if (need > 0) {
-        const Chunks c = decode_chunks(num_seqs, a.c.head_size, a.c.num_kv_heads, max_keys_of(max_seq_len, win),
-                                       partition_size);
-        a.nw = c.nw;
-        a.min_steps = c.min_steps;
+    if (need > 0 && ((uintptr_t)workspace & 15) != 0)
+        return fail(PA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    if (p.chunk_bytes > 0) {
+        a.nw = p.c.nw;
+        a.min_steps = p.c.min_steps;
         a.ws_o = (float*)workspace;
-        a.ws_ml = a.ws_o + (size_t)c.nw * 2 * num_heads * a.c.head_size;
+        a.ws_ml = a.ws_o + (size_t)p.c.nw * 2 * num_heads * a.c.head_size;
+    }
+    if (p.prefix_bytes > 0) {
+        a.prefix_chunks = p.prefix_chunks;
+        a.pre_o = (float*)((char*)workspace + p.chunk_bytes);
+        a.pre_ml = a.pre_o + (size_t)p.prefix_chunks * num_seqs * num_heads * a.c.head_size;
     }
     return PA_OK;
 }
@@ -367,6 +418,32 @@ int pa_decode_with_store(const pa_cache_desc* cache, void* out, const void* quer
     hipError_t e = pa::launch_store(sa, s);
     if (e != hipSuccess) return launch_status(e);
     return launch_status(a.c.dtype == PA_F32 ? pa::launch_decode_f32(a, s) : pa::launch_decode_bf16(a, s));
+}
+
+int pa_cascade_decode(const pa_cache_desc* cache, void* out, const void* query, const int32_t* block_table,
+                      int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t num_seqs,
+                      int32_t max_seq_len, int32_t num_heads, float scale, int32_t common_prefix_len,
+                      int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream) {
+    if (cache && cache->dtype == PA_F32)
+        return fail(PA_ERR_UNSUPPORTED, "shared-prefix decode needs a bf16 cache");
+    if (cache && (cache->block_size <= 0 || common_prefix_len < 0 || common_prefix_len % cache->block_size != 0))
+        return fail(PA_ERR_INVALID_ARG, "common_prefix_len must be a non-negative multiple of block_size (got %d)",
+                    common_prefix_len);
+    if (num_seqs > 0 && common_prefix_len > max_seq_len)
+        return fail(PA_ERR_INVALID_ARG, "common_prefix_len %d exceeds max_seq_len %d", common_prefix_len, max_seq_len);
+    pa::DecodeArgs a;
+    bool empty;
+    int st = decode_args(cache, out, query, block_table, max_blocks_per_seq, seq_lens, num_seqs, max_seq_len,
+                         num_heads, scale, 0, nullptr, partition_size, workspace, workspace_bytes, &a, &empty,
+                         common_prefix_len);
+    if (st) return st;
+    if (empty) { g_last_error[0] = 0; return PA_OK; }
+    if ((int64_t)8 * (((int64_t)num_seqs * a.group + 15) / 16) * (((int64_t)a.c.num_kv_heads * a.prefix_chunks + 7) / 8) >
+        0x7fffffff)
+        return fail(PA_ERR_INVALID_ARG, "num_seqs * num_heads too large for the prefix pass");
+    hipStream_t s = (hipStream_t)stream;
+    if (common_prefix_len == 0) return launch_status(pa::launch_decode_bf16(a, s));
+    return launch_status(pa::launch_cascade_decode_bf16(a, s));
 }
 
 }  // extern "C"

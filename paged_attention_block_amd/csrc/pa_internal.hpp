@@ -41,13 +41,16 @@ constexpr int kWave = 64;
 // Split-K bookkeeping for decode.  Sequence s with n keys attends [lo, n); its keys are
 // walked in 32-key steps from lo rounded down to 32, so every step is aligned in absolute
 // key index.  The steps of the whole batch, sequence after sequence, form one list that is
-// cut into equal chunks, one per partition workgroup.
+// cut into equal chunks, one per partition workgroup.  `start` > 0 (shared-prefix decode)
+// leaves keys [0, start) to the prefix pass: lo is then at least start.
 __host__ __device__ inline int decode_base(int lo) { return lo & ~31; }
-__host__ __device__ inline int decode_lo(int n, int window) {
-    return (window > 0 && n > window) ? n - window : 0;
+__host__ __device__ inline int decode_lo(int n, int window, int start) {
+    const int lo = (window > 0 && n > window) ? n - window : 0;
+    return lo > start ? lo : start;
 }
-__host__ __device__ inline int decode_steps(int n, int window) {
-    return n > 0 ? (n - decode_base(decode_lo(n, window)) + 31) >> 5 : 0;
+__host__ __device__ inline int decode_steps(int n, int window, int start) {
+    const int lo = decode_lo(n, window, start);
+    return n > lo ? (n - decode_base(lo) + 31) >> 5 : 0;
 }
 
 // ---------------------------------------------------------------- launch parameter blocks
@@ -117,6 +120,13 @@ struct DecodeArgs {
     const float* alibi;  // [num_heads] ALiBi slopes, or null
     float* ws_o;         // [nw][2][H][D] unnormalised partial outputs (first, last segment)
     float* ws_ml;        // [nw][2][H][2] running max (log2 units) and sum
+    // shared-prefix decode: every sequence's keys [0, key_start) are one shared prefix,
+    // attended by the prefix pass in prefix_chunks key chunks whose states (unnormalised
+    // output; running max in log2 units and sum) the partition kernel folds in
+    int32_t key_start;
+    int32_t prefix_chunks;
+    float* pre_o;        // [prefix_chunks][num_seqs][H][D]
+    float* pre_ml;       // [prefix_chunks][num_seqs][H][2]
 };
 
 // Host launchers (return hipGetLastError() of the launches).
@@ -126,6 +136,8 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t s);
+// Shared-prefix decode (bf16): prefix pass, then the partition (+ merge) kernels.
+hipError_t launch_cascade_decode_bf16(const DecodeArgs& a, hipStream_t s);
 // Partition workgroups of the bf16 decode kernel that fit on the current device at once
 // (compute units x resident workgroups per unit); 256 when the device cannot be queried.
 int decode_resident_slots(int head_size, int num_kv_heads);

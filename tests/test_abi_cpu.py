@@ -147,3 +147,26 @@ def test_fused_store_entry_points_check_arguments(lib):
     assert lib.pa_decode_with_store(*args) == 1 and b"key" in lib.pa_last_error()
     args = (d, None, None, None, None, None, None, 1, None, 0, 0, 8, 0.1, 0, None, 0, None, 0, None)
     assert lib.pa_decode_with_store(*args) == 0                          # no sequences
+
+
+def test_cascade_decode_checks_and_workspace(lib):
+    d = desc(nb=1000, bs=16, hkv=8, d=128)
+    # own keys after a 1024-key prefix: at most 4097 - 1024 = 3073 keys = 97 steps; chunks
+    # of at least 4 steps -> ceil(64 * 97 / 4) chunks; the prefix (32 steps) over 16-row
+    # groups: 64 * 4 / 16 = 16 groups x 8 KV heads = 128 units -> 2 prefix chunks
+    need = lib.pa_cascade_decode_workspace_size(d, 64, 32, 4097, 1024, 128)
+    assert need == -(-64 * 97 // 4) * 2 * 32 * 130 * 4 + 2 * 64 * 32 * 130 * 4
+    # automatic split without a device: 256 chunks
+    assert lib.pa_cascade_decode_workspace_size(d, 64, 32, 4097, 1024, 0) == 256 * 2 * 32 * 130 * 4 + 2 * 64 * 32 * 130 * 4
+    # no prefix: exactly pa_decode's workspace
+    assert lib.pa_cascade_decode_workspace_size(d, 64, 32, 4097, 0, 128) == lib.pa_decode_workspace_size(d, 64, 32, 4097, 0, 128)
+    args = lambda P, ws=need, dd=d: (dd, FAKE, FAKE, FAKE, 300, FAKE, 64, 4097, 32, 0.1, P, 128, FAKE, ws, None)  # noqa: E731
+    assert lib.pa_cascade_decode(*args(1000)) == 1 and b"multiple of block_size" in lib.pa_last_error()
+    assert lib.pa_cascade_decode(*args(-16)) == 1
+    assert lib.pa_cascade_decode(*args(4112)) == 1 and b"max_seq_len" in lib.pa_last_error()
+    assert lib.pa_cascade_decode(*args(1024, need - 1)) == 3
+    assert lib.pa_cascade_decode(*args(1024, need, desc(dtype=0))) == 2 and b"bf16" in lib.pa_last_error()
+    # a misaligned workspace is refused
+    a = list(args(1024)); a[12] = FAKE + 8
+    assert lib.pa_cascade_decode(*a) == 1 and b"aligned" in lib.pa_last_error()
+    assert lib.pa_cascade_decode(d, None, None, None, 1, None, 0, 0, 32, 0.1, 0, 0, None, 0, None) == 0

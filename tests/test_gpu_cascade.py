@@ -1,0 +1,132 @@
+"""GPU parity of shared-prefix (cascade) decode: pa_cascade_decode through the C ABI against
+the oracle's cascade decode (pinned to plain attention), at small sizes on every output and
+at the GQA decode shape with a 1024-key shared prefix on sampled rows."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from tests.gpu_helpers import GpuRun, assert_close, host_values, sample_picks, say
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    import paged_attention_block_amd as pa
+    pa.load()  # fails loudly when libpa.so is missing
+    yield
+    torch.cuda.synchronize()
+
+
+def _cascade(run: GpuRun, dec, prefix, lens=None, partition_size=0, workspace=None):
+    import paged_attention_block_amd as pa
+    wl = run.wl
+    lens = dec.seq_lens if lens is None else lens
+    return pa.pa_cascade_decode(dec.query.to(DEV), run.cache, run.i32(dec.block_table), run.i32(lens),
+                                int(dec.max_seq_len), wl.scale, wl.num_kv_heads, prefix,
+                                partition_size=partition_size, workspace=workspace)
+
+
+CASES = {
+    # name: (H, Hkv, D, BS, shared prefix, [ctx0 ...]); ctx0 >= prefix, the new token follows
+    "g4_d128_p48": (32, 8, 128, 16, 48, [48, 49, 63, 64, 95, 96, 200, 700]),
+    "g4_d128_p64": (32, 8, 128, 16, 64, [64, 65, 127, 128, 300, 1000, 64, 90]),
+    "g5_d128_p256": (10, 2, 128, 16, 256, [256, 300, 257, 600]),
+    "g8_d64_p32": (16, 2, 64, 32, 32, [32, 33, 100, 31 + 32]),
+    "g16_d128_p512": (16, 1, 128, 16, 512, [512, 520, 900]),
+    "g2_d128_hkv12_p128": (24, 12, 128, 16, 128, [128, 129, 400, 2000, 160]),
+    "g4_d128_b1_p1024": (8, 2, 128, 16, 1024, [1500]),
+}
+
+
+@pytest.mark.parametrize("part", [0, 64, 256])
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_small_cascade_decode(name, part):
+    H, Hkv, D, BS, P, ctxs = CASES[name]
+    seqs = [W.SeqSpec(c, [1], ["decode"]) for c in ctxs]
+    wl = W.build(name, 400, seqs, num_heads=H, num_kv_heads=Hkv, head_size=D, block_size=BS,
+                 dtype=torch.bfloat16, shared_prefix=P)
+    run = GpuRun(wl, DEV)
+    store, dec = wl.phases[0]
+    run.run(store)
+    say(f"[cascade {name} p{part}] B {len(ctxs)} prefix {P}")
+    out = _cascade(run, dec, P, partition_size=part)
+    torch.cuda.synchronize()
+    vals = host_values(run.cache.cpu())
+    ref = oracle.cascade_decode(host_values(dec.query), vals, dec.block_table, dec.seq_lens, wl.scale,
+                                wl.num_kv_heads, P)
+    assert_close(out.float().cpu().numpy(), ref, wl.dtype, f"cascade {name} p{part}")
+
+
+def test_cascade_sequences_with_no_own_key_and_prefix_zero():
+    """Sequences whose whole context is the shared prefix (seq_len == prefix) get the
+    prefix's attention; prefix 0 is plain decode, bit for bit."""
+    import paged_attention_block_amd as pa
+    P = 96
+    seqs = [W.SeqSpec(c, [1], ["decode"]) for c in (96, 100, 96, 400, 130)]
+    wl = W.build("own0", 401, seqs, num_heads=16, num_kv_heads=4, head_size=128, block_size=16,
+                 dtype=torch.bfloat16, shared_prefix=P)
+    run = GpuRun(wl, DEV)
+    store, dec = wl.phases[0]
+    run.run(store)
+    lens = dec.seq_lens.copy()
+    lens[[0, 2]] = P
+    vals = host_values(run.cache.cpu())
+    for part in (0, 64):
+        say(f"[cascade no-own-key p{part}]")
+        out = _cascade(run, dec, P, lens=lens, partition_size=part)
+        torch.cuda.synchronize()
+        ref = oracle.cascade_decode(host_values(dec.query), vals, dec.block_table, lens, wl.scale,
+                                    wl.num_kv_heads, P)
+        assert_close(out.float().cpu().numpy(), ref, wl.dtype, f"no own key p{part}")
+        plain = pa.pa_decode(dec.query.to(DEV), run.cache, run.i32(dec.block_table), run.i32(dec.seq_lens),
+                             int(dec.max_seq_len), wl.scale, wl.num_kv_heads, partition_size=part)
+        zero = _cascade(run, dec, 0, partition_size=part)
+        torch.cuda.synchronize()
+        assert torch.equal(plain.view(torch.int16), zero.view(torch.int16))
+
+
+def test_cascade_workspace_contents_need_no_init():
+    seqs = [W.SeqSpec(c, [1], ["decode"]) for c in (256, 300, 1000, 257, 600, 2000)]
+    wl = W.build("cws", 402, seqs, num_heads=32, num_kv_heads=8, head_size=128, block_size=16,
+                 dtype=torch.bfloat16, shared_prefix=256)
+    import paged_attention_block_amd as pa
+    run = GpuRun(wl, DEV)
+    store, dec = wl.phases[0]
+    run.run(store)
+    need = pa.pa_cascade_decode_workspace_size(run.cache, len(seqs), 32, int(dec.max_seq_len), 256, 64)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device=DEV)
+    a = _cascade(run, dec, 256, partition_size=64, workspace=ws)
+    b = _cascade(run, dec, 256, partition_size=64)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("part", [0, 128])
+def test_shared_prefix_decode_full_size_sampled(part):
+    """B 64, shared prefix 1024, contexts U[1024, 4096], H 32/8, D 128: sampled rows against
+    the oracle's plain decode definition (which the cascade oracle is pinned to equal)."""
+    wl = W.shared_prefix_decode()
+    run = GpuRun(wl, DEV)
+    store, dec = wl.phases[0]
+    run.run(store)
+    say(f"[cascade full p{part}]")
+    out = _cascade(run, dec, 1024, partition_size=part)
+    torch.cuda.synchronize()
+    vals = host_values(run.cache.cpu())
+    picks = sample_picks(dec, wl.num_heads, np.random.default_rng(part + 7), n_random=48)
+    cu_q = np.arange(len(dec.seq_lens) + 1)
+    cu_k = np.concatenate([[0], np.cumsum(dec.seq_lens)])
+    ref = oracle.attention_rows(host_values(dec.query), vals, dec.block_table, cu_q, cu_k, wl.scale,
+                                wl.num_kv_heads, 0, picks)
+    got = out.float().cpu().numpy()
+    assert_close(np.stack([got[r, h] for r, h in picks]), ref, wl.dtype, f"shared prefix full p{part}")
