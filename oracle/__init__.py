@@ -1,4 +1,5 @@
-"""fp64 CPU oracle for paged attention: test infrastructure only.
+"""fp64 CPU oracle for paged attention (and, in ``oracle.fp8``, an FP8 KV cache): test
+infrastructure only.
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s ``cpu_baseline`` leg may
 import this package.  It holds no C sources, so there is nothing to compile for it.
@@ -21,3 +22,4 @@ from .paged_attention import (  # noqa: F401
     prefill_varlen,
     store_kv,
 )
+from . import fp8  # noqa: F401,E402

@@ -122,3 +122,57 @@ def test_pins_catch_planted_mistake(name, monkeypatch, golden_dir):
         except (AssertionError, IndexError, ValueError):
             failures += 1
     assert failures > 0, f"no pin caught mutation {name}"
+
+
+# ----------------------------------------------------------------------------- FP8 cache
+
+
+from oracle import fp8 as _fp8  # noqa: E402
+from tests import test_oracle_fp8 as fp8_pins  # noqa: E402
+
+FP8_PINS = [
+    fp8_pins.test_decode_of_every_code_matches_torch,
+    fp8_pins.test_encode_matches_torch_inside_the_range,
+    fp8_pins.test_round_trip_error_bound,
+    lambda: fp8_pins.test_power_of_two_scales_are_exact(2),
+    lambda: fp8_pins.test_attention_over_grid_values_is_lossless(8.0),
+]
+
+_orig_encode, _orig_decode = _fp8.e4m3_encode, _fp8.e4m3_decode
+
+
+def _encode_truncating(x):
+    # round toward zero instead of to nearest: step just above each code
+    x = np.asarray(x, np.float32)
+    codes = _orig_encode(x)
+    back = _orig_decode(codes)
+    down = np.abs(back) > np.abs(x.astype(np.float64))
+    return np.where(down & (codes & 0x7F > 0), codes - 1, codes).astype(np.uint8)
+
+
+def _decode_bias_8(codes):
+    return _orig_decode(codes) / 2.0
+
+
+def _dequantize_divides(codes, kv_scale):
+    return _orig_decode(codes) / float(np.float32(kv_scale))
+
+
+FP8_MUTATIONS = {
+    "fp8_round_toward_zero": ("e4m3_encode", _encode_truncating),
+    "fp8_exponent_bias_8": ("e4m3_decode", _decode_bias_8),
+    "fp8_read_divides_by_scale": ("dequantize", _dequantize_divides),
+}
+
+
+@pytest.mark.parametrize("name", sorted(FP8_MUTATIONS))
+def test_fp8_pins_catch_planted_mistake(name, monkeypatch):
+    attr, fn = FP8_MUTATIONS[name]
+    monkeypatch.setattr(_fp8, attr, fn)
+    failures = 0
+    for pin in FP8_PINS:
+        try:
+            pin()
+        except (AssertionError, IndexError, ValueError):
+            failures += 1
+    assert failures > 0, f"no pin caught mutation {name}"
