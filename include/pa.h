@@ -46,11 +46,24 @@ typedef enum pa_status {
 
 typedef enum pa_dtype {
     PA_F32 = 0,               /* float32 cache, q/k/v and output                          */
-    PA_BF16 = 1               /* bfloat16 cache, q/k/v and output; fp32 accumulation      */
+    PA_BF16 = 1,              /* bfloat16 cache, q/k/v and output; fp32 accumulation      */
+    PA_FP8_E4M3 = 2           /* 8-bit float cache holding value / kv_scale; q/k/v and
+                                 output bfloat16; fp32 accumulation (see below)           */
 } pa_dtype;
 
 /* Description of the caller's cache.  head_size in {64, 128}; block_size a power of two in
- * [1, 256] for PA_F32 and in [16, 256] for PA_BF16; num_blocks*block_size < 2^31. */
+ * [1, 256] for PA_F32 and in [16, 256] for PA_BF16 and PA_FP8_E4M3; num_blocks*block_size
+ * < 2^31.
+ *
+ * PA_FP8_E4M3 (vllm-npu 0.4.2 diff, torch_sdpa.py forward: the store and decode calls take
+ * kv_cache_dtype and kv_scale; vLLM learning book, "05. Attention Backends", section 5: the
+ * cache planes viewed as an FP8 dtype): one byte per element, the E4M3 format of the OCP 8-bit
+ * floating-point specification (sign, 4 exponent bits with bias 7, 3 mantissa bits, no
+ * infinities, largest finite 448).  The store writes e4m3(x * r), r = fp32(1 / kv_scale),
+ * rounded to nearest even and saturated to +-448; attention reads e4m3 * kv_scale.  kv_scale
+ * must be finite and > 0 for such a cache and is ignored otherwise.  Supported by pa_store_kv,
+ * pa_copy_blocks, pa_decode, pa_decode_with_store and pa_cascade_decode; the prefill calls
+ * return PA_ERR_UNSUPPORTED for it. */
 typedef struct pa_cache_desc {
     void*   kv_cache;
     int32_t num_blocks;
@@ -58,6 +71,7 @@ typedef struct pa_cache_desc {
     int32_t num_kv_heads;
     int32_t head_size;
     int32_t dtype;            /* a pa_dtype value */
+    float   kv_scale;         /* PA_FP8_E4M3 only */
 } pa_cache_desc;
 
 /*
@@ -66,9 +80,11 @@ typedef struct pa_cache_desc {
  * MinivLLM API docs, "Attention" page, section store_kvcache (and its example); vLLM
  * learning book, section 10 question 2: slot = physical_block * block_size + offset, so
  * cache[0][slot / block_size][slot % block_size][:][:] = key[t] and plane 1 = value[t].
- * A negative slot (-1 padding) skips the token.  The copy is bitwise.
+ * A negative slot (-1 padding) skips the token.  The copy is bitwise (for PA_FP8_E4M3 each
+ * element is quantized as the cache description states).
  *
- *   key, value    [num_tokens][num_kv_heads][head_size], contiguous, cache dtype
+ *   key, value    [num_tokens][num_kv_heads][head_size], contiguous, cache dtype (bfloat16
+ *                 for PA_FP8_E4M3)
  *   slot_mapping  [num_tokens] int32
  * Preconditions: every non-negative slot < num_blocks*block_size and no slot repeats
  * (a repeated slot is a write race).

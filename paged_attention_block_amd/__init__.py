@@ -29,8 +29,10 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libpa.so"
 _lib = None
 
-PA_F32, PA_BF16 = 0, 1
-_DTYPES = {torch.float32: PA_F32, torch.bfloat16: PA_BF16}
+PA_F32, PA_BF16, PA_FP8_E4M3 = 0, 1, 2
+# an FP8 cache holds float8_e4m3fn codes of value / kv_scale; its queries, keys, values and
+# outputs are bfloat16
+_DTYPES = {torch.float32: PA_F32, torch.bfloat16: PA_BF16, torch.float8_e4m3fn: PA_FP8_E4M3}
 
 
 class PaError(RuntimeError):
@@ -47,6 +49,7 @@ class _CacheDesc(ctypes.Structure):
         ("num_kv_heads", ctypes.c_int32),
         ("head_size", ctypes.c_int32),
         ("dtype", ctypes.c_int32),
+        ("kv_scale", ctypes.c_float),
     ]
 
 
@@ -118,7 +121,12 @@ def _alibi(slopes: Optional[torch.Tensor], query: torch.Tensor, dev) -> Optional
     return _ptr(slopes)
 
 
-def _desc(kv_cache: torch.Tensor) -> _CacheDesc:
+def _act(kv_cache: torch.Tensor) -> torch.dtype:
+    """dtype of the queries, keys, values and outputs that go with this cache."""
+    return torch.bfloat16 if kv_cache.dtype == torch.float8_e4m3fn else kv_cache.dtype
+
+
+def _desc(kv_cache: torch.Tensor, kv_scale: float = 1.0) -> _CacheDesc:
     if kv_cache.dim() != 5 or kv_cache.shape[0] != 2:
         raise ValueError(f"kv_cache must be [2, num_blocks, block_size, num_kv_heads, head_size], got {tuple(kv_cache.shape)}")
     if kv_cache.dtype not in _DTYPES:
@@ -126,7 +134,7 @@ def _desc(kv_cache: torch.Tensor) -> _CacheDesc:
     if not kv_cache.is_contiguous():
         raise ValueError("kv_cache must be contiguous")
     _, nb, bs, hkv, d = kv_cache.shape
-    return _CacheDesc(kv_cache.data_ptr(), nb, bs, hkv, d, _DTYPES[kv_cache.dtype])
+    return _CacheDesc(kv_cache.data_ptr(), nb, bs, hkv, d, _DTYPES[kv_cache.dtype], float(kv_scale))
 
 
 def _need(t: torch.Tensor, name: str, dtype, device, dims: Optional[int] = None) -> None:
@@ -143,13 +151,14 @@ def _need(t: torch.Tensor, name: str, dtype, device, dims: Optional[int] = None)
 
 
 def pa_store_kv(key: torch.Tensor, value: torch.Tensor, kv_cache: torch.Tensor,
-                slot_mapping: torch.Tensor) -> None:
-    """Scatter ``key``/``value`` ``[T, Hkv, D]`` into ``kv_cache`` at ``slot_mapping`` (-1 skips)."""
+                slot_mapping: torch.Tensor, kv_scale: float = 1.0) -> None:
+    """Scatter ``key``/``value`` ``[T, Hkv, D]`` into ``kv_cache`` at ``slot_mapping`` (-1 skips);
+    an FP8 cache stores e4m3(x / kv_scale)."""
     lib = load()
-    desc = _desc(kv_cache)
+    desc = _desc(kv_cache, kv_scale)
     dev = kv_cache.device
-    _need(key, "key", kv_cache.dtype, dev, 3)
-    _need(value, "value", kv_cache.dtype, dev, 3)
+    _need(key, "key", _act(kv_cache), dev, 3)
+    _need(value, "value", _act(kv_cache), dev, 3)
     _need(slot_mapping, "slot_mapping", torch.int32, dev, 1)
     if key.shape != value.shape or key.shape[1:] != kv_cache.shape[3:] or key.shape[0] != slot_mapping.shape[0]:
         raise ValueError("key/value must be [num_tokens, num_kv_heads, head_size] matching slot_mapping and the cache")
@@ -180,7 +189,7 @@ def pa_prefill_varlen(query: torch.Tensor, kv_cache: torch.Tensor, block_table: 
     dev = kv_cache.device
     if num_kv_heads != kv_cache.shape[3]:
         raise ValueError(f"num_kv_heads {num_kv_heads} != cache's {kv_cache.shape[3]}")
-    _need(query, "query", kv_cache.dtype, dev, 3)
+    _need(query, "query", _act(kv_cache), dev, 3)
     _need(block_table, "block_table", torch.int32, dev, 2)
     _need(cu_seqlens_q, "cu_seqlens_q", torch.int32, dev, 1)
     _need(cu_seqlens_k, "cu_seqlens_k", torch.int32, dev, 1)
@@ -192,7 +201,7 @@ def pa_prefill_varlen(query: torch.Tensor, kv_cache: torch.Tensor, block_table: 
     if out is None:
         out = torch.empty_like(query)
     else:
-        _need(out, "out", kv_cache.dtype, dev, 3)
+        _need(out, "out", _act(kv_cache), dev, 3)
         if out.shape != query.shape:
             raise ValueError("out must match query's shape")
     _check(lib.pa_prefill_varlen(ctypes.byref(desc), _ptr(out), _ptr(query), _ptr(block_table),
@@ -222,18 +231,19 @@ def pa_decode(query: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Te
               seq_lens: torch.Tensor, max_seq_len: int, scale: float, num_kv_heads: int,
               sliding_window: int = 0, out: Optional[torch.Tensor] = None,
               workspace: Optional[torch.Tensor] = None, partition_size: int = 0,
-              alibi_slopes: Optional[torch.Tensor] = None) -> torch.Tensor:
+              alibi_slopes: Optional[torch.Tensor] = None, kv_scale: float = 1.0) -> torch.Tensor:
     """One query per sequence (``query [B, H, D]``) over its ``seq_lens[s]`` cached keys.
 
     ``workspace`` is a device byte buffer of at least ``pa_decode_workspace_size(...)``
-    bytes; when None one is allocated through torch for this call.
+    bytes; when None one is allocated through torch for this call.  ``kv_scale``: the scale
+    of an FP8 cache (ignored otherwise).
     """
     lib = load()
-    desc = _desc(kv_cache)
+    desc = _desc(kv_cache, kv_scale)
     dev = kv_cache.device
     if num_kv_heads != kv_cache.shape[3]:
         raise ValueError(f"num_kv_heads {num_kv_heads} != cache's {kv_cache.shape[3]}")
-    _need(query, "query", kv_cache.dtype, dev, 3)
+    _need(query, "query", _act(kv_cache), dev, 3)
     _need(block_table, "block_table", torch.int32, dev, 2)
     _need(seq_lens, "seq_lens", torch.int32, dev, 1)
     num_seqs = query.shape[0]
@@ -244,7 +254,7 @@ def pa_decode(query: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Te
     if out is None:
         out = torch.empty_like(query)
     else:
-        _need(out, "out", kv_cache.dtype, dev, 3)
+        _need(out, "out", _act(kv_cache), dev, 3)
         if out.shape != query.shape:
             raise ValueError("out must match query's shape")
     need = pa_decode_workspace_size(kv_cache, num_seqs, query.shape[1], int(max_seq_len),
@@ -277,16 +287,17 @@ def pa_cascade_decode_workspace_size(kv_cache: torch.Tensor, num_seqs: int, num_
 def pa_cascade_decode(query: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
                       seq_lens: torch.Tensor, max_seq_len: int, scale: float, num_kv_heads: int,
                       common_prefix_len: int, out: Optional[torch.Tensor] = None,
-                      workspace: Optional[torch.Tensor] = None, partition_size: int = 0) -> torch.Tensor:
+                      workspace: Optional[torch.Tensor] = None, partition_size: int = 0,
+                      kv_scale: float = 1.0) -> torch.Tensor:
     """Decode of a batch whose block-table rows all start with the same
     ``common_prefix_len / block_size`` physical blocks: the shared prefix is attended once
     for every query, then each sequence's own keys (arguments otherwise as ``pa_decode``)."""
     lib = load()
-    desc = _desc(kv_cache)
+    desc = _desc(kv_cache, kv_scale)
     dev = kv_cache.device
     if num_kv_heads != kv_cache.shape[3]:
         raise ValueError(f"num_kv_heads {num_kv_heads} != cache's {kv_cache.shape[3]}")
-    _need(query, "query", kv_cache.dtype, dev, 3)
+    _need(query, "query", _act(kv_cache), dev, 3)
     _need(block_table, "block_table", torch.int32, dev, 2)
     _need(seq_lens, "seq_lens", torch.int32, dev, 1)
     num_seqs = query.shape[0]
@@ -297,7 +308,7 @@ def pa_cascade_decode(query: torch.Tensor, kv_cache: torch.Tensor, block_table: 
     if out is None:
         out = torch.empty_like(query)
     else:
-        _need(out, "out", kv_cache.dtype, dev, 3)
+        _need(out, "out", _act(kv_cache), dev, 3)
         if out.shape != query.shape:
             raise ValueError("out must match query's shape")
     need = pa_cascade_decode_workspace_size(kv_cache, num_seqs, query.shape[1], int(max_seq_len),
@@ -319,8 +330,8 @@ def pa_cascade_decode(query: torch.Tensor, kv_cache: torch.Tensor, block_table: 
 def _new_rows(key: torch.Tensor, value: torch.Tensor, slot_mapping: torch.Tensor, kv_cache: torch.Tensor,
               rows: int) -> None:
     dev = kv_cache.device
-    _need(key, "key", kv_cache.dtype, dev, 3)
-    _need(value, "value", kv_cache.dtype, dev, 3)
+    _need(key, "key", _act(kv_cache), dev, 3)
+    _need(value, "value", _act(kv_cache), dev, 3)
     _need(slot_mapping, "slot_mapping", torch.int32, dev, 1)
     want = (rows, kv_cache.shape[3], kv_cache.shape[4])
     if tuple(key.shape) != want or tuple(value.shape) != want or slot_mapping.shape[0] != rows:
@@ -341,7 +352,7 @@ def pa_prefill_varlen_with_store(query: torch.Tensor, key: torch.Tensor, value: 
     dev = kv_cache.device
     if num_kv_heads != kv_cache.shape[3]:
         raise ValueError(f"num_kv_heads {num_kv_heads} != cache's {kv_cache.shape[3]}")
-    _need(query, "query", kv_cache.dtype, dev, 3)
+    _need(query, "query", _act(kv_cache), dev, 3)
     _need(block_table, "block_table", torch.int32, dev, 2)
     _need(cu_seqlens_q, "cu_seqlens_q", torch.int32, dev, 1)
     _need(cu_seqlens_k, "cu_seqlens_k", torch.int32, dev, 1)
@@ -354,7 +365,7 @@ def pa_prefill_varlen_with_store(query: torch.Tensor, key: torch.Tensor, value: 
     if out is None:
         out = torch.empty_like(query)
     else:
-        _need(out, "out", kv_cache.dtype, dev, 3)
+        _need(out, "out", _act(kv_cache), dev, 3)
         if out.shape != query.shape:
             raise ValueError("out must match query's shape")
     _check(lib.pa_prefill_varlen_with_store(ctypes.byref(desc), _ptr(out), _ptr(query), _ptr(key), _ptr(value),
@@ -372,15 +383,15 @@ def pa_decode_with_store(query: torch.Tensor, key: torch.Tensor, value: torch.Te
                          seq_lens: torch.Tensor, max_seq_len: int, scale: float, num_kv_heads: int,
                          sliding_window: int = 0, out: Optional[torch.Tensor] = None,
                          workspace: Optional[torch.Tensor] = None, partition_size: int = 0,
-                         alibi_slopes: Optional[torch.Tensor] = None) -> torch.Tensor:
+                         alibi_slopes: Optional[torch.Tensor] = None, kv_scale: float = 1.0) -> torch.Tensor:
     """Store each sequence's new token (``key``/``value [B, Hkv, D]`` at ``slot_mapping``) and
     decode ``query [B, H, D]`` over the ``seq_lens[s]`` keys that include it, in one call."""
     lib = load()
-    desc = _desc(kv_cache)
+    desc = _desc(kv_cache, kv_scale)
     dev = kv_cache.device
     if num_kv_heads != kv_cache.shape[3]:
         raise ValueError(f"num_kv_heads {num_kv_heads} != cache's {kv_cache.shape[3]}")
-    _need(query, "query", kv_cache.dtype, dev, 3)
+    _need(query, "query", _act(kv_cache), dev, 3)
     _need(block_table, "block_table", torch.int32, dev, 2)
     _need(seq_lens, "seq_lens", torch.int32, dev, 1)
     num_seqs = query.shape[0]
@@ -392,7 +403,7 @@ def pa_decode_with_store(query: torch.Tensor, key: torch.Tensor, value: torch.Te
     if out is None:
         out = torch.empty_like(query)
     else:
-        _need(out, "out", kv_cache.dtype, dev, 3)
+        _need(out, "out", _act(kv_cache), dev, 3)
         if out.shape != query.shape:
             raise ValueError("out must match query's shape")
     need = pa_decode_workspace_size(kv_cache, num_seqs, query.shape[1], int(max_seq_len),

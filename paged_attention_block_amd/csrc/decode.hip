@@ -37,8 +37,41 @@ __device__ inline uint32_t pack_bf16(float lo, float hi) { return pack_bf16x2(lo
 template <int D> struct VRow;
 template <> struct VRow<128> { typedef u32x4 T; };
 template <> struct VRow<64> { typedef u32x2 T; };
+// the same V piece in an FP8 cache: DPL bytes
+template <int D> struct VRow8;
+template <> struct VRow8<128> { typedef u32x2 T; };
+template <> struct VRow8<64> { typedef uint32_t T; };
+
+// Two FP8 (E4M3) cache bytes -> two bf16, exactly (every E4M3 value is a bf16 value).
+__device__ inline uint32_t e4m3x2_lo(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.f, false));
+}
+__device__ inline uint32_t e4m3x2_hi(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.f, true));
+}
 
 }  // namespace
+
+// Register types of one 32-key step as loaded: bf16 rows, or FP8 rows at half the bytes
+// (widened to bf16 right before the step's MFMAs).  K: k[2][D/32], V: v[8].
+template <int D, bool FP8> struct StepT;
+template <int D> struct StepT<D, false> {
+    typedef u32x4 K;
+    typedef typename VRow<D>::T V;
+};
+template <int D> struct StepT<D, true> {
+    typedef u32x2 K;
+    typedef typename VRow8<D>::T V;
+};
+
+// Per-lane byte offsets from a 16-key group's first row: K rows (key col, dims 8*grp of each
+// 32-dim slice), V rows (key 4*grp + j%4, dims DPL*col).
+template <int D, bool FP8>
+__device__ inline void lane_offsets(int col, int grp, uint32_t row_bytes, uint32_t& k_off, uint32_t& v_off) {
+    constexpr int ELT = FP8 ? 1 : 2;
+    k_off = (uint32_t)col * row_bytes + (uint32_t)(8 * ELT) * grp;
+    v_off = (uint32_t)(4 * grp) * row_bytes + (uint32_t)(ELT * (D / 16)) * col;
+}
 
 // Loads of the 32-key step at k0 into registers: K rows (2 groups of 16 keys x KS slices,
 // MFMA A-operand layout) and the V rows one lane needs for the PV MFMAs (8 keys x DPL
@@ -46,14 +79,15 @@ template <> struct VRow<64> { typedef u32x2 T; };
 // 16-aligned); a group with no live key is never looked up and its lanes read the other
 // group's rows instead, so every load is in bounds and unconditional.  Keys outside
 // [kb, ke) are masked after the load.
-template <int D>
+template <int D, bool FP8>
 __device__ __forceinline__ void load_step(int k0, int kb, int ke, const int32_t* __restrict__ table,
                                           int shift, int BS, int64_t row_elems, int g,
                                           const char* __restrict__ kplane,
                                           const char* __restrict__ vplane, uint32_t k_off,
                                           uint32_t v_off, uint32_t row_bytes,
-                                          u32x4 (&kr)[2][D / 32], typename VRow<D>::T (&vr)[8]) {
-    typedef typename VRow<D>::T VT;
+                                          typename StepT<D, FP8>::K (&kr)[2][D / 32],
+                                          typename StepT<D, FP8>::V (&vr)[8]) {
+    constexpr int ELT = FP8 ? 1 : 2;
     // wave-uniform byte offset of (first key of each 16-key group, KV head g) in a plane
     int64_t gb[2];
     bool gv[2];
@@ -62,7 +96,7 @@ __device__ __forceinline__ void load_step(int k0, int kb, int ke, const int32_t*
         const int j0 = k0 + 16 * ga;
         gv[ga] = (j0 < ke) && (j0 + 16 > kb);
         const int blk = gv[ga] ? table[j0 >> shift] : 0;
-        gb[ga] = (((int64_t)blk * BS + (j0 & (BS - 1))) * row_elems + (int64_t)g * D) * 2;
+        gb[ga] = (((int64_t)blk * BS + (j0 & (BS - 1))) * row_elems + (int64_t)g * D) * ELT;
     }
     if (!gv[0]) gb[0] = gb[1];
     if (!gv[1]) gb[1] = gb[0];
@@ -70,12 +104,33 @@ __device__ __forceinline__ void load_step(int k0, int kb, int ke, const int32_t*
     for (int ga = 0; ga < 2; ++ga) {
         const char* base = kplane + gb[ga];
 #pragma unroll
-        for (int t = 0; t < D / 32; ++t) kr[ga][t] = *(const u32x4*)(base + k_off + 64 * t);
+        for (int t = 0; t < D / 32; ++t) {
+            kr[ga][t] = *(const typename StepT<D, FP8>::K*)(base + k_off + 16 * (FP8 ? 2 : 4) * t);
+        }
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         const char* base = vplane + gb[j >> 2] + (int64_t)(j & 3) * row_bytes;
-        vr[j] = *(const VT*)(base + v_off);
+        vr[j] = *(const typename StepT<D, FP8>::V*)(base + v_off);
+    }
+}
+
+// FP8 step registers widened to the bf16 layout the MFMAs take.
+template <int D>
+__device__ __forceinline__ void widen_step(const u32x2 (&k8)[2][D / 32], const typename VRow8<D>::T (&v8)[8],
+                                           u32x4 (&kr)[2][D / 32], typename VRow<D>::T (&vr)[8]) {
+#pragma unroll
+    for (int ga = 0; ga < 2; ++ga)
+#pragma unroll
+        for (int t = 0; t < D / 32; ++t)
+            kr[ga][t] = u32x4{e4m3x2_lo(k8[ga][t][0]), e4m3x2_hi(k8[ga][t][0]), e4m3x2_lo(k8[ga][t][1]),
+                              e4m3x2_hi(k8[ga][t][1])};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        if constexpr (D == 128)
+            vr[j] = u32x4{e4m3x2_lo(v8[j][0]), e4m3x2_hi(v8[j][0]), e4m3x2_lo(v8[j][1]), e4m3x2_hi(v8[j][1])};
+        else
+            vr[j] = u32x2{e4m3x2_lo(v8[j]), e4m3x2_hi(v8[j])};
     }
 }
 
@@ -83,7 +138,7 @@ __device__ __forceinline__ void load_step(int k0, int kb, int ke, const int32_t*
 // With ALiBi, sl2 = this lane's head slope in log2 units and pos the query's position: the
 // score of key j gets sl2 * (j - pos) added after the scale.
 template <int D, bool ALIBI>
-__device__ __forceinline__ void compute_step(int k0, int kb, int ke, int grp, float c_log2,
+__device__ __forceinline__ void compute_core(int k0, int kb, int ke, int grp, float c_log2,
                                              float sl2, int pos,
                                              const bf16x8 (&qf)[D / 32], u32x4 (&kr)[2][D / 32],
                                              typename VRow<D>::T (&vr)[8], f32x4 (&oacc)[D / 16],
@@ -154,6 +209,23 @@ __device__ __forceinline__ void compute_step(int k0, int kb, int ke, int grp, fl
         w[3] = __builtin_amdgcn_perm(vr[7][t >> 1], vr[6][t >> 1], sel);
         oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w), pb, oacc[t],
                                                           0, 0, 0);
+    }
+}
+
+// One 32-key step from its loaded registers (FP8 rows widened first).
+template <int D, bool ALIBI, bool FP8>
+__device__ __forceinline__ void compute_step(int k0, int kb, int ke, int grp, float c_log2, float sl2, int pos,
+                                             const bf16x8 (&qf)[D / 32],
+                                             typename StepT<D, FP8>::K (&kr)[2][D / 32],
+                                             typename StepT<D, FP8>::V (&vr)[8],
+                                             f32x4 (&oacc)[D / 16], float& m_run, float& l_run) {
+    if constexpr (FP8) {
+        u32x4 kw[2][D / 32];
+        typename VRow<D>::T vw[8];
+        widen_step<D>(kr, vr, kw, vw);
+        compute_core<D, ALIBI>(k0, kb, ke, grp, c_log2, sl2, pos, qf, kw, vw, oacc, m_run, l_run);
+    } else {
+        compute_core<D, ALIBI>(k0, kb, ke, grp, c_log2, sl2, pos, qf, kr, vr, oacc, m_run, l_run);
     }
 }
 
@@ -240,11 +312,10 @@ __device__ __forceinline__ void fold_prefix(const DecodeArgs& a, int s, int head
 // CASCADE: shared-prefix decode.  Every sequence's steps then start at key_start, the first
 // piece of a sequence folds the prefix's state into its own, and a sequence with no own key
 // writes the prefix's result.
-template <int D, bool ALIBI, bool CASCADE>
+template <int D, bool ALIBI, bool CASCADE, bool FP8>
 __global__ __launch_bounds__(512) void decode_bf16_kernel(const DecodeArgs a) {
     constexpr int KS = D / 32;   // k-slices of q.K^T
     constexpr int DPL = D / 16;  // dims per lane chunk of a V row = PV MFMAs per step
-    typedef typename VRow<D>::T VT;
 
     // one workgroup per (chunk of the step list, group of up to 8 KV heads); wave w serves
     // KV head 8*blockIdx.y + w, so the waves of a workgroup stream the same physical blocks
@@ -272,15 +343,14 @@ __global__ __launch_bounds__(512) void decode_bf16_kernel(const DecodeArgs a) {
     const int shift = a.c.block_shift;
     const int Hkv = a.c.num_kv_heads;
     const char* __restrict__ kplane = (const char*)a.c.kv;
-    const char* __restrict__ vplane = kplane + a.c.plane_elems * 2;
-    const float c_log2 = a.scale * 1.4426950408889634f;
+    const char* __restrict__ vplane = kplane + a.c.plane_elems * (FP8 ? 1 : 2);
+    // an FP8 cache holds K / kv_scale: the scale joins the softmax scale (and V's, the output's)
+    const float c_log2 = a.scale * (FP8 ? a.c.kv_scale : 1.f) * 1.4426950408889634f;
     const float sl2 = ALIBI && head_ok ? a.alibi[head] * 1.4426950408889634f : 0.f;  // ALiBi slope, log2 units
-    // per-lane byte offsets from a group's first row: K rows (key col, dims 8*grp of each
-    // 32-dim slice), V rows (key 4*grp + j%4, dims DPL*col)
     const int64_t row_elems = (int64_t)Hkv * D;
-    const uint32_t row_bytes = (uint32_t)(row_elems * 2);
-    const uint32_t k_off = (uint32_t)col * row_bytes + 16u * grp;
-    const uint32_t v_off = (uint32_t)(4 * grp) * row_bytes + 2u * DPL * col;
+    const uint32_t row_bytes = (uint32_t)(row_elems * (FP8 ? 1 : 2));
+    uint32_t k_off, v_off;
+    lane_offsets<D, FP8>(col, grp, row_bytes, k_off, v_off);
 
     int carry = 0;  // steps of the sequences before chunk c of 64
     for (int c = 0; c < a.num_seqs; c += 64) {
@@ -313,7 +383,7 @@ __global__ __launch_bounds__(512) void decode_bf16_kernel(const DecodeArgs a) {
                     float m_run = -INFINITY, l_run = 0.f;
                     fold_prefix<D>(a, s, head_ok ? head : g * G, grp, oacc, m_run, l_run);
                     const float l_tot = group4_sum(l_run);
-                    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+                    const float inv = l_tot > 0.f ? (FP8 ? a.c.kv_scale : 1.f) / l_tot : 0.f;
                     if (head_ok) {
                         for (int r = 0; r < 4; ++r) {
                             const int d0 = DPL * (4 * grp + r);
@@ -360,20 +430,20 @@ __global__ __launch_bounds__(512) void decode_bf16_kernel(const DecodeArgs a) {
             // waits stay exact.  A workgroup barrier per two steps keeps the 8 waves, which
             // read adjacent 256-byte pieces of the same 2 KB token rows, close together in
             // the key walk (measured: 3% more bandwidth than free-running waves).
-            u32x4 kA[2][KS], kB[2][KS];
-            VT vA[8], vB[8];
+            typename StepT<D, FP8>::K kA[2][KS], kB[2][KS];
+            typename StepT<D, FP8>::V vA[8], vB[8];
             int k0 = step_begin;
-            load_step<D>(k0, kb, ke, table, shift, BS, row_elems, g, kplane, vplane, k_off, v_off, row_bytes, kA, vA);
+            load_step<D, FP8>(k0, kb, ke, table, shift, BS, row_elems, g, kplane, vplane, k_off, v_off, row_bytes, kA, vA);
             while (true) {
                 __syncthreads();
                 const int n1 = k0 + 32 < ke ? k0 + 32 : k0;
-                load_step<D>(n1, kb, ke, table, shift, BS, row_elems, g, kplane, vplane, k_off, v_off, row_bytes, kB, vB);
-                compute_step<D, ALIBI>(k0, kb, ke, grp, c_log2, sl2, n - 1, qf, kA, vA, oacc, m_run, l_run);
+                load_step<D, FP8>(n1, kb, ke, table, shift, BS, row_elems, g, kplane, vplane, k_off, v_off, row_bytes, kB, vB);
+                compute_step<D, ALIBI, FP8>(k0, kb, ke, grp, c_log2, sl2, n - 1, qf, kA, vA, oacc, m_run, l_run);
                 k0 += 32;
                 if (k0 >= ke) break;
                 const int n2 = k0 + 32 < ke ? k0 + 32 : k0;
-                load_step<D>(n2, kb, ke, table, shift, BS, row_elems, g, kplane, vplane, k_off, v_off, row_bytes, kA, vA);
-                compute_step<D, ALIBI>(k0, kb, ke, grp, c_log2, sl2, n - 1, qf, kB, vB, oacc, m_run, l_run);
+                load_step<D, FP8>(n2, kb, ke, table, shift, BS, row_elems, g, kplane, vplane, k_off, v_off, row_bytes, kA, vA);
+                compute_step<D, ALIBI, FP8>(k0, kb, ke, grp, c_log2, sl2, n - 1, qf, kB, vB, oacc, m_run, l_run);
                 k0 += 32;
                 if (k0 >= ke) break;
             }
@@ -384,7 +454,7 @@ __global__ __launch_bounds__(512) void decode_bf16_kernel(const DecodeArgs a) {
             const float l_tot = group4_sum(l_run);
             if (head_ok) {
                 if (ls == 0 && le == steps) {  // the whole sequence: normalised output
-                    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+                    const float inv = l_tot > 0.f ? (FP8 ? a.c.kv_scale : 1.f) / l_tot : 0.f;
                     for (int r = 0; r < 4; ++r) {
                         const int d0 = DPL * (4 * grp + r);
                         uint32_t wv[DPL / 2];
@@ -419,11 +489,10 @@ __global__ __launch_bounds__(512) void decode_bf16_kernel(const DecodeArgs a) {
 // wave 0 writes the chunk's state.  Workgroup ids are dealt to the 8 XCDs in turn; they are
 // mapped so that all row groups of one (g, c) run on the same XCD, where the chunk's K/V is
 // read from HBM once and from that XCD's L2 by the other row groups.
-template <int D>
+template <int D, bool FP8>
 __global__ __launch_bounds__(512) void cascade_prefix_kernel(const DecodeArgs a, int row_groups) {
     constexpr int KS = D / 32;
     constexpr int DPL = D / 16;
-    typedef typename VRow<D>::T VT;
     __shared__ float red[4][4 * DPL + 2][64];
     const int lane = threadIdx.x & 63;
     const int col = lane & 15;
@@ -454,12 +523,13 @@ __global__ __launch_bounds__(512) void cascade_prefix_kernel(const DecodeArgs a,
     const int BS = a.c.block_size;
     const int shift = a.c.block_shift;
     const char* __restrict__ kplane = (const char*)a.c.kv;
-    const char* __restrict__ vplane = kplane + a.c.plane_elems * 2;
-    const float c_log2 = a.scale * 1.4426950408889634f;
+    const char* __restrict__ vplane = kplane + a.c.plane_elems * (FP8 ? 1 : 2);
+    // an FP8 cache holds K / kv_scale: the scale joins the softmax scale (and V's, the output's)
+    const float c_log2 = a.scale * (FP8 ? a.c.kv_scale : 1.f) * 1.4426950408889634f;
     const int64_t row_elems = (int64_t)Hkv * D;
-    const uint32_t row_bytes = (uint32_t)(row_elems * 2);
-    const uint32_t k_off = (uint32_t)col * row_bytes + 16u * grp;
-    const uint32_t v_off = (uint32_t)(4 * grp) * row_bytes + 2u * DPL * col;
+    const uint32_t row_bytes = (uint32_t)(row_elems * (FP8 ? 1 : 2));
+    uint32_t k_off, v_off;
+    lane_offsets<D, FP8>(col, grp, row_bytes, k_off, v_off);
 
     bf16x8 qf[KS];
     {
@@ -477,19 +547,19 @@ __global__ __launch_bounds__(512) void cascade_prefix_kernel(const DecodeArgs a,
     float l_run = 0.f;
     if (st1 > st0) {
         // the waves read different keys, so they run free (no barrier in the walk)
-        u32x4 kA[2][KS], kB[2][KS];
-        VT vA[8], vB[8];
+        typename StepT<D, FP8>::K kA[2][KS], kB[2][KS];
+            typename StepT<D, FP8>::V vA[8], vB[8];
         int k0 = kb;
-        load_step<D>(k0, kb, ke, a.table, shift, BS, row_elems, g, kplane, vplane, k_off, v_off, row_bytes, kA, vA);
+        load_step<D, FP8>(k0, kb, ke, a.table, shift, BS, row_elems, g, kplane, vplane, k_off, v_off, row_bytes, kA, vA);
         while (true) {
             const int n1 = k0 + 32 < ke ? k0 + 32 : k0;
-            load_step<D>(n1, kb, ke, a.table, shift, BS, row_elems, g, kplane, vplane, k_off, v_off, row_bytes, kB, vB);
-            compute_step<D, false>(k0, kb, ke, grp, c_log2, 0.f, 0, qf, kA, vA, oacc, m_run, l_run);
+            load_step<D, FP8>(n1, kb, ke, a.table, shift, BS, row_elems, g, kplane, vplane, k_off, v_off, row_bytes, kB, vB);
+            compute_step<D, false, FP8>(k0, kb, ke, grp, c_log2, 0.f, 0, qf, kA, vA, oacc, m_run, l_run);
             k0 += 32;
             if (k0 >= ke) break;
             const int n2 = k0 + 32 < ke ? k0 + 32 : k0;
-            load_step<D>(n2, kb, ke, a.table, shift, BS, row_elems, g, kplane, vplane, k_off, v_off, row_bytes, kA, vA);
-            compute_step<D, false>(k0, kb, ke, grp, c_log2, 0.f, 0, qf, kB, vB, oacc, m_run, l_run);
+            load_step<D, FP8>(n2, kb, ke, a.table, shift, BS, row_elems, g, kplane, vplane, k_off, v_off, row_bytes, kA, vA);
+            compute_step<D, false, FP8>(k0, kb, ke, grp, c_log2, 0.f, 0, qf, kB, vB, oacc, m_run, l_run);
             k0 += 32;
             if (k0 >= ke) break;
         }
@@ -626,7 +696,7 @@ __global__ __launch_bounds__(64 * MW) void decode_merge_kernel(const DecodeArgs 
         }
     }
     if (!h_ok) return;
-    const float inv = Lt > 0.f ? 1.f / Lt : 0.f;
+    const float inv = Lt > 0.f ? a.c.kv_scale / Lt : 0.f;  // an FP8 cache holds V / kv_scale
     uint32_t wv[DL / 2];
 #pragma unroll
     for (int t = 0; t < DL / 2; ++t) wv[t] = pack_bf16(acc[2 * t] * inv, acc[2 * t + 1] * inv);
@@ -654,8 +724,8 @@ int decode_resident_slots(int head_size, int num_kv_heads) {
         hipError_t e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
         if (e == hipSuccess)
             e = head_size == 128
-                    ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_bf16_kernel<128, false, false>, 64 * waves, 0)
-                    : hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_bf16_kernel<64, false, false>, 64 * waves, 0);
+                    ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_bf16_kernel<128, false, false, false>, 64 * waves, 0)
+                    : hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_bf16_kernel<64, false, false, false>, 64 * waves, 0);
         if (e != hipSuccess || ncu <= 0 || nb <= 0) {
             (void)hipGetLastError();
             return 256;
@@ -667,15 +737,15 @@ int decode_resident_slots(int head_size, int num_kv_heads) {
 }
 
 // Partition kernel (+ merge kernel when the batch is cut into more than one chunk).
-template <bool ALIBI, bool CASCADE>
+template <bool ALIBI, bool CASCADE, bool FP8>
 static void launch_partition_merge(const DecodeArgs& a, hipStream_t st) {
     const int hkv = a.c.num_kv_heads;
     const dim3 grid(a.nw, (hkv + 7) / 8);
     const dim3 block(64 * (hkv < 8 ? hkv : 8));
     if (a.c.head_size == 128)
-        hipLaunchKernelGGL((decode_bf16_kernel<128, ALIBI, CASCADE>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((decode_bf16_kernel<128, ALIBI, CASCADE, FP8>), grid, block, 0, st, a);
     else
-        hipLaunchKernelGGL((decode_bf16_kernel<64, ALIBI, CASCADE>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((decode_bf16_kernel<64, ALIBI, CASCADE, FP8>), grid, block, 0, st, a);
     if (a.nw > 1) {
         const dim3 mg(a.num_seqs, (a.num_heads + 3) / 4);
         const bool many = a.nw > 8 * a.num_seqs;  // more than ~8 pieces per sequence
@@ -690,8 +760,14 @@ static void launch_partition_merge(const DecodeArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t st) {
-    if (a.alibi) launch_partition_merge<true, false>(a, st);
-    else launch_partition_merge<false, false>(a, st);
+    const bool fp8 = a.c.dtype == 2;
+    if (a.alibi) {
+        if (fp8) launch_partition_merge<true, false, true>(a, st);
+        else launch_partition_merge<true, false, false>(a, st);
+    } else {
+        if (fp8) launch_partition_merge<false, false, true>(a, st);
+        else launch_partition_merge<false, false, false>(a, st);
+    }
     return hipGetLastError();
 }
 
@@ -699,11 +775,20 @@ hipError_t launch_cascade_decode_bf16(const DecodeArgs& a, hipStream_t st) {
     const int row_groups = (a.num_seqs * a.group + 15) / 16;
     const int units = a.c.num_kv_heads * a.prefix_chunks;
     const dim3 grid((unsigned)(8LL * row_groups * ((units + 7) / 8)));
-    if (a.c.head_size == 128)
-        hipLaunchKernelGGL((cascade_prefix_kernel<128>), grid, dim3(512), 0, st, a, row_groups);
-    else
-        hipLaunchKernelGGL((cascade_prefix_kernel<64>), grid, dim3(512), 0, st, a, row_groups);
-    launch_partition_merge<false, true>(a, st);
+    const bool fp8 = a.c.dtype == 2;
+    if (fp8) {
+        if (a.c.head_size == 128)
+            hipLaunchKernelGGL((cascade_prefix_kernel<128, true>), grid, dim3(512), 0, st, a, row_groups);
+        else
+            hipLaunchKernelGGL((cascade_prefix_kernel<64, true>), grid, dim3(512), 0, st, a, row_groups);
+        launch_partition_merge<false, true, true>(a, st);
+    } else {
+        if (a.c.head_size == 128)
+            hipLaunchKernelGGL((cascade_prefix_kernel<128, false>), grid, dim3(512), 0, st, a, row_groups);
+        else
+            hipLaunchKernelGGL((cascade_prefix_kernel<64, false>), grid, dim3(512), 0, st, a, row_groups);
+        launch_partition_merge<false, true, false>(a, st);
+    }
     return hipGetLastError();
 }
 

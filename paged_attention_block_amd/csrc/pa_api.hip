@@ -36,7 +36,10 @@ int check_cache(const pa_cache_desc* d, pa::CacheArgs* c) {
     if (!d->kv_cache) return fail(PA_ERR_INVALID_ARG, "kv_cache is NULL");
     if (d->num_blocks <= 0) return fail(PA_ERR_INVALID_ARG, "num_blocks must be > 0 (got %d)", d->num_blocks);
     if (d->num_kv_heads <= 0) return fail(PA_ERR_INVALID_ARG, "num_kv_heads must be > 0 (got %d)", d->num_kv_heads);
-    if (d->dtype != PA_F32 && d->dtype != PA_BF16) return fail(PA_ERR_UNSUPPORTED, "dtype %d not supported", d->dtype);
+    if (d->dtype != PA_F32 && d->dtype != PA_BF16 && d->dtype != PA_FP8_E4M3)
+        return fail(PA_ERR_UNSUPPORTED, "dtype %d not supported", d->dtype);
+    if (d->dtype == PA_FP8_E4M3 && !(d->kv_scale > 0.f && d->kv_scale <= 3.4e38f))
+        return fail(PA_ERR_INVALID_ARG, "kv_scale must be finite and > 0 for an FP8 cache (got %g)", (double)d->kv_scale);
     if (d->head_size != 64 && d->head_size != 128)
         return fail(PA_ERR_UNSUPPORTED, "head_size %d not supported (64 or 128)", d->head_size);
     if (!is_pow2(d->block_size) || d->block_size > 256)
@@ -52,6 +55,8 @@ int check_cache(const pa_cache_desc* d, pa::CacheArgs* c) {
     c->num_kv_heads = d->num_kv_heads;
     c->head_size = d->head_size;
     c->dtype = d->dtype;
+    c->kv_scale = d->dtype == PA_FP8_E4M3 ? d->kv_scale : 1.f;
+    c->kv_inv_scale = 1.f / c->kv_scale;
     c->plane_elems = (int64_t)d->num_blocks * d->block_size * d->num_kv_heads * d->head_size;
     return PA_OK;
 }
@@ -62,10 +67,10 @@ int check_heads(const pa::CacheArgs& c, int32_t num_heads) {
         return fail(PA_ERR_INVALID_ARG, "num_heads %d is not a multiple of num_kv_heads %d", num_heads,
                     c.num_kv_heads);
     const int group = num_heads / c.num_kv_heads;
-    if (c.dtype == PA_BF16 && group > 16)
+    if (c.dtype != PA_F32 && group > 16)
         return fail(PA_ERR_UNSUPPORTED, "bf16 decode supports up to 16 query heads per KV head (got %d)", group);
-    if (c.dtype == PA_BF16 && c.block_size < 16)
-        return fail(PA_ERR_UNSUPPORTED, "bf16 kernels need block_size >= 16 (got %d)", c.block_size);
+    if (c.dtype != PA_F32 && c.block_size < 16)
+        return fail(PA_ERR_UNSUPPORTED, "bf16 and fp8 kernels need block_size >= 16 (got %d)", c.block_size);
     if (num_heads > 65535) return fail(PA_ERR_INVALID_ARG, "num_heads too large");
     return PA_OK;
 }
@@ -138,7 +143,7 @@ struct DecodePlan {
 DecodePlan decode_plan(const pa_cache_desc* cache, int32_t num_seqs, int32_t num_heads, int32_t max_seq_len,
                        int32_t window, int32_t key_start, int32_t partition_size) {
     DecodePlan p = {{1, 1}, 0, 0, 0};
-    if (cache->dtype != PA_BF16) return p;
+    if (cache->dtype == PA_F32) return p;
     p.c = decode_chunks(num_seqs, cache->head_size, cache->num_kv_heads,
                         max_keys_of(max_seq_len, window > 0 ? window : 0, key_start), partition_size);
     if (p.c.nw > 1) p.chunk_bytes = (size_t)p.c.nw * 2 * num_heads * ((size_t)cache->head_size + 2) * sizeof(float);
@@ -204,6 +209,7 @@ static int prefill_args(const pa_cache_desc* cache, void* out, const void* query
     *empty = false;
     int st = check_cache(cache, &a.c);
     if (st) return st;
+    if (a.c.dtype == PA_FP8_E4M3) return fail(PA_ERR_UNSUPPORTED, "prefill over an FP8 cache is not supported");
     if ((st = check_heads(a.c, num_heads))) return st;
     if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs must be >= 0 (got %d)", num_seqs);
     if (max_seqlen_q < 0 || max_seqlen_k < 0) return fail(PA_ERR_INVALID_ARG, "max_seqlen_q/k must be >= 0");

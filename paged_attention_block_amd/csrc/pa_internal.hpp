@@ -62,8 +62,13 @@ struct CacheArgs {
     int32_t block_shift; // log2(block_size)
     int32_t num_kv_heads;
     int32_t head_size;
-    int32_t dtype;       // 0 f32, 1 bf16
+    int32_t dtype;       // 0 f32, 1 bf16, 2 fp8 e4m3 (q/k/v/out bf16)
+    float kv_scale;      // fp8: the cache holds value / kv_scale (1 otherwise)
+    float kv_inv_scale;  // fp8: fp32(1 / kv_scale), the store's multiplier
 };
+
+// Bytes per cache element.
+__host__ __device__ inline int cache_elt(int dtype) { return dtype == 0 ? 4 : (dtype == 1 ? 2 : 1); }
 
 struct StoreArgs {
     CacheArgs c;

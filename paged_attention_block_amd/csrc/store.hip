@@ -1,4 +1,5 @@
-// KV store scatter and block copies: bitwise moves of 16-byte chunks.
+// KV store scatter and block copies: bitwise moves of 16-byte chunks (and the quantizing
+// store of an FP8 cache).
 //
 // Store (MinivLLM API docs, "Attention", store_kvcache; vLLM learning book section 10 Q2):
 // the flat slot index equals the row index of the [NB*BS] token rows of a cache plane, so a
@@ -27,6 +28,39 @@ __global__ __launch_bounds__(256) void store_kernel(uint4* __restrict__ cache,
     }
 }
 
+// FP8 (E4M3) cache: a thread turns one 16-byte piece of a bf16 key or value row (8 elements)
+// into 8 cache bytes, e4m3(x * r) with r = fp32(1 / kv_scale): the product in fp32,
+// magnitudes above 448 saturated (NaN passes through), then v_cvt_pk_fp8_f32 (round to
+// nearest even) two elements at a time.
+__device__ inline float sat_e4m3(float x) { return fabsf(x) > 448.f ? copysignf(448.f, x) : x; }
+__device__ inline uint32_t e4m3x4(uint32_t lo, uint32_t hi, float r) {
+    // lo, hi: two bf16 pairs (element 2i in the low half)
+    const float a = __uint_as_float(lo << 16) * r, b = __uint_as_float(lo & 0xffff0000u) * r;
+    const float c = __uint_as_float(hi << 16) * r, d = __uint_as_float(hi & 0xffff0000u) * r;
+    uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sat_e4m3(a), sat_e4m3(b), 0, false);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sat_e4m3(c), sat_e4m3(d), (int)w, true);
+}
+
+__global__ __launch_bounds__(256) void store_fp8_kernel(u32x2* __restrict__ cache,
+                                                        const uint4* __restrict__ key,
+                                                        const uint4* __restrict__ value,
+                                                        const int32_t* __restrict__ slots,
+                                                        int32_t row_chunks, int64_t plane_chunks,
+                                                        float r) {
+    // row_chunks: 16-byte pieces of an input row = 8-byte pieces of a cache row
+    const int32_t t = blockIdx.x;
+    const int32_t slot = slots[t];
+    if (slot < 0) return;
+    const int64_t src = (int64_t)t * row_chunks;
+    const int64_t dst = (int64_t)slot * row_chunks;
+    for (int32_t c = threadIdx.x; c < 2 * row_chunks; c += blockDim.x) {
+        const bool is_v = c >= row_chunks;
+        const int32_t cc = is_v ? c - row_chunks : c;
+        const uint4 x = is_v ? value[src + cc] : key[src + cc];
+        cache[(is_v ? plane_chunks : 0) + dst + cc] = u32x2{e4m3x4(x.x, x.y, r), e4m3x4(x.z, x.w, r)};
+    }
+}
+
 // copy_blocks (vllm-npu 0.4.2 diff, backend copy_blocks): one workgroup per (pair, plane),
 // each moving the block's BS*Hkv*D elements as 16-byte chunks.
 __global__ __launch_bounds__(256) void copy_blocks_kernel(uint4* __restrict__ cache,
@@ -41,7 +75,17 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(uint4* __restrict__ ca
 }
 
 hipError_t launch_store(const StoreArgs& a, hipStream_t s) {
-    const int elt = a.c.dtype == 1 ? 2 : 4;
+    if (a.c.dtype == 2) {
+        const int32_t row_chunks = a.c.num_kv_heads * a.c.head_size / 8;
+        const int64_t plane_chunks = a.c.plane_elems / 8;
+        int threads = 2 * row_chunks;
+        threads = threads > 256 ? 256 : ((threads + 63) / 64) * 64;
+        hipLaunchKernelGGL(store_fp8_kernel, dim3(a.num_tokens), dim3(threads), 0, s, (u32x2*)a.c.kv,
+                           (const uint4*)a.key, (const uint4*)a.value, a.slots, row_chunks, plane_chunks,
+                           a.c.kv_inv_scale);
+        return hipGetLastError();
+    }
+    const int elt = cache_elt(a.c.dtype);
     const int32_t row_chunks = a.c.num_kv_heads * a.c.head_size * elt / 16;
     const int64_t plane_chunks = a.c.plane_elems * elt / 16;
     int threads = 2 * row_chunks;
@@ -53,7 +97,7 @@ hipError_t launch_store(const StoreArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_copy_blocks(const CopyArgs& a, hipStream_t s) {
-    const int elt = a.c.dtype == 1 ? 2 : 4;
+    const int elt = cache_elt(a.c.dtype);
     const int32_t block_chunks =
         (int32_t)((int64_t)a.c.block_size * a.c.num_kv_heads * a.c.head_size * elt / 16);
     const int64_t plane_chunks = a.c.plane_elems * elt / 16;

@@ -45,7 +45,7 @@ def assert_close(got: np.ndarray, ref: np.ndarray, dtype, what: str) -> float:
 def bits(t: torch.Tensor) -> np.ndarray:
     """Raw bits of a CPU tensor as an integer numpy array."""
     t = t.contiguous()
-    return (t.view(torch.int16) if t.element_size() == 2 else t.view(torch.int32)).numpy()
+    return t.view({1: torch.uint8, 2: torch.int16, 4: torch.int32}[t.element_size()]).numpy()
 
 
 def host_values(t: torch.Tensor) -> np.ndarray:
@@ -61,6 +61,7 @@ class GpuRun:
         self.dev = device
         self.cache = wl.kv_cache.to(device)
         self.alibi = None        # optional np.ndarray [num_heads] ALiBi slopes
+        self.kv_scale = 1.0      # the scale of an FP8 cache
 
     def _slopes(self):
         return None if self.alibi is None else torch.from_numpy(np.asarray(self.alibi, np.float32)).to(self.dev)
@@ -74,7 +75,8 @@ class GpuRun:
             pa.pa_copy_blocks(self.cache, self.i32(op.pairs))
             return None
         if isinstance(op, W.StoreOp):
-            pa.pa_store_kv(op.key.to(self.dev), op.value.to(self.dev), self.cache, self.i32(op.slot_mapping))
+            pa.pa_store_kv(op.key.to(self.dev), op.value.to(self.dev), self.cache, self.i32(op.slot_mapping),
+                           kv_scale=self.kv_scale)
             return None
         if isinstance(op, W.PrefillOp):
             return pa.pa_prefill_varlen(op.query.to(self.dev), self.cache, self.i32(op.block_table),
@@ -85,7 +87,7 @@ class GpuRun:
             return pa.pa_decode(op.query.to(self.dev), self.cache, self.i32(op.block_table),
                                 self.i32(op.seq_lens), op.max_seq_len, wl.scale, wl.num_kv_heads,
                                 wl.sliding_window, partition_size=partition_size,
-                                alibi_slopes=self._slopes())
+                                alibi_slopes=self._slopes(), kv_scale=self.kv_scale)
         raise TypeError(op)
 
     def run_with_store(self, store, op, partition_size: int = 0):
@@ -102,7 +104,7 @@ class GpuRun:
         return pa.pa_decode_with_store(op.query.to(d), k, v, sl, self.cache, self.i32(op.block_table),
                                        self.i32(op.seq_lens), op.max_seq_len, wl.scale, wl.num_kv_heads,
                                        wl.sliding_window, partition_size=partition_size,
-                                       alibi_slopes=self._slopes())
+                                       alibi_slopes=self._slopes(), kv_scale=self.kv_scale)
 
 
 def oracle_attention(wl: W.Workload, op, cache_vals: np.ndarray, picks=None, alibi=None) -> np.ndarray:

@@ -28,8 +28,8 @@ def lib():
     return pa.load()
 
 
-def desc(nb=64, bs=16, hkv=2, d=128, dtype=1, ptr=FAKE):
-    return ctypes.byref(pa._CacheDesc(ptr, nb, bs, hkv, d, dtype))
+def desc(nb=64, bs=16, hkv=2, d=128, dtype=1, ptr=FAKE, kv_scale=1.0):
+    return ctypes.byref(pa._CacheDesc(ptr, nb, bs, hkv, d, dtype, kv_scale))
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -170,3 +170,25 @@ def test_cascade_decode_checks_and_workspace(lib):
     a = list(args(1024)); a[12] = FAKE + 8
     assert lib.pa_cascade_decode(*a) == 1 and b"aligned" in lib.pa_last_error()
     assert lib.pa_cascade_decode(d, None, None, None, 1, None, 0, 0, 32, 0.1, 0, 0, None, 0, None) == 0
+
+
+def test_fp8_cache_checks(lib):
+    # the descriptor gained kv_scale in what was padding: same size as before
+    assert ctypes.sizeof(pa._CacheDesc) == 32
+    for bad in (0.0, -1.0, float("nan"), float("inf")):
+        assert lib.pa_store_kv(desc(dtype=2, kv_scale=bad), FAKE, FAKE, FAKE, 4, None) == 1
+        assert b"kv_scale" in lib.pa_last_error()
+    d = desc(dtype=2, kv_scale=0.5)
+    assert lib.pa_store_kv(d, FAKE, FAKE, FAKE, 0, None) == 0
+    # prefill over an FP8 cache is refused, with or without the fused store
+    assert lib.pa_prefill_varlen(d, FAKE, FAKE, FAKE, 4, FAKE, FAKE, 2, 10, 60, 8, 0.1, 0, None, None) == 2
+    assert b"FP8" in lib.pa_last_error()
+    args = (d, FAKE, FAKE, FAKE, FAKE, FAKE, 40, FAKE, 4, FAKE, FAKE, 2, 20, 30, 8, 0.1, 0, None, None)
+    assert lib.pa_prefill_varlen_with_store(*args) == 2
+    # decode plans the same split as for bf16
+    d8 = desc(nb=1000, bs=16, hkv=8, d=128, dtype=2, kv_scale=0.5)
+    b8 = desc(nb=1000, bs=16, hkv=8, d=128, dtype=1)
+    assert lib.pa_decode_workspace_size(d8, 64, 32, 4097, 0, 128) == lib.pa_decode_workspace_size(b8, 64, 32, 4097, 0, 128) > 0
+    assert lib.pa_cascade_decode_workspace_size(d8, 64, 32, 4097, 1024, 0) == lib.pa_cascade_decode_workspace_size(b8, 64, 32, 4097, 1024, 0)
+    # bf16-kernel limits apply: block_size >= 16
+    assert lib.pa_decode(desc(bs=8, dtype=2, kv_scale=1.0), FAKE, FAKE, FAKE, 4, FAKE, 2, 30, 4, 0.1, 0, None, 0, FAKE, 1 << 20, None) == 2

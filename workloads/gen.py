@@ -128,7 +128,7 @@ def build(name: str, seed: int, seqs: List[SeqSpec], *, num_heads: int, num_kv_h
           head_size: int, block_size: int, dtype: torch.dtype, sliding_window: int = 0,
           scale: Optional[float] = None, num_blocks: Optional[int] = None,
           copy_fraction: float = 0.0, rng: Optional[np.random.Generator] = None,
-          shared_prefix: int = 0) -> Workload:
+          shared_prefix: int = 0, cache_dtype: Optional[torch.dtype] = None) -> Workload:
     """Draw the inputs of every phase of ``seqs`` (see the module docstring for the order).
 
     The pool is ``ceil(1.1 * total blocks)`` physical blocks unless ``num_blocks`` is given;
@@ -136,7 +136,9 @@ def build(name: str, seed: int, seqs: List[SeqSpec], *, num_heads: int, num_kv_h
     rows are padded with -1.  ``shared_prefix`` (a multiple of ``block_size``, at most every
     ``ctx0``): the first that many keys of every sequence are the first sequence's, through
     the same physical blocks (a prefix-cache hit shared by the batch); the other sequences
-    take blocks only for the rest.
+    take blocks only for the rest.  ``cache_dtype`` (default ``dtype``): the cache fill is drawn
+    in that dtype (``torch.float8_e4m3fn``: N(0,1) rounded by torch's conversion), the queries
+    and new keys/values in ``dtype``.
     """
     rng = np.random.default_rng(seed) if rng is None else rng
     nphase = max(len(s.q) for s in seqs) if seqs else 0
@@ -161,7 +163,7 @@ def build(name: str, seed: int, seqs: List[SeqSpec], *, num_heads: int, num_kv_h
     allocated = perm[:cursor]
     free = perm[cursor:]
 
-    kv_cache = _gauss(rng, (2, num_blocks, block_size, num_kv_heads, head_size), dtype)
+    kv_cache = _gauss(rng, (2, num_blocks, block_size, num_kv_heads, head_size), cache_dtype or dtype)
 
     # per-phase token order: prefill chunks (sequence order) then decode tokens
     order = []
@@ -270,7 +272,8 @@ def config(n: int) -> Workload:
 def shared_prefix_decode(seed: int = 6, num_seqs: int = 64, prefix: int = 1024, lo: int = 1024,
                          hi: int = 4096, num_heads: int = 32, num_kv_heads: int = 8,
                          head_size: int = 128, block_size: int = 16,
-                         dtype: torch.dtype = torch.bfloat16) -> Workload:
+                         dtype: torch.dtype = torch.bfloat16,
+                         cache_dtype: Optional[torch.dtype] = None) -> Workload:
     """One decode step of ``num_seqs`` sequences that share their first ``prefix`` keys (one
     system prompt, served from the prefix cache): contexts U[lo, hi] (at least ``prefix``),
     the GQA decode shape otherwise.  The vLLM learning book (self-check question 4) names a
@@ -280,4 +283,4 @@ def shared_prefix_decode(seed: int = 6, num_seqs: int = 64, prefix: int = 1024, 
     seqs = [SeqSpec(int(c), [1], ["decode"]) for c in ctx]
     return build(f"shared_prefix{prefix}_b{num_seqs}", seed, seqs, num_heads=num_heads,
                  num_kv_heads=num_kv_heads, head_size=head_size, block_size=block_size, dtype=dtype,
-                 rng=rng, shared_prefix=prefix)
+                 rng=rng, shared_prefix=prefix, cache_dtype=cache_dtype)
