@@ -18,15 +18,18 @@ Default run (one JSON line on stdout):
     its mean duration, timed with HIP events on the stream the library launches on.
   * ``cpu_baseline``: the fp64 numpy oracle on the host, on a bounded sample of the same
     workload, in the same unit.
-  * ``shared_prefix``: decode of 64 sequences that share a 1024-key prefix (contexts
-    U[1024, 4096], same heads), as plain decode and as cascade decode (the shared prefix
-    attended once for all queries).
+  * ``fp8``: the headline decode step with the cache in FP8 (E4M3, kv_scale 1): half the
+    K/V bytes.
+  * ``shared_prefix``: decode of a batch whose sequences share a prefix of cached blocks,
+    as plain decode and as cascade decode (the shared prefix attended once for all
+    queries): 64 sequences sharing 1024 keys (contexts U[1024, 4096]) and 256 sequences
+    sharing 4096 keys (contexts U[4096, 8192]), same heads.
 
 Algorithmic work (not the work the kernels actually do):
   decode bytes  = sum_s keys(s) * Hkv * D * 2 (K and V) * 2 B + q + out + 4 B per block-table
                   entry read and per seq_len
   prefill FLOPs = sum over (query row, allowed key, head) of 4 * D
-  store bytes   = 2 * T * Hkv * D * 2 B read + the same written + 4 B per slot
+  store bytes   = 2 * T * Hkv * D * (bytes per element read + per element stored) + 4 B per slot
   cascade bytes = decode bytes with the shared prefix's K/V and block-table entries counted
                   once for the batch
 
@@ -67,7 +70,7 @@ def key_span(sq, sk, i, window):
 def decode_bytes(op, wl) -> float:
     import numpy as np
     elt = 2 if wl.dtype.itemsize == 2 else 4
-    row = wl.num_kv_heads * wl.head_size * elt
+    row = wl.num_kv_heads * wl.head_size * wl.kv_cache.element_size()   # 1 B per element for FP8
     total = 0
     for n in op.seq_lens.astype(np.int64):
         lo = max(0, int(n) - wl.sliding_window) if wl.sliding_window > 0 else 0
@@ -85,7 +88,7 @@ def cascade_bytes(op, wl, prefix: int) -> float:
     read once: the prefix K/V and table entries once, each sequence's own keys and entries."""
     import numpy as np
     elt = 2 if wl.dtype.itemsize == 2 else 4
-    row = wl.num_kv_heads * wl.head_size * elt
+    row = wl.num_kv_heads * wl.head_size * wl.kv_cache.element_size()
     total = 2 * prefix * row + 4 * (prefix // wl.block_size)
     for n in op.seq_lens.astype(np.int64):
         own = int(n) - prefix
@@ -112,13 +115,14 @@ def prefill_flops(op, wl) -> float:
 
 
 def store_bytes(op, wl) -> float:
-    elt = 2 if wl.dtype.itemsize == 2 else 4
+    elt = 2 if wl.dtype.itemsize == 2 else 4      # the new rows as passed in
+    celt = wl.kv_cache.element_size()             # as stored (1 B for FP8)
     t = len(op.slot_mapping)
-    return float(2 * 2 * t * wl.num_kv_heads * wl.head_size * elt + 4 * t)
+    return float(2 * t * wl.num_kv_heads * wl.head_size * (elt + celt) + 4 * t)
 
 
 def copy_bytes(op, wl) -> float:
-    elt = 2 if wl.dtype.itemsize == 2 else 4
+    elt = wl.kv_cache.element_size()
     return float(2 * len(op.pairs) * 2 * wl.block_size * wl.num_kv_heads * wl.head_size * elt)
 
 
@@ -351,26 +355,47 @@ def roofline(achieved, peak, unit, bound, traffic=None):
             "frac": round(achieved / peak, 4), "traffic": traffic}
 
 
-SHARED_PREFIX = 1024
-SHARED_PREFIX_NAME = ("shared-prefix decode: B 64, prefix 1024 keys shared, ctx U[1024,4096], H 32/8, "
-                      "D 128, bs 16, bf16")
+# shared-prefix decode batches: name -> (sequences, shared prefix keys, context range)
+SHARED_PREFIX = {"b64_p1024": (64, 1024, 1024, 4096), "b256_p4096": (256, 4096, 4096, 8192)}
+
+
+def shared_prefix_name(key):
+    b, p, lo, hi = SHARED_PREFIX[key]
+    return f"shared-prefix decode: B {b}, prefix {p} keys shared, ctx U[{lo},{hi}], H 32/8, D 128, bs 16, bf16"
 
 
 @functools.lru_cache(maxsize=1)
 def _workload(n):
+    import torch
     import workloads as W
-    return W.shared_prefix_decode(prefix=SHARED_PREFIX) if n == "shared_prefix" else W.config(n)
+    if n == "fp8_decode":
+        # the config-2 sequences with an FP8 cache
+        c2 = W.config(2)
+        return W.build("config2_fp8", 2, c2.seqs, num_heads=c2.num_heads, num_kv_heads=c2.num_kv_heads,
+                       head_size=c2.head_size, block_size=c2.block_size, dtype=torch.bfloat16,
+                       cache_dtype=torch.float8_e4m3fn)
+    if isinstance(n, str) and n in SHARED_PREFIX:
+        b, p, lo, hi = SHARED_PREFIX[n]
+        return W.shared_prefix_decode(num_seqs=b, prefix=p, lo=lo, hi=hi)
+    return W.config(n)
 
 
 def bench_workload(name, steps, warmup, dev, with_cpu, partition_size=0, flush_mb=1024, fused=False,
                    alibi=False, cascade=False):
     import workloads as W
-    wl = _workload("shared_prefix" if name == "shared_prefix" else WORKLOAD_CONFIG[name])
+    shared = name in SHARED_PREFIX
+    wl = _workload(name if shared or name == "fp8_decode" else WORKLOAD_CONFIG[name])
+    prefix = SHARED_PREFIX[name][1] if shared else 0
     phase = wl.phases[-1] if name == "chunked_decode" else wl.phases[0]
-    step = Step(wl, phase, dev, partition_size, fused, alibi, SHARED_PREFIX if cascade else 0)
+    step = Step(wl, phase, dev, partition_size, fused, alibi, prefix if cascade else 0)
     step_t, per_op, wall = step.time(steps, warmup, flush_mb * 1024 * 1024)
     ops = [d["op"] for d in step.prepared]
-    wname = SHARED_PREFIX_NAME if name == "shared_prefix" else W.CONFIG_NAMES[WORKLOAD_CONFIG[name]]
+    if shared:
+        wname = shared_prefix_name(name)
+    elif name == "fp8_decode":
+        wname = W.CONFIG_NAMES[2] + ", cache FP8 E4M3 (kv_scale 1)"
+    else:
+        wname = W.CONFIG_NAMES[WORKLOAD_CONFIG[name]]
     res = {"workload": wname, "ms_per_step": round(step_t * 1e3, 4),
            "wall_ms_per_step": round(wall * 1e3, 4), "cache_eviction_MiB_per_step": flush_mb, "ops": {}}
     total_bytes, total_flops = 0.0, 0.0
@@ -385,7 +410,7 @@ def bench_workload(name, steps, warmup, dev, with_cpu, partition_size=0, flush_m
             sb = float(2 * 2 * rows * wl.num_kv_heads * wl.head_size * elt + 4 * rows)
             total_bytes += sb
         if n == "DecodeOp" and cascade:
-            b = cascade_bytes(op, wl, SHARED_PREFIX)
+            b = cascade_bytes(op, wl, prefix)
             total_bytes += b
             res["ops"]["cascade_decode"] = {
                 "ms": round(t * 1e3, 4), "GB/s": round(b / t / 1e9, 1), "bytes": b,
@@ -503,12 +528,18 @@ def main() -> int:
         # the other two workloads, every op with its roofline (no CPU baseline): chunked prefill
         # with a 4096-key window and the decode after it (config 4), and the mixed step
         # copy_blocks -> store -> prefill -> decode (config 5)
-        # a batch sharing a 1024-key prefix: plain decode, then cascade decode
+        # the headline decode step over an FP8 cache
+        r = bench_workload("fp8_decode", 30, 5, dev, False, flush_mb=args.flush_mb)
+        line["fp8"] = {"workload": r["workload"], "ms_per_step": r["ms_per_step"], "step_GB/s": r["step_GB/s"],
+                       "ops": r["ops"]}
+        # batches sharing a prefix of cached blocks: plain decode, then cascade decode
         line["shared_prefix"] = {}
-        for kind, casc in (("decode", False), ("cascade", True)):
-            r = bench_workload("shared_prefix", 20, 5, dev, False, flush_mb=args.flush_mb, cascade=casc)
-            line["shared_prefix"][kind] = {"workload": r["workload"], "ms_per_step": r["ms_per_step"],
-                                           "ops": r["ops"]}
+        for key in SHARED_PREFIX:
+            line["shared_prefix"][key] = {}
+            for kind, casc in (("decode", False), ("cascade", True)):
+                r = bench_workload(key, 20, 5, dev, False, flush_mb=args.flush_mb, cascade=casc)
+                line["shared_prefix"][key][kind] = {"workload": r["workload"], "ms_per_step": r["ms_per_step"],
+                                                    "ops": r["ops"]}
         line["secondary"] = {}
         for name in ("chunked", "chunked_decode", "mixed"):
             r = bench_workload(name, 10, 3, dev, False, flush_mb=args.flush_mb)
