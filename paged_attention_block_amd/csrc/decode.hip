@@ -64,14 +64,22 @@ template <int D> struct StepT<D, true> {
     typedef typename VRow8<D>::T V;
 };
 
-// Per-lane byte offsets from a 16-key group's first row: K rows (key col, dims 8*grp of each
-// 32-dim slice), V rows (key 4*grp + j%4, dims DPL*col).
+// Per-lane byte offsets from a 16-key group's first row: K rows (key col, 16 bytes at 16*grp
+// of each 32-dim (bf16) or 64-dim (FP8) piece), V rows (key 4*grp + j%4, dims DPL*col).
+//
+// K.Q^T sums over the dims in any order as long as q uses the same one, so the MFMA k-slices
+// need not be 32 consecutive dims.  bf16: slice t = dims 32t + 8*grp .. +8 (one 16-byte load).
+// FP8: one 16-byte load brings dims 64u + 16*grp .. +16, split into slices t = 2u (first 8)
+// and 2u + 1 (last 8): half the K load instructions of 8-byte loads.  q_slice() gives the
+// matching 16-byte piece of the bf16 q row for slice t.
 template <int D, bool FP8>
 __device__ inline void lane_offsets(int col, int grp, uint32_t row_bytes, uint32_t& k_off, uint32_t& v_off) {
     constexpr int ELT = FP8 ? 1 : 2;
-    k_off = (uint32_t)col * row_bytes + (uint32_t)(8 * ELT) * grp;
+    k_off = (uint32_t)col * row_bytes + 16u * grp;
     v_off = (uint32_t)(4 * grp) * row_bytes + (uint32_t)(ELT * (D / 16)) * col;
 }
+template <bool FP8>
+__device__ inline int q_slice(int t, int grp) { return FP8 ? 8 * (t >> 1) + 2 * grp + (t & 1) : 4 * t + grp; }
 
 // Loads of the 32-key step at k0 into registers: K rows (2 groups of 16 keys x KS slices,
 // MFMA A-operand layout) and the V rows one lane needs for the PV MFMAs (8 keys x DPL
@@ -103,9 +111,16 @@ __device__ __forceinline__ void load_step(int k0, int kb, int ke, const int32_t*
 #pragma unroll
     for (int ga = 0; ga < 2; ++ga) {
         const char* base = kplane + gb[ga];
+        if constexpr (FP8) {
 #pragma unroll
-        for (int t = 0; t < D / 32; ++t) {
-            kr[ga][t] = *(const typename StepT<D, FP8>::K*)(base + k_off + 16 * (FP8 ? 2 : 4) * t);
+            for (int u = 0; u < D / 64; ++u) {
+                const u32x4 x = *(const u32x4*)(base + k_off + 64 * u);
+                kr[ga][2 * u] = u32x2{x[0], x[1]};
+                kr[ga][2 * u + 1] = u32x2{x[2], x[3]};
+            }
+        } else {
+#pragma unroll
+            for (int t = 0; t < D / 32; ++t) kr[ga][t] = *(const u32x4*)(base + k_off + 64 * t);
         }
     }
 #pragma unroll
@@ -407,13 +422,13 @@ __global__ __launch_bounds__(512) void decode_bf16_kernel(const DecodeArgs a) {
             const int ke = min(n, base + 32 * le);             // one past the last
             const int32_t* __restrict__ table = a.table + (int64_t)s * a.max_blocks;
 
-            // Q^T operand: head col, dims 32t + 8*grp .. +8
+            // Q^T operand: head col, the dims of k-slice t (q_slice)
             bf16x8 qf[KS];
             {
                 const u32x4* qrow = (const u32x4*)((const __bf16*)a.q + ((int64_t)s * H + (head_ok ? head : g * G)) * D);
 #pragma unroll
                 for (int t = 0; t < KS; ++t) {
-                    const u32x4 x = qrow[4 * t + grp];
+                    const u32x4 x = qrow[q_slice<FP8>(t, grp)];
                     qf[t] = __builtin_bit_cast(bf16x8, head_ok ? x : (u32x4)(0u));
                 }
             }
@@ -536,7 +551,7 @@ __global__ __launch_bounds__(512) void cascade_prefix_kernel(const DecodeArgs a,
         const u32x4* qrow = (const u32x4*)((const __bf16*)a.q + ((int64_t)s * H + head) * D);
 #pragma unroll
         for (int t = 0; t < KS; ++t) {
-            const u32x4 x = qrow[4 * t + grp];
+            const u32x4 x = qrow[q_slice<FP8>(t, grp)];
             qf[t] = __builtin_bit_cast(bf16x8, row_ok ? x : (u32x4)(0u));
         }
     }
