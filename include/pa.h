@@ -61,9 +61,9 @@ typedef enum pa_dtype {
  * floating-point specification (sign, 4 exponent bits with bias 7, 3 mantissa bits, no
  * infinities, largest finite 448).  The store writes e4m3(x * r), r = fp32(1 / kv_scale),
  * rounded to nearest even and saturated to +-448; attention reads e4m3 * kv_scale.  kv_scale
- * must be finite and > 0 for such a cache and is ignored otherwise.  Supported by pa_store_kv,
- * pa_copy_blocks, pa_decode, pa_decode_with_store and pa_cascade_decode; the prefill calls
- * return PA_ERR_UNSUPPORTED for it. */
+ * must be finite and > 0 for such a cache and is ignored otherwise.  Every call supports it;
+ * pa_prefill_varlen_with_store then runs the store before the attention instead of inside
+ * it, so the attention reads the quantized new rows like any other cached row. */
 typedef struct pa_cache_desc {
     void*   kv_cache;
     int32_t num_blocks;
@@ -147,10 +147,11 @@ int pa_prefill_varlen(const pa_cache_desc* cache, void* out, const void* query,
  * the section-10 question on how K/V reach the cache: the attention kernel itself writes the
  * new tokens' K/V at their slot_mapping slots, saving the separate store launch.  Here, for
  * bf16 caches, the prefill kernel takes the new keys straight from key/value (they are the
- * last seqlen_q keys of each sequence) and writes them to the cache as it goes; float32 caches
- * run the store and the attention back to back.
+ * last seqlen_q keys of each sequence) and writes them to the cache as it goes; float32 and
+ * FP8 caches run the store and the attention back to back.
  *
  *   key, value    [num_tokens][num_kv_heads][head_size], row t = query row t, cache dtype
+ *                 (bfloat16 for PA_FP8_E4M3)
  *   slot_mapping  [num_tokens] int32: the cache slot of each row's token
  *   num_tokens    == cu_seqlens_q[num_seqs] (the rows of query, key and value)
  * Other arguments as pa_prefill_varlen.  Precondition (as in the paged layout everywhere):

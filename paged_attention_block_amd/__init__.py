@@ -181,11 +181,12 @@ def pa_prefill_varlen(query: torch.Tensor, kv_cache: torch.Tensor, block_table: 
                       cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor, max_seqlen_q: int,
                       max_seqlen_k: int, scale: float, num_kv_heads: int, sliding_window: int = 0,
                       out: Optional[torch.Tensor] = None,
-                      alibi_slopes: Optional[torch.Tensor] = None) -> torch.Tensor:
+                      alibi_slopes: Optional[torch.Tensor] = None, kv_scale: float = 1.0) -> torch.Tensor:
     """Varlen causal attention of packed ``query [Tq, H, D]`` over the cached keys
-    (``alibi_slopes``: optional float32 ``[H]`` ALiBi slopes on the cache's device)."""
+    (``alibi_slopes``: optional float32 ``[H]`` ALiBi slopes on the cache's device;
+    ``kv_scale``: the scale of an FP8 cache)."""
     lib = load()
-    desc = _desc(kv_cache)
+    desc = _desc(kv_cache, kv_scale)
     dev = kv_cache.device
     if num_kv_heads != kv_cache.shape[3]:
         raise ValueError(f"num_kv_heads {num_kv_heads} != cache's {kv_cache.shape[3]}")
@@ -344,11 +345,12 @@ def pa_prefill_varlen_with_store(query: torch.Tensor, key: torch.Tensor, value: 
                                  cu_seqlens_k: torch.Tensor, max_seqlen_q: int, max_seqlen_k: int,
                                  scale: float, num_kv_heads: int, sliding_window: int = 0,
                                  out: Optional[torch.Tensor] = None,
-                                 alibi_slopes: Optional[torch.Tensor] = None) -> torch.Tensor:
+                                 alibi_slopes: Optional[torch.Tensor] = None,
+                                 kv_scale: float = 1.0) -> torch.Tensor:
     """Store the batch's new tokens (``key``/``value [Tq, Hkv, D]`` at ``slot_mapping``) and run
     the varlen causal attention of ``query [Tq, H, D]`` in one call (one kernel for bf16)."""
     lib = load()
-    desc = _desc(kv_cache)
+    desc = _desc(kv_cache, kv_scale)
     dev = kv_cache.device
     if num_kv_heads != kv_cache.shape[3]:
         raise ValueError(f"num_kv_heads {num_kv_heads} != cache's {kv_cache.shape[3]}")

@@ -209,7 +209,6 @@ static int prefill_args(const pa_cache_desc* cache, void* out, const void* query
     *empty = false;
     int st = check_cache(cache, &a.c);
     if (st) return st;
-    if (a.c.dtype == PA_FP8_E4M3) return fail(PA_ERR_UNSUPPORTED, "prefill over an FP8 cache is not supported");
     if ((st = check_heads(a.c, num_heads))) return st;
     if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs must be >= 0 (got %d)", num_seqs);
     if (max_seqlen_q < 0 || max_seqlen_k < 0) return fail(PA_ERR_INVALID_ARG, "max_seqlen_q/k must be >= 0");
@@ -257,7 +256,7 @@ int pa_prefill_varlen(const pa_cache_desc* cache, void* out, const void* query,
     if (st) return st;
     if (empty) { g_last_error[0] = 0; return PA_OK; }
     hipStream_t s = (hipStream_t)stream;
-    return launch_status(a.c.dtype == PA_BF16 ? pa::launch_prefill_bf16(a, s) : pa::launch_prefill_f32(a, s));
+    return launch_status(a.c.dtype == PA_F32 ? pa::launch_prefill_f32(a, s) : pa::launch_prefill_bf16(a, s));
 }
 
 int pa_prefill_varlen_with_store(const pa_cache_desc* cache, void* out, const void* query,
@@ -289,7 +288,8 @@ int pa_prefill_varlen_with_store(const pa_cache_desc* cache, void* out, const vo
         a.slots = slot_mapping;
         return launch_status(pa::launch_prefill_bf16(a, s));
     }
-    // float32 correctness path: the store, then the attention, on the same stream
+    // float32 and FP8 caches: the store, then the attention, on the same stream (an FP8 cache
+    // must hold the quantized new rows before the attention reads them)
     pa::StoreArgs sa;
     sa.c = a.c;
     sa.key = key;
@@ -298,7 +298,7 @@ int pa_prefill_varlen_with_store(const pa_cache_desc* cache, void* out, const vo
     sa.num_tokens = num_tokens;
     hipError_t e = pa::launch_store(sa, s);
     if (e != hipSuccess) return launch_status(e);
-    return launch_status(pa::launch_prefill_f32(a, s));
+    return launch_status(a.c.dtype == PA_F32 ? pa::launch_prefill_f32(a, s) : pa::launch_prefill_bf16(a, s));
 }
 
 size_t pa_decode_workspace_size(const pa_cache_desc* cache, int32_t num_seqs, int32_t num_heads,

@@ -1,4 +1,4 @@
-// Varlen causal paged prefill for bf16 caches on gfx950 (MFMA, fp32 online softmax).
+// Varlen causal paged prefill for bf16 and FP8 caches on gfx950 (MFMA, fp32 online softmax).
 //
 // The operation (MinivLLM API docs, "Attention", flash_attention_prefill; HF transformers
 // continuous_batching input_ouputs.py, build_attention_mask): packed query chunks, causal
@@ -97,9 +97,19 @@ struct PrefillGrid {
 };
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// two E4M3 codes (bytes 0-1, or 2-3 with hi) -> two bf16, exactly
+__device__ inline uint32_t e4m3x2_to_bf16(uint32_t w, bool hi) {
+    return hi ? __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.f, true))
+              : __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.f, false));
+}
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-template <int D, int NBR, int BN, int NBUF, bool ALIBI>
+// FP8: the cache holds E4M3 codes of K / kv_scale and V / kv_scale.  A tile copy is then a
+// register-staged 8-byte load per lane, widened exactly to bf16 (every E4M3 value is a bf16
+// value) and written to the same swizzled LDS slot the bf16 copy fills, so the MFMA operand
+// reads are unchanged; kv_scale joins the softmax scale and the output normalisation.
+template <int D, int NBR, int BN, int NBUF, bool ALIBI, bool FP8>
 __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const PrefillArgs a, const PrefillGrid pg) {
     constexpr int NGA = BN / 16;      // 16-key groups per K/V tile
     constexpr int NCC = BN / 32;      // 32-key chunks per K/V tile (PV MFMA k-steps)
@@ -113,6 +123,8 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const PrefillArgs 
     constexpr int TILE = BN * D * 2;  // bytes of one plane of one tile
     constexpr int KSW = CPR >= 16 ? 15 : CPR - 1;        // K swizzle mask
     constexpr int VSW = CPR >= 16 ? 14 : CPR - 2;        // V swizzle mask (even values)
+    constexpr int ELT = FP8 ? 1 : 2;  // bytes per cache element
+    static_assert(!FP8 || NBUF == 2, "the FP8 copy stages one tile in registers");
 
     // NBUF K and NBUF V buffers as distinct objects, so the compiler can tell a copy into one
     // from a read of another and does not wait for in-flight copies before every LDS read
@@ -177,20 +189,20 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const PrefillArgs 
     const int wv_lo_max = W > 0 ? max(0, off + r_last - W + 1) : 0;
     const int wv_p_min = off + r0;
 
-    const float c_log2 = a.scale * 1.4426950408889634f;
+    const float c_log2 = a.scale * (FP8 ? a.c.kv_scale : 1.f) * 1.4426950408889634f;
     // ALiBi slope of this wave's head in log2 units (the bias slope * (j - p) is added to the
     // scaled score before the softmax)
     const float sl2 = ALIBI && wave_ok ? a.alibi[h] * 1.4426950408889634f : 0.f;
     const int BS = a.c.block_size;
     const int shift = a.c.block_shift;
     const char* __restrict__ kplane = (const char*)a.c.kv;
-    const int64_t vdelta = a.c.plane_elems * 2;
+    const int64_t vdelta = a.c.plane_elems * ELT;
     // the block table through the constant address space: it is never written while the
     // kernel runs, so the (wave-uniform) lookups become scalar loads that do not share the
     // vector-memory counter with the in-flight tile copies
     typedef __attribute__((address_space(4))) const int32_t cint32;
     cint32* table = (cint32*)(a.table + (int64_t)s * a.max_blocks);
-    const int64_t RB = (int64_t)Hkv * D * 2;  // cache token-row bytes
+    const int64_t RB = (int64_t)Hkv * D * ELT;  // cache token-row bytes
 
     // ---------------------------------------------------------------- Q^T operands
     bf16x8 qf[NBR][KS];
@@ -244,8 +256,8 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const PrefillArgs 
         const int row = RPI * ig + crow;   // token row within the group (0..15)
         const int ck = cslot ^ (row & KSW);
         const int cv = cslot ^ ((2 * row) & VSW);
-        cgk[jj] = (uint32_t)(((row * Hkv + g) * D + ck * 8) * 2);
-        cgv[jj] = (uint32_t)(((row * Hkv + g) * D + cv * 8) * 2);
+        cgk[jj] = (uint32_t)(((row * Hkv + g) * D + ck * 8) * ELT);
+        cgv[jj] = (uint32_t)(((row * Hkv + g) * D + cv * 8) * ELT);
         my_copies += (copier && ig < IPG) ? 2 : 0;
     }
 
@@ -258,7 +270,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const PrefillArgs 
     // the sequence's rows (rows past the last key are zeroed after the copy).
     const char* knew = (const char*)a.knew;
     const char* vnew = (const char*)a.vnew;
-    const bool fused = knew != nullptr;
+    const bool fused = !FP8 && knew != nullptr;  // an FP8 cache is stored by its own kernel first
     struct GroupSrc {
         const char* k;   // uniform base (non-mixed) of the group's first row, KV head 0
         const char* v;
@@ -285,9 +297,20 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const PrefillArgs 
         }
         return r;
     };
+    // FP8: the codes of the tile in flight, staged until land() widens them into LDS
+    u32x2 stg_k[IPG], stg_v[IPG];
     // copy this wave's share of one plane of a tile into LDS buffer dst
     auto issue = [&](const GroupSrc& gs, bool vplane_, const uint32_t (&cg)[IPG], char* dst) {
         if (!copier) return;
+        if constexpr (FP8) {
+            const char* src = vplane_ ? gs.v : gs.k;
+#pragma unroll
+            for (int jj = 0; jj < IPG; ++jj) {
+                const int ig = csub + nsub * jj;
+                if (ig < IPG) (vplane_ ? stg_v : stg_k)[jj] = *(const u32x2*)(src + cg[jj]);
+            }
+            return;
+        }
         const uint32_t lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)dst;
         if (!gs.mixed) {
             const char* src = vplane_ ? gs.v : gs.k;
@@ -312,6 +335,23 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const PrefillArgs 
                     }
                     copy_to_lds16_lane(p, lds + 1024u * (uint32_t)(IPG * cga + ig));
                 }
+            }
+        }
+    };
+    // FP8: widen the staged codes of this wave's share of a tile into its LDS buffers
+    auto land = [&](char* dk, char* dv) {
+        if (!copier) return;
+        auto widen = [](u32x2 w) {
+            return u32x4{e4m3x2_to_bf16(w[0], false), e4m3x2_to_bf16(w[0], true), e4m3x2_to_bf16(w[1], false),
+                         e4m3x2_to_bf16(w[1], true)};
+        };
+#pragma unroll
+        for (int jj = 0; jj < IPG; ++jj) {
+            const int ig = csub + nsub * jj;
+            if (ig < IPG) {
+                const uint32_t o = 1024u * (uint32_t)(IPG * cga + ig) + 16u * lane;
+                *(u32x4*)(dk + o) = widen(stg_k[jj]);
+                *(u32x4*)(dv + o) = widen(stg_v[jj]);
             }
         }
     };
@@ -512,8 +552,12 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const PrefillArgs 
         const int k0 = kt * BN;
         // this wave's copies of tile kt have landed once at most those of the tiles after
         // it (up to NBUF - 2 of them) are still in flight
-        const int later = min(NBUF - 2, kt_end - 1 - kt);
-        wait_vmcnt(my_copies * later);
+        if constexpr (FP8) {
+            land(kc, vc);  // the compiler waits for the staged loads it issued
+        } else {
+            const int later = min(NBUF - 2, kt_end - 1 - kt);
+            wait_vmcnt(my_copies * later);
+        }
         zero_dead(k0, kc);
         zero_dead(k0, vc);
         // all copies of tile kt visible; buffer jn (tile kt - 1) is free.  Not a fenced
@@ -570,7 +614,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const PrefillArgs 
         const float lt = group4_sum(l_run[nb]);
         const int row = r0 + 16 * nb + col;
         if (row >= rows_end) continue;
-        const float inv = lt > 0.f ? 1.f / lt : 0.f;
+        const float inv = lt > 0.f ? (FP8 ? a.c.kv_scale : 1.f) / lt : 0.f;  // FP8: V / kv_scale in the cache
         __bf16* dst = (__bf16*)a.out + ((int64_t)(q0 + row) * H + h) * D + 4 * grp;
 #pragma unroll
         for (int d = 0; d < DB; ++d) {
@@ -598,13 +642,16 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t st) {
     const int64_t nsg_pad = ((int64_t)pg.n_sg + 7) / 8 * 8;
     const dim3 grid((unsigned)(nsg_pad * pg.n_tiles));
     const bool alibi = a.alibi != nullptr;
+    const bool fp8 = a.c.dtype == 2;
+#define PA_PREFILL(DD, AL, F8) hipLaunchKernelGGL((prefill_bf16_kernel<DD, 2, kPrefillBN, kPrefillNBUF, AL, F8>), grid, dim3(256), 0, st, a, pg)
     if (a.c.head_size == 128) {
-        if (alibi) hipLaunchKernelGGL((prefill_bf16_kernel<128, 2, kPrefillBN, kPrefillNBUF, true>), grid, dim3(256), 0, st, a, pg);
-        else hipLaunchKernelGGL((prefill_bf16_kernel<128, 2, kPrefillBN, kPrefillNBUF, false>), grid, dim3(256), 0, st, a, pg);
+        if (fp8) { if (alibi) PA_PREFILL(128, true, true); else PA_PREFILL(128, false, true); }
+        else { if (alibi) PA_PREFILL(128, true, false); else PA_PREFILL(128, false, false); }
     } else {
-        if (alibi) hipLaunchKernelGGL((prefill_bf16_kernel<64, 2, kPrefillBN, kPrefillNBUF, true>), grid, dim3(256), 0, st, a, pg);
-        else hipLaunchKernelGGL((prefill_bf16_kernel<64, 2, kPrefillBN, kPrefillNBUF, false>), grid, dim3(256), 0, st, a, pg);
+        if (fp8) { if (alibi) PA_PREFILL(64, true, true); else PA_PREFILL(64, false, true); }
+        else { if (alibi) PA_PREFILL(64, true, false); else PA_PREFILL(64, false, false); }
     }
+#undef PA_PREFILL
     return hipGetLastError();
 }
 

@@ -82,7 +82,7 @@ class GpuRun:
             return pa.pa_prefill_varlen(op.query.to(self.dev), self.cache, self.i32(op.block_table),
                                         self.i32(op.cu_seqlens_q), self.i32(op.cu_seqlens_k),
                                         op.max_seqlen_q, op.max_seqlen_k, wl.scale, wl.num_kv_heads,
-                                        wl.sliding_window, alibi_slopes=self._slopes())
+                                        wl.sliding_window, alibi_slopes=self._slopes(), kv_scale=self.kv_scale)
         if isinstance(op, W.DecodeOp):
             return pa.pa_decode(op.query.to(self.dev), self.cache, self.i32(op.block_table),
                                 self.i32(op.seq_lens), op.max_seq_len, wl.scale, wl.num_kv_heads,
@@ -100,7 +100,8 @@ class GpuRun:
             return pa.pa_prefill_varlen_with_store(op.query.to(d), k, v, sl, self.cache, self.i32(op.block_table),
                                                    self.i32(op.cu_seqlens_q), self.i32(op.cu_seqlens_k),
                                                    op.max_seqlen_q, op.max_seqlen_k, wl.scale, wl.num_kv_heads,
-                                                   wl.sliding_window, alibi_slopes=self._slopes())
+                                                   wl.sliding_window, alibi_slopes=self._slopes(),
+                                                   kv_scale=self.kv_scale)
         return pa.pa_decode_with_store(op.query.to(d), k, v, sl, self.cache, self.i32(op.block_table),
                                        self.i32(op.seq_lens), op.max_seq_len, wl.scale, wl.num_kv_heads,
                                        wl.sliding_window, partition_size=partition_size,

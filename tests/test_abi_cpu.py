@@ -180,11 +180,13 @@ def test_fp8_cache_checks(lib):
         assert b"kv_scale" in lib.pa_last_error()
     d = desc(dtype=2, kv_scale=0.5)
     assert lib.pa_store_kv(d, FAKE, FAKE, FAKE, 0, None) == 0
-    # prefill over an FP8 cache is refused, with or without the fused store
-    assert lib.pa_prefill_varlen(d, FAKE, FAKE, FAKE, 4, FAKE, FAKE, 2, 10, 60, 8, 0.1, 0, None, None) == 2
-    assert b"FP8" in lib.pa_last_error()
-    args = (d, FAKE, FAKE, FAKE, FAKE, FAKE, 40, FAKE, 4, FAKE, FAKE, 2, 20, 30, 8, 0.1, 0, None, None)
-    assert lib.pa_prefill_varlen_with_store(*args) == 2
+    # prefill over an FP8 cache takes the same argument checks (and the kv_scale one)
+    assert lib.pa_prefill_varlen(d, FAKE, FAKE, FAKE, 4, FAKE, FAKE, 2, 10, 65, 8, 0.1, 0, None, None) == 1
+    assert b"max_blocks_per_seq" in lib.pa_last_error()
+    bad = desc(dtype=2, kv_scale=-2.0)
+    assert lib.pa_prefill_varlen(bad, FAKE, FAKE, FAKE, 4, FAKE, FAKE, 2, 10, 60, 8, 0.1, 0, None, None) == 1
+    args = (d, FAKE, FAKE, None, FAKE, FAKE, 40, FAKE, 4, FAKE, FAKE, 2, 20, 30, 8, 0.1, 0, None, None)
+    assert lib.pa_prefill_varlen_with_store(*args) == 1 and b"key" in lib.pa_last_error()
     # decode plans the same split as for bf16
     d8 = desc(nb=1000, bs=16, hkv=8, d=128, dtype=2, kv_scale=0.5)
     b8 = desc(nb=1000, bs=16, hkv=8, d=128, dtype=1)

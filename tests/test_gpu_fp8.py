@@ -1,6 +1,7 @@
 """GPU parity of the FP8 (E4M3) KV cache: the quantizing store bit for bit against the
-oracle (every finite bf16 value, and random rows at several scales), and decode / cascade
-decode over FP8 caches against the oracle's attention over the dequantized cache."""
+oracle (every finite bf16 value, and random rows at several scales), and decode, cascade
+decode and prefill over FP8 caches against the oracle's attention over the dequantized
+cache."""
 
 from __future__ import annotations
 
@@ -177,12 +178,71 @@ def test_fp8_decode_gqa_full_size_sampled():
     assert_close(np.stack([got[r, h] for r, h in picks]), ref, torch.bfloat16, "fp8 decode full")
 
 
-def test_fp8_prefill_is_refused():
-    import paged_attention_block_amd as pa
-    wl = W.build("fp", 504, [W.SeqSpec(0, [20], ["prefill"])], num_heads=4, num_kv_heads=2, head_size=64,
-                 block_size=16, dtype=torch.bfloat16, cache_dtype=F8)
+PREFILL_CASES = {
+    # name: (H, Hkv, D, BS, window, [(ctx0, q) ...])
+    "g4_d128": (32, 8, 128, 16, 0, [(0, 1), (0, 37), (0, 200), (150, 90)]),
+    "g5_d128_window": (10, 2, 128, 16, 70, [(0, 130), (300, 64), (20, 5)]),
+    "g8_d64_chunked": (16, 2, 64, 32, 0, [(64, 100), (1000, 33)]),
+}
+
+
+@pytest.mark.parametrize("kv_scale", [1.0, 0.5])
+@pytest.mark.parametrize("name", sorted(PREFILL_CASES))
+def test_fp8_prefill(name, kv_scale):
+    H, Hkv, D, BS, win, spec = PREFILL_CASES[name]
+    seqs = [W.SeqSpec(c, [q], ["prefill"]) for c, q in spec]
+    wl = W.build(name, 505, seqs, num_heads=H, num_kv_heads=Hkv, head_size=D, block_size=BS,
+                 dtype=torch.bfloat16, sliding_window=win, cache_dtype=F8)
     run = GpuRun(wl, DEV)
-    _, pre = wl.phases[0]
-    with pytest.raises(pa.PaError) as e:
-        run.run(pre)
-    assert e.value.status == 2
+    run.kv_scale = kv_scale
+    store, pre = wl.phases[0]
+    vals = _store_then(run, store, kv_scale)
+    say(f"[fp8 prefill {name} s{kv_scale}]")
+    out = run.run(pre)
+    torch.cuda.synchronize()
+    ref = oracle.prefill_varlen(host_values(pre.query), vals, pre.block_table, pre.cu_seqlens_q, pre.cu_seqlens_k,
+                                wl.scale, wl.num_kv_heads, win)
+    assert_close(out.float().cpu().numpy(), ref, torch.bfloat16, f"fp8 prefill {name}")
+
+
+def test_fp8_prefill_with_store_alibi():
+    """The fused call over an FP8 cache: the store runs first, so the attention reads the
+    quantized new rows; cache contents and output match the oracle's store then prefill."""
+    wl = W.build("fpws", 506, [W.SeqSpec(0, [150], ["prefill"]), W.SeqSpec(200, [70], ["prefill"])],
+                 num_heads=16, num_kv_heads=4, head_size=128, block_size=16, dtype=torch.bfloat16,
+                 cache_dtype=F8)
+    slopes = np.array([2.0 ** (-8.0 * (i + 1) / 16) for i in range(16)])
+    run = GpuRun(wl, DEV)
+    run.kv_scale = 0.25
+    run.alibi = slopes
+    store, pre = wl.phases[0]
+    before = bits(wl.kv_cache)
+    say("[fp8 prefill with store alibi]")
+    out = run.run_with_store(store, pre)
+    torch.cuda.synchronize()
+    ref_cache = fp8.store_kv_fp8(before, store.key.float().numpy(), store.value.float().numpy(),
+                                 store.slot_mapping, 0.25)
+    np.testing.assert_array_equal(bits(run.cache.cpu()), ref_cache)
+    ref = oracle.prefill_varlen(host_values(pre.query), fp8.dequantize(ref_cache, 0.25), pre.block_table,
+                                pre.cu_seqlens_q, pre.cu_seqlens_k, wl.scale, wl.num_kv_heads, 0, slopes)
+    assert_close(out.float().cpu().numpy(), ref, torch.bfloat16, "fp8 prefill with store")
+
+
+def test_fp8_prefill_varlen_full_size_sampled():
+    """16 prompts U[128, 2048], H 32/8, D 128 over an FP8 cache: sampled rows."""
+    rng = np.random.default_rng(3)
+    lens = rng.integers(128, 2048 + 1, size=16)
+    wl = W.build("fp8_prefill", 507, [W.SeqSpec(0, [int(n)], ["prefill"]) for n in lens], num_heads=32,
+                 num_kv_heads=8, head_size=128, block_size=16, dtype=torch.bfloat16, cache_dtype=F8)
+    run = GpuRun(wl, DEV)
+    run.kv_scale = 1.5
+    store, pre = wl.phases[0]
+    vals = _store_then(run, store, 1.5)
+    say("[fp8 prefill full size]")
+    out = run.run(pre)
+    torch.cuda.synchronize()
+    picks = sample_picks(pre, wl.num_heads, np.random.default_rng(10), n_random=64)
+    ref = oracle.attention_rows(host_values(pre.query), vals, pre.block_table, pre.cu_seqlens_q, pre.cu_seqlens_k,
+                                wl.scale, wl.num_kv_heads, 0, picks)
+    got = out.float().cpu().numpy()
+    assert_close(np.stack([got[r, h] for r, h in picks]), ref, torch.bfloat16, "fp8 prefill full")
