@@ -787,23 +787,24 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_cascade_decode_bf16(const DecodeArgs& a, hipStream_t st) {
-    const int row_groups = (a.num_seqs * a.group + 15) / 16;
-    const int units = a.c.num_kv_heads * a.prefix_chunks;
-    const dim3 grid((unsigned)(8LL * row_groups * ((units + 7) / 8)));
     const bool fp8 = a.c.dtype == 2;
-    if (fp8) {
-        if (a.c.head_size == 128)
-            hipLaunchKernelGGL((cascade_prefix_kernel<128, true>), grid, dim3(512), 0, st, a, row_groups);
-        else
-            hipLaunchKernelGGL((cascade_prefix_kernel<64, true>), grid, dim3(512), 0, st, a, row_groups);
-        launch_partition_merge<false, true, true>(a, st);
+    if (a.prefix_mfma) {
+        const hipError_t e = launch_prefix_states(a, st);
+        if (e != hipSuccess) return e;
     } else {
-        if (a.c.head_size == 128)
-            hipLaunchKernelGGL((cascade_prefix_kernel<128, false>), grid, dim3(512), 0, st, a, row_groups);
-        else
-            hipLaunchKernelGGL((cascade_prefix_kernel<64, false>), grid, dim3(512), 0, st, a, row_groups);
-        launch_partition_merge<false, true, false>(a, st);
+        const int row_groups = (a.num_seqs * a.group + 15) / 16;
+        const int units = a.c.num_kv_heads * a.prefix_chunks;
+        const dim3 grid((unsigned)(8LL * row_groups * ((units + 7) / 8)));
+        if (a.c.head_size == 128) {
+            if (fp8) hipLaunchKernelGGL((cascade_prefix_kernel<128, true>), grid, dim3(512), 0, st, a, row_groups);
+            else hipLaunchKernelGGL((cascade_prefix_kernel<128, false>), grid, dim3(512), 0, st, a, row_groups);
+        } else {
+            if (fp8) hipLaunchKernelGGL((cascade_prefix_kernel<64, true>), grid, dim3(512), 0, st, a, row_groups);
+            else hipLaunchKernelGGL((cascade_prefix_kernel<64, false>), grid, dim3(512), 0, st, a, row_groups);
+        }
     }
+    if (fp8) launch_partition_merge<false, true, true>(a, st);
+    else launch_partition_merge<false, true, false>(a, st);
     return hipGetLastError();
 }
 

@@ -120,16 +120,37 @@ int32_t max_keys_of(int32_t max_seq_len, int32_t window, int32_t start = 0) {
     return max_seq_len;
 }
 
-// Key chunks of a shared prefix of P keys: about one 8-wave prefix workgroup per compute
-// unit over the (KV head, 16-row group) pairs, each wave keeping at least two 32-key steps.
-int32_t cascade_prefix_chunks(int32_t num_seqs, int32_t group, int32_t num_kv_heads, int32_t P) {
-    const int64_t steps = (P + 31) / 32;
-    const int64_t units = (((int64_t)num_seqs * group + 15) / 16) * num_kv_heads;
-    int64_t nc = (256 + units - 1) / units;
-    const int64_t most = steps / 16 > 1 ? steps / 16 : 1;
+// The shared prefix's pass and its key chunks.  With many (sequence, query head) rows per KV
+// head the pass runs on the prefill kernel (64-key tiles in LDS shared by four waves of 32
+// rows), its chunks sized for about one workgroup per compute unit with at least two tiles
+// each; with few rows that kernel has too few q-tiles to fill the device and the pass runs on
+// the split-key kernel (16 rows per wave, the waves of a workgroup splitting the chunk's
+// keys), with about one 8-wave workgroup per compute unit and at least two 32-key steps per
+// wave.  Measured crossover: B 64 x G 4 = 256 rows favour the split-key kernel, 1024 rows the
+// prefill kernel.
+struct PrefixPlan {
+    int32_t chunks;
+    bool mfma;
+};
+PrefixPlan cascade_prefix_plan(int32_t num_seqs, int32_t group, int32_t num_kv_heads, int32_t P) {
+    PrefixPlan p;
+    p.mfma = (int64_t)num_seqs * group >= 512;
+    int64_t nc, most;
+    if (p.mfma) {
+        const int64_t wpc = pa::prefix_workgroups_per_chunk(num_seqs, group, num_kv_heads);
+        const int64_t tiles = pa::prefix_tiles(P);
+        nc = (256 + wpc - 1) / wpc;
+        most = tiles / 2;
+    } else {
+        const int64_t steps = (P + 31) / 32;
+        const int64_t units = (((int64_t)num_seqs * group + 15) / 16) * num_kv_heads;
+        nc = (256 + units - 1) / units;
+        most = steps / 16;
+    }
     if (nc > most) nc = most;
     if (nc > 64) nc = 64;
-    return (int32_t)(nc < 1 ? 1 : nc);
+    p.chunks = (int32_t)(nc < 1 ? 1 : nc);
+    return p;
 }
 
 // Workspace bytes of a decode launch: partial states of the chunk split (none with a
@@ -137,18 +158,21 @@ int32_t cascade_prefix_chunks(int32_t num_seqs, int32_t group, int32_t num_kv_he
 struct DecodePlan {
     Chunks c;
     int32_t prefix_chunks;
+    bool prefix_mfma;
     size_t chunk_bytes;
     size_t prefix_bytes;
 };
 DecodePlan decode_plan(const pa_cache_desc* cache, int32_t num_seqs, int32_t num_heads, int32_t max_seq_len,
                        int32_t window, int32_t key_start, int32_t partition_size) {
-    DecodePlan p = {{1, 1}, 0, 0, 0};
+    DecodePlan p = {{1, 1}, 0, false, 0, 0};
     if (cache->dtype == PA_F32) return p;
     p.c = decode_chunks(num_seqs, cache->head_size, cache->num_kv_heads,
                         max_keys_of(max_seq_len, window > 0 ? window : 0, key_start), partition_size);
     if (p.c.nw > 1) p.chunk_bytes = (size_t)p.c.nw * 2 * num_heads * ((size_t)cache->head_size + 2) * sizeof(float);
     if (key_start > 0) {
-        p.prefix_chunks = cascade_prefix_chunks(num_seqs, num_heads / cache->num_kv_heads, cache->num_kv_heads, key_start);
+        const PrefixPlan pp = cascade_prefix_plan(num_seqs, num_heads / cache->num_kv_heads, cache->num_kv_heads, key_start);
+        p.prefix_chunks = pp.chunks;
+        p.prefix_mfma = pp.mfma;
         p.prefix_bytes = (size_t)p.prefix_chunks * num_seqs * num_heads * ((size_t)cache->head_size + 2) * sizeof(float);
     }
     return p;
@@ -239,6 +263,10 @@ static int prefill_args(const pa_cache_desc* cache, void* out, const void* query
     a.vnew = nullptr;
     a.slots = nullptr;
     a.alibi = alibi_slopes;
+    a.prefix_len = 0;
+    a.prefix_chunks = 0;
+    a.pre_o = nullptr;
+    a.pre_ml = nullptr;
     return PA_OK;
 }
 
@@ -360,6 +388,7 @@ static int decode_args(const pa_cache_desc* cache, void* out, const void* query,
     a.ws_ml = nullptr;
     a.key_start = key_start;
     a.prefix_chunks = 0;
+    a.prefix_mfma = 0;
     a.pre_o = nullptr;
     a.pre_ml = nullptr;
     if (a.c.dtype == PA_F32) return PA_OK;
@@ -378,6 +407,7 @@ static int decode_args(const pa_cache_desc* cache, void* out, const void* query,
     }
     if (p.prefix_bytes > 0) {
         a.prefix_chunks = p.prefix_chunks;
+        a.prefix_mfma = p.prefix_mfma ? 1 : 0;
         a.pre_o = (float*)((char*)workspace + p.chunk_bytes);
         a.pre_ml = a.pre_o + (size_t)p.prefix_chunks * num_seqs * num_heads * a.c.head_size;
     }

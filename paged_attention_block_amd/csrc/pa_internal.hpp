@@ -106,6 +106,13 @@ struct PrefillArgs {
     const void* vnew;
     const int32_t* slots;
     const float* alibi;  // [num_heads] ALiBi slopes, or null
+    // shared-prefix pass (the prefix instantiation only): the queries are the num_seqs x
+    // num_heads decode queries, the keys chunk c of [0, prefix_len) read through table row 0,
+    // no causal mask; each (chunk, query row, head) leaves its state in pre_o / pre_ml
+    int32_t prefix_len;
+    int32_t prefix_chunks;
+    float* pre_o;        // [prefix_chunks][num_seqs][H][D]
+    float* pre_ml;       // [prefix_chunks][num_seqs][H][2]
 };
 
 struct DecodeArgs {
@@ -130,6 +137,7 @@ struct DecodeArgs {
     // output; running max in log2 units and sum) the partition kernel folds in
     int32_t key_start;
     int32_t prefix_chunks;
+    int32_t prefix_mfma; // 1: the prefix pass runs on the prefill kernel, 0: the split-key kernel
     float* pre_o;        // [prefix_chunks][num_seqs][H][D]
     float* pre_ml;       // [prefix_chunks][num_seqs][H][2]
 };
@@ -143,6 +151,12 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t s);
 // Shared-prefix decode (bf16): prefix pass, then the partition (+ merge) kernels.
 hipError_t launch_cascade_decode_bf16(const DecodeArgs& a, hipStream_t s);
+// The prefix pass of shared-prefix decode on the prefill kernel: the decode queries of the
+// batch against the prefix chunks, states into a.pre_o / a.pre_ml.
+hipError_t launch_prefix_states(const DecodeArgs& a, hipStream_t s);
+// 64-key tiles of the prefill kernel's prefix pass per chunk, and its workgroups per chunk.
+int prefix_tiles(int prefix_len);
+int prefix_workgroups_per_chunk(int num_seqs, int group, int num_kv_heads);
 // Partition workgroups of the bf16 decode kernel that fit on the current device at once
 // (compute units x resident workgroups per unit); 256 when the device cannot be queried.
 int decode_resident_slots(int head_size, int num_kv_heads);

@@ -109,7 +109,15 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 // register-staged 8-byte load per lane, widened exactly to bf16 (every E4M3 value is a bf16
 // value) and written to the same swizzled LDS slot the bf16 copy fills, so the MFMA operand
 // reads are unchanged; kv_scale joins the softmax scale and the output normalisation.
-template <int D, int NBR, int BN, int NBUF, bool ALIBI, bool FP8>
+//
+// PREFIX: the shared-prefix pass of cascade decode.  The "sequence" is the batch's decode
+// queries (query[B][H][D] is a packed query block of B rows), the keys are chunk c of the
+// shared prefix [0, prefix_len) read through table row 0, every query sees every key of the
+// chunk (no causal diagonal; the chunk's last partial tile is masked at its end), and each
+// (chunk, row, head) leaves its unnormalised state (O, m, l) in pre_o / pre_ml instead of a
+// bf16 output row.  Work item numbering treats (chunk, KV head) as the (sequence, KV head)
+// index, so the q-tiles of one chunk and KV head share its K/V through one XCD's L2.
+template <int D, int NBR, int BN, int NBUF, bool ALIBI, bool FP8, bool PREFIX>
 __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const PrefillArgs a, const PrefillGrid pg) {
     constexpr int NGA = BN / 16;      // 16-key groups per K/V tile
     constexpr int NCC = BN / 32;      // 32-key chunks per K/V tile (PV MFMA k-steps)
@@ -148,20 +156,28 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const PrefillArgs 
     const int ti = pg.n_tiles - 1 - li % pg.n_tiles;
     const int qt = ti / pg.wgs_per_tile;
     const int jw = ti % pg.wgs_per_tile;
-    const int s = sg / a.c.num_kv_heads;
+    const int s = PREFIX ? 0 : sg / a.c.num_kv_heads;
     const int g = sg % a.c.num_kv_heads;
+    const int pc = PREFIX ? sg / a.c.num_kv_heads : 0;  // prefix chunk
     const int G = a.group;
 
-    const int q0 = a.cu_q[s];
-    const int sq = a.cu_q[s + 1] - q0;
+    const int q0 = PREFIX ? 0 : a.cu_q[s];
+    const int sq = PREFIX ? a.num_seqs : a.cu_q[s + 1] - q0;
     const int i0 = qt * 32 * pg.rb;
     // the rows of this workgroup's pairs: row blocks (4 jw) / G .. (4 jw + 3) / G
     const int wg_row0 = i0 + 32 * ((4 * jw) / G);
     if (wg_row0 >= sq) return;
     const int wg_row_end = min(i0 + 32 * ((4 * jw + 3) / G + 1), sq);
-    const int sk = a.cu_k[s + 1] - a.cu_k[s];
+    // PREFIX: chunk pc of the prefix = 64-key tiles [tb, te), keys [kc0, kc1)
+    int kc0 = 0, kc1 = 0;
+    if constexpr (PREFIX) {
+        const int pt = (a.prefix_len + BN - 1) / BN;
+        kc0 = BN * (int)((int64_t)pc * pt / a.prefix_chunks);
+        kc1 = min(a.prefix_len, BN * (int)((int64_t)(pc + 1) * pt / a.prefix_chunks));
+    }
+    const int sk = PREFIX ? kc1 : a.cu_k[s + 1] - a.cu_k[s];
     const int off = sk - sq;
-    const int W = a.window;
+    const int W = PREFIX ? 0 : a.window;
     const int rows_end = sq;
 
     const int tid = threadIdx.x;
@@ -178,16 +194,17 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const PrefillArgs 
     const int Hkv = a.c.num_kv_heads;
 
     // key range of the whole workgroup (union over its rows)
-    const int wg_lo = W > 0 ? max(0, off + wg_row0 - W + 1) : 0;
-    const int wg_hi = min(off + wg_row_end - 1, sk - 1);
+    const int wg_lo = PREFIX ? kc0 : (W > 0 ? max(0, off + wg_row0 - W + 1) : 0);
+    const int wg_hi = PREFIX ? kc1 - 1 : min(off + wg_row_end - 1, sk - 1);
     // this wave's rows and key range
     const int r0 = i0 + RPW * (pair / G);
     const int r_last = min(r0 + RPW - 1, rows_end - 1);
     const bool wave_active = wave_ok && r0 < rows_end;
-    const int wv_hi = min(off + r_last, sk - 1);
-    const int wv_lo = W > 0 ? max(0, off + r0 - W + 1) : 0;
-    const int wv_lo_max = W > 0 ? max(0, off + r_last - W + 1) : 0;
-    const int wv_p_min = off + r0;
+    // (PREFIX: every row sees keys [kc0, kc1); the mask then only cuts at kc1)
+    const int wv_hi = PREFIX ? kc1 - 1 : min(off + r_last, sk - 1);
+    const int wv_lo = PREFIX ? kc0 : (W > 0 ? max(0, off + r0 - W + 1) : 0);
+    const int wv_lo_max = PREFIX ? kc0 : (W > 0 ? max(0, off + r_last - W + 1) : 0);
+    const int wv_p_min = PREFIX ? kc1 - 1 : off + r0;
 
     const float c_log2 = a.scale * (FP8 ? a.c.kv_scale : 1.f) * 1.4426950408889634f;
     // ALiBi slope of this wave's head in log2 units (the bias slope * (j - p) is added to the
@@ -217,7 +234,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const PrefillArgs 
             const u32x4 x = src[4 * t + grp];
             qf[nb][t] = __builtin_bit_cast(bf16x8, ok ? x : (u32x4)(0u));
         }
-        prow[nb] = off + row;
+        prow[nb] = PREFIX ? kc1 - 1 : off + row;
         plo[nb] = W > 0 ? max(0, off + row - W + 1) : 0;
     }
 
@@ -270,7 +287,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const PrefillArgs 
     // the sequence's rows (rows past the last key are zeroed after the copy).
     const char* knew = (const char*)a.knew;
     const char* vnew = (const char*)a.vnew;
-    const bool fused = !FP8 && knew != nullptr;  // an FP8 cache is stored by its own kernel first
+    const bool fused = !FP8 && !PREFIX && knew != nullptr;  // an FP8 cache is stored by its own kernel first
     struct GroupSrc {
         const char* k;   // uniform base (non-mixed) of the group's first row, KV head 0
         const char* v;
@@ -609,6 +626,20 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const PrefillArgs 
 
     // ---------------------------------------------------------------- epilogue
     if (!wave_active) return;
+    if constexpr (PREFIX) {  // the chunk's state of each (row, head): O, running max, sum
+#pragma unroll
+        for (int nb = 0; nb < NBR; ++nb) {
+            const float lt = group4_sum(l_run[nb]);
+            const int row = r0 + 16 * nb + col;
+            if (row >= rows_end) continue;
+            const int64_t st = ((int64_t)pc * a.num_seqs + row) * H + h;
+            float* po = a.pre_o + st * D + 4 * grp;
+#pragma unroll
+            for (int d = 0; d < DB; ++d) *(f32x4*)(po + 16 * d) = oacc[d][nb];
+            if (grp == 0) *(f32x2*)(a.pre_ml + st * 2) = f32x2{m_run[nb], lt};
+        }
+        return;
+    }
 #pragma unroll
     for (int nb = 0; nb < NBR; ++nb) {
         const float lt = group4_sum(l_run[nb]);
@@ -643,7 +674,7 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t st) {
     const dim3 grid((unsigned)(nsg_pad * pg.n_tiles));
     const bool alibi = a.alibi != nullptr;
     const bool fp8 = a.c.dtype == 2;
-#define PA_PREFILL(DD, AL, F8) hipLaunchKernelGGL((prefill_bf16_kernel<DD, 2, kPrefillBN, kPrefillNBUF, AL, F8>), grid, dim3(256), 0, st, a, pg)
+#define PA_PREFILL(DD, AL, F8) hipLaunchKernelGGL((prefill_bf16_kernel<DD, 2, kPrefillBN, kPrefillNBUF, AL, F8, false>), grid, dim3(256), 0, st, a, pg)
     if (a.c.head_size == 128) {
         if (fp8) { if (alibi) PA_PREFILL(128, true, true); else PA_PREFILL(128, false, true); }
         else { if (alibi) PA_PREFILL(128, true, false); else PA_PREFILL(128, false, false); }
@@ -652,6 +683,59 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t st) {
         else { if (alibi) PA_PREFILL(64, true, false); else PA_PREFILL(64, false, false); }
     }
 #undef PA_PREFILL
+    return hipGetLastError();
+}
+
+// q-tile pairs of the prefill grid for group size G (rb row blocks of 32 per q-tile)
+static PrefillGrid prefix_grid(int num_seqs, int group, int num_kv_heads, int chunks) {
+    PrefillGrid pg;
+    pg.rb = (group % 4 == 0) ? 1 : (group % 2 == 0 ? 2 : 4);
+    pg.wgs_per_tile = group * pg.rb / 4;
+    pg.n_sg = chunks * num_kv_heads;
+    pg.n_tiles = (num_seqs + 32 * pg.rb - 1) / (32 * pg.rb) * pg.wgs_per_tile;
+    return pg;
+}
+
+int prefix_tiles(int prefix_len) { return (prefix_len + kPrefillBN - 1) / kPrefillBN; }
+
+int prefix_workgroups_per_chunk(int num_seqs, int group, int num_kv_heads) {
+    return prefix_grid(num_seqs, group, num_kv_heads, 1).n_tiles * num_kv_heads;
+}
+
+hipError_t launch_prefix_states(const DecodeArgs& d, hipStream_t st) {
+    PrefillArgs a;
+    a.c = d.c;
+    a.out = nullptr;
+    a.q = d.q;
+    a.table = d.table;  // row 0: the prefix blocks every row shares
+    a.max_blocks = d.max_blocks;
+    a.cu_q = nullptr;
+    a.cu_k = nullptr;
+    a.num_seqs = d.num_seqs;
+    a.max_seqlen_q = d.num_seqs;
+    a.num_heads = d.num_heads;
+    a.group = d.group;
+    a.scale = d.scale;
+    a.window = 0;
+    a.knew = nullptr;
+    a.vnew = nullptr;
+    a.slots = nullptr;
+    a.alibi = nullptr;
+    a.prefix_len = d.key_start;
+    a.prefix_chunks = d.prefix_chunks;
+    a.pre_o = d.pre_o;
+    a.pre_ml = d.pre_ml;
+    const PrefillGrid pg = prefix_grid(d.num_seqs, d.group, d.c.num_kv_heads, d.prefix_chunks);
+    const int64_t nsg_pad = ((int64_t)pg.n_sg + 7) / 8 * 8;
+    const dim3 grid((unsigned)(nsg_pad * pg.n_tiles));
+    const bool fp8 = a.c.dtype == 2;
+#define PA_PREFIX(DD, F8) hipLaunchKernelGGL((prefill_bf16_kernel<DD, 2, kPrefillBN, kPrefillNBUF, false, F8, true>), grid, dim3(256), 0, st, a, pg)
+    if (a.c.head_size == 128) {
+        if (fp8) PA_PREFIX(128, true); else PA_PREFIX(128, false);
+    } else {
+        if (fp8) PA_PREFIX(64, true); else PA_PREFIX(64, false);
+    }
+#undef PA_PREFIX
     return hipGetLastError();
 }
 

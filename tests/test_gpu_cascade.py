@@ -130,3 +130,56 @@ def test_shared_prefix_decode_full_size_sampled(part):
                                 wl.num_kv_heads, 0, picks)
     got = out.float().cpu().numpy()
     assert_close(np.stack([got[r, h] for r, h in picks]), ref, wl.dtype, f"shared prefix full p{part}")
+
+
+# With at least 512 (sequence, query head) rows per KV head the prefix pass runs on the
+# prefill kernel (64-key tiles, 32 rows per wave); the cases above have fewer rows and run
+# the split-key prefix kernel.
+MFMA_CASES = {
+    # name: (H, Hkv, D, BS, shared prefix, batch, context range)
+    "g4_d128_p80": (32, 8, 128, 16, 80, 160, (80, 300)),
+    "g5_d64_p128": (10, 2, 64, 32, 128, 110, (128, 400)),
+    "g8_d128_p1024": (16, 2, 128, 16, 1024, 64, (1024, 1300)),
+}
+
+
+@pytest.mark.parametrize("part", [0, 64])
+@pytest.mark.parametrize("name", sorted(MFMA_CASES))
+def test_cascade_decode_prefill_kernel_prefix(name, part):
+    H, Hkv, D, BS, P, B, (lo, hi) = MFMA_CASES[name]
+    assert B * (H // Hkv) >= 512
+    rng = np.random.default_rng(403)
+    ctxs = rng.integers(lo, hi + 1, size=B)
+    seqs = [W.SeqSpec(int(c), [1], ["decode"]) for c in ctxs]
+    wl = W.build(name, 403, seqs, num_heads=H, num_kv_heads=Hkv, head_size=D, block_size=BS,
+                 dtype=torch.bfloat16, shared_prefix=P)
+    run = GpuRun(wl, DEV)
+    store, dec = wl.phases[0]
+    run.run(store)
+    say(f"[cascade mfma prefix {name} p{part}] B {B} prefix {P}")
+    out = _cascade(run, dec, P, partition_size=part)
+    torch.cuda.synchronize()
+    vals = host_values(run.cache.cpu())
+    ref = oracle.cascade_decode(host_values(dec.query), vals, dec.block_table, dec.seq_lens, wl.scale,
+                                wl.num_kv_heads, P)
+    assert_close(out.float().cpu().numpy(), ref, wl.dtype, f"cascade mfma {name} p{part}")
+
+
+def test_shared_prefix_b256_p4096_sampled():
+    """The large shared-prefix batch (B 256, prefix 4096, contexts U[4096, 8192], H 32/8):
+    sampled rows against the plain decode definition."""
+    wl = W.shared_prefix_decode(num_seqs=256, prefix=4096, lo=4096, hi=8192)
+    run = GpuRun(wl, DEV)
+    store, dec = wl.phases[0]
+    run.run(store)
+    say("[cascade b256 p4096]")
+    out = _cascade(run, dec, 4096)
+    torch.cuda.synchronize()
+    vals = host_values(run.cache.cpu())
+    picks = sample_picks(dec, wl.num_heads, np.random.default_rng(404), n_random=24)[:160]
+    cu_q = np.arange(len(dec.seq_lens) + 1)
+    cu_k = np.concatenate([[0], np.cumsum(dec.seq_lens)])
+    ref = oracle.attention_rows(host_values(dec.query), vals, dec.block_table, cu_q, cu_k, wl.scale,
+                                wl.num_kv_heads, 0, picks)
+    got = out.float().cpu().numpy()
+    assert_close(np.stack([got[r, h] for r, h in picks]), ref, wl.dtype, "shared prefix b256")

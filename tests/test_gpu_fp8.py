@@ -246,3 +246,24 @@ def test_fp8_prefill_varlen_full_size_sampled():
                                 wl.scale, wl.num_kv_heads, 0, picks)
     got = out.float().cpu().numpy()
     assert_close(np.stack([got[r, h] for r, h in picks]), ref, torch.bfloat16, "fp8 prefill full")
+
+
+def test_fp8_cascade_decode_prefill_kernel_prefix():
+    """FP8 cache, 130 sequences x 4 query heads per KV head (the prefix pass on the prefill
+    kernel), prefix 192 keys."""
+    import paged_attention_block_amd as pa
+    P = 192
+    rng = np.random.default_rng(508)
+    ctxs = [int(c) for c in rng.integers(192, 500, size=130)]
+    wl = _fp8_decode_workload("fcm", 508, ctxs, 32, 8, 128, 16, shared_prefix=P)
+    run = GpuRun(wl, DEV)
+    run.kv_scale = 0.5
+    store, dec = wl.phases[0]
+    vals = _store_then(run, store, 0.5)
+    say("[fp8 cascade mfma prefix]")
+    out = pa.pa_cascade_decode(dec.query.to(DEV), run.cache, run.i32(dec.block_table), run.i32(dec.seq_lens),
+                               int(dec.max_seq_len), wl.scale, wl.num_kv_heads, P, kv_scale=0.5)
+    torch.cuda.synchronize()
+    ref = oracle.cascade_decode(host_values(dec.query), vals, dec.block_table, dec.seq_lens, wl.scale,
+                                wl.num_kv_heads, P)
+    assert_close(out.float().cpu().numpy(), ref, torch.bfloat16, "fp8 cascade mfma")
