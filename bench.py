@@ -17,7 +17,9 @@ Default run (one JSON line on stdout):
   * ``roofline`` per op: algorithmic bytes (decode) or FLOPs (prefill) of one launch over
     its mean duration, timed with HIP events on the stream the library launches on.
   * ``cpu_baseline``: the fp64 numpy oracle on the host, on a bounded sample of the same
-    workload, in the same unit.
+    workload, in the same unit (``cpu_baseline_1thread``: the decode one with one BLAS thread).
+  * ``config1``: the fp32 smoke workload (prefill step, then one decode step): times only,
+    the fp32 path makes no roofline claim.
   * ``fp8``: the headline decode step with the cache in FP8 (E4M3, kv_scale 1): half the
     K/V bytes.
   * ``shared_prefix``: decode of a batch whose sequences share a prefix of cached blocks,
@@ -54,7 +56,8 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CU x 4096 FLOP/clk x 2.4 GHz)
 METRIC = "paged decode HBM GB/s (% peak); varlen prefill bf16 TFLOP/s (% MFMA peak)"
 
-WORKLOAD_CONFIG = {"decode": 2, "prefill": 3, "chunked": 4, "chunked_decode": 4, "mixed": 5}
+WORKLOAD_CONFIG = {"decode": 2, "prefill": 3, "chunked": 4, "chunked_decode": 4, "mixed": 5,
+                   "smoke": 1, "smoke_decode": 1}
 
 
 # ----------------------------------------------------------------------------- algorithmic work
@@ -240,6 +243,11 @@ class Step:
         step_t = sum(evs[k][0].elapsed_time(evs[k][n_ops]) for k in range(steps)) / steps / 1e3
         per_op = [sum(evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(steps)) / steps / 1e3
                   for i in range(n_ops)]
+        # median and minimum of every op over the timed steps
+        self.op_stats = []
+        for i in range(n_ops):
+            ts = sorted(evs[k][i].elapsed_time(evs[k][i + 1]) / 1e3 for k in range(steps))
+            self.op_stats.append((ts[len(ts) // 2], ts[0]))
         return step_t, per_op, wall
 
 
@@ -255,8 +263,15 @@ def cpu_threads() -> int:
         return 1
 
 
-def cpu_baseline_decode(wl, op, budget_s: float = 10.0):
-    """Oracle decode of the sequences in order (wrapping around) until ~budget_s, in GB/s."""
+def cpu_baseline_decode(wl, op, budget_s: float = 10.0, threads: int = 0):
+    """Oracle decode of the sequences in order (wrapping around) until ~budget_s, in GB/s
+    (threads > 0: BLAS limited to that many threads)."""
+    if threads > 0:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=threads):
+            r = cpu_baseline_decode(wl, op, budget_s)
+        r["cores"] = threads
+        return r
     import oracle
     vals = wl.kv_cache.float().numpy()
     q = op.query.float().numpy()
@@ -386,7 +401,7 @@ def bench_workload(name, steps, warmup, dev, with_cpu, partition_size=0, flush_m
     shared = name in SHARED_PREFIX
     wl = _workload(name if shared or name == "fp8_decode" else WORKLOAD_CONFIG[name])
     prefix = SHARED_PREFIX[name][1] if shared else 0
-    phase = wl.phases[-1] if name == "chunked_decode" else wl.phases[0]
+    phase = wl.phases[-1] if name == "chunked_decode" else (wl.phases[1] if name == "smoke_decode" else wl.phases[0])
     step = Step(wl, phase, dev, partition_size, fused, alibi, prefix if cascade else 0)
     step_t, per_op, wall = step.time(steps, warmup, flush_mb * 1024 * 1024)
     ops = [d["op"] for d in step.prepared]
@@ -443,6 +458,9 @@ def bench_workload(name, steps, warmup, dev, with_cpu, partition_size=0, flush_m
             total_bytes += b
             res["ops"]["copy_blocks"] = {"ms": round(t * 1e3, 4), "GB/s": round(b / t / 1e9, 1), "bytes": b,
                                          "roofline": roofline(b / t / 1e9, HBM_PEAK_GBS, "GB/s", "hbm")}
+    for (med, lo), (opname, r) in zip(step.op_stats, res["ops"].items()):
+        r["ms_median"] = round(med * 1e3, 4)
+        r["ms_min"] = round(lo * 1e3, 4)
     res["step_GB/s"] = round(total_bytes / step_t / 1e9, 2)
     res["step_TFLOP/s"] = round(total_flops / step_t / 1e12, 3)
     if with_cpu:
@@ -504,6 +522,9 @@ def main() -> int:
                       "cache_eviction_MiB_per_step": args.flush_mb,
                       "wall_ms_per_step": main_res["wall_ms_per_step"]}
     line["cpu_baseline"] = main_res.get("cpu_baseline")
+    if with_cpu and args.workload == "decode":
+        wl2 = _workload(2)
+        line["cpu_baseline_1thread"] = cpu_baseline_decode(wl2, wl2.phases[0][-1], budget_s=5.0, threads=1)
     if args.workload == "decode" and not args.no_prefill:
         pre = bench_workload("prefill", max(10, args.steps // 2), max(3, args.warmup // 2), dev, with_cpu,
                              flush_mb=args.flush_mb)
@@ -525,6 +546,13 @@ def main() -> int:
         for name in ("decode", "prefill"):
             r = bench_workload(name, 20, 5, dev, False, flush_mb=args.flush_mb, alibi=True)
             line["alibi"][name] = {"workload": r["workload"], "ms_per_step": r["ms_per_step"], "ops": r["ops"]}
+        # config 1 (fp32 correctness path): times only
+        line["config1"] = {}
+        for name in ("smoke", "smoke_decode"):
+            r = bench_workload(name, 20, 5, dev, False, flush_mb=args.flush_mb)
+            for op in r["ops"].values():
+                op.pop("roofline", None)
+            line["config1"][name] = {"workload": r["workload"], "ms_per_step": r["ms_per_step"], "ops": r["ops"]}
         # the other two workloads, every op with its roofline (no CPU baseline): chunked prefill
         # with a 4096-key window and the decode after it (config 4), and the mixed step
         # copy_blocks -> store -> prefill -> decode (config 5)
