@@ -45,6 +45,7 @@ CASES = {
     "g16_d128_p512": (16, 1, 128, 16, 512, [512, 520, 900]),
     "g2_d128_hkv12_p128": (24, 12, 128, 16, 128, [128, 129, 400, 2000, 160]),
     "g4_d128_b1_p1024": (8, 2, 128, 16, 1024, [1500]),
+    "g4_d128_bs256_p512": (32, 8, 128, 256, 512, [512, 600, 1000, 2000]),
 }
 
 

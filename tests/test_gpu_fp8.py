@@ -92,6 +92,7 @@ DECODE_CASES = {
     "g4_d128": (32, 8, 128, 16, 0, [0, 4, 31, 32, 100, 700, 2000]),
     "g5_d128_window": (10, 2, 128, 16, 40, [0, 39, 41, 300]),
     "g8_d64": (16, 2, 64, 16, 0, [5, 64, 900]),
+    "g4_d64_bs256": (16, 4, 64, 256, 0, [0, 255, 256, 300, 1000]),
 }
 
 
@@ -183,6 +184,7 @@ PREFILL_CASES = {
     "g4_d128": (32, 8, 128, 16, 0, [(0, 1), (0, 37), (0, 200), (150, 90)]),
     "g5_d128_window": (10, 2, 128, 16, 70, [(0, 130), (300, 64), (20, 5)]),
     "g8_d64_chunked": (16, 2, 64, 32, 0, [(64, 100), (1000, 33)]),
+    "g4_d128_bs256": (16, 4, 128, 256, 0, [(0, 300), (500, 70)]),
 }
 
 

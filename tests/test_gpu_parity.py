@@ -264,7 +264,7 @@ def test_block_relabelling_and_block_size_give_bitwise_identical_outputs(window)
     wl = W.build("perm", 400, seqs, num_heads=16, num_kv_heads=4, head_size=128, block_size=16,
                  dtype=torch.bfloat16, sliding_window=window)
     base = _run_all(wl, 64)
-    for bs, seed in ((16, 1), (32, 2), (64, 3)):
+    for bs, seed in ((16, 1), (32, 2), (64, 3), (128, 4), (256, 5)):  # up to the largest block size
         other = _run_all(relayout(wl, bs, seed), 64)
         assert len(other) == len(base)
         for a, b in zip(base, other):
