@@ -1,7 +1,7 @@
 /*
  * pa.h — C ABI of the paged-attention library (libpa.so) for AMD Instinct MI355X (gfx950).
  *
- * Three operations on a paged, block-structured KV cache, plus block copies:
+ * Attention over a paged, block-structured KV cache, and the cache operations around it:
  *   pa_store_kv        scatter new keys/values into cache slots (slot_mapping)
  *   pa_copy_blocks     duplicate physical blocks of both cache planes
  *   pa_prefill_varlen  varlen causal attention (chunked, optional sliding window)
@@ -9,6 +9,8 @@
  *   pa_prefill_varlen_with_store, pa_decode_with_store
  *                      the store of the new tokens and the attention in one call
  *   pa_cascade_decode  decode of a batch that shares a prefix of cached blocks
+ * Options: ALiBi slopes (alibi_slopes arguments) and an FP8 (E4M3) cache with a kv_scale
+ * (pa_cache_desc.dtype / kv_scale).
  *
  * Conventions shared by every entry point
  *   - All tensor arguments are DEVICE pointers, caller-allocated and caller-owned; the
