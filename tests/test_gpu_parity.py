@@ -139,6 +139,8 @@ PREFILL_CASES = {
     "g2_d64_rows64": (4, 2, 64, 32, 0, torch.bfloat16, [(0, 100), (33, 66)]),
     "g3_d128": (6, 2, 128, 16, 9, torch.bfloat16, [(10, 80)]),
     "g16_d128_headchunks": (16, 1, 128, 16, 0, torch.bfloat16, [(0, 90), (64, 40)]),
+    "g16_d64": (16, 1, 64, 16, 0, torch.bfloat16, [(0, 100), (30, 33)]),
+    "g2_d128_hkv12": (24, 12, 128, 16, 0, torch.bfloat16, [(0, 70), (100, 40)]),
     "f32_d64": (4, 2, 64, 16, 0, torch.float32, [(0, 5), (0, 13), (9, 20)]),
     "f32_d128_window": (6, 3, 128, 8, 6, torch.float32, [(0, 19), (30, 7)]),
 }
@@ -240,6 +242,19 @@ def test_prefill_zero_length_sequence_in_batch():
     pre.block_table = np.ascontiguousarray(wl.tables[[0, 1, 2], :pre.block_table.shape[1]])
     run = GpuRun(wl, DEV)
     _check_phase(run, [store, pre], bits(wl.kv_cache), label="zero-length prefill")
+
+
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
+def test_prefill_more_queries_than_keys(dt):
+    """seqlen_q > seqlen_k (reading c4): row i sits at p = seqlen_k - seqlen_q + i; rows with
+    p < 0 see no key and are written as zeros, the others attend keys [0, p]."""
+    seqs = [W.SeqSpec(0, [40], ["prefill"]), W.SeqSpec(0, [70], ["prefill"])]
+    wl = W.build("sq_gt_sk", 302, seqs, num_heads=8, num_kv_heads=2, head_size=128, block_size=16, dtype=dt)
+    store, pre = wl.phases[0]
+    pre.cu_seqlens_k = np.array([0, 40, 90], dtype=np.int32)   # the second sequence: 50 keys, 70 rows
+    pre.max_seqlen_k = 50
+    run = GpuRun(wl, DEV)
+    _check_phase(run, [store, pre], bits(wl.kv_cache), label=f"sq > sk {dt}")
 
 
 # ----------------------------------------------------------------------------- invariants on the GPU
