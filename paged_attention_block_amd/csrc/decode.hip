@@ -25,6 +25,8 @@
 //   each lane owns DPL*4 consecutive dims of one head.
 #include <math.h>
 
+#include <atomic>
+
 #include "pa_internal.hpp"
 
 namespace pa {
@@ -723,10 +725,10 @@ __global__ __launch_bounds__(64 * MW) void decode_merge_kernel(const DecodeArgs 
 }
 
 int decode_resident_slots(int head_size, int num_kv_heads) {
-    // per device: compute units, and resident workgroups per unit for each (head size,
-    // waves per workgroup); 0 = not yet queried
-    static int cus[64];
-    static int per_cu[64][2][9];
+    // per device and (head size, waves per workgroup): compute units x resident workgroups per
+    // unit, 0 = not yet queried.  Relaxed atomics: concurrent first calls from several host
+    // threads may each query, and all store the same value.
+    static std::atomic<int> slots[64][2][9];
     const int waves = num_kv_heads < 8 ? num_kv_heads : 8;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64 || waves < 1) {
@@ -734,7 +736,8 @@ int decode_resident_slots(int head_size, int num_kv_heads) {
         return 256;
     }
     const int di = head_size == 128 ? 1 : 0;
-    if (cus[dev] == 0 || per_cu[dev][di][waves] == 0) {
+    int v = slots[dev][di][waves].load(std::memory_order_relaxed);
+    if (v == 0) {
         int ncu = 0, nb = 0;
         hipError_t e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
         if (e == hipSuccess)
@@ -745,10 +748,10 @@ int decode_resident_slots(int head_size, int num_kv_heads) {
             (void)hipGetLastError();
             return 256;
         }
-        cus[dev] = ncu;
-        per_cu[dev][di][waves] = nb;
+        v = ncu * nb;
+        slots[dev][di][waves].store(v, std::memory_order_relaxed);
     }
-    return cus[dev] * per_cu[dev][di][waves];
+    return v;
 }
 
 // Partition kernel (+ merge kernel when the batch is cut into more than one chunk).
