@@ -17,7 +17,8 @@ Default run (one JSON line on stdout):
   * ``roofline`` per op: algorithmic bytes (decode) or FLOPs (prefill) of one launch over
     its mean duration, timed with HIP events on the stream the library launches on.
   * ``cpu_baseline``: the fp64 numpy oracle on the host, on a bounded sample of the same
-    workload, in the same unit (``cpu_baseline_1thread``: the decode one with one BLAS thread).
+    workload, in the same unit (``cpu_baseline_1thread``: the decode one with one BLAS thread;
+    ``config1.cpu_baseline_1thread``: the fp32 smoke workload's calls on one thread).
   * ``config1``: the fp32 smoke workload (prefill step, then one decode step): times only,
     the fp32 path makes no roofline claim.
   * ``fp8``: the headline decode step with the cache in FP8 (E4M3, kv_scale 1): half the
@@ -325,6 +326,37 @@ def cpu_baseline_prefill(wl, op, budget_s: float = 10.0):
                       f"({flops / 1e9:.1f} GFLOP algorithmic, {t_used:.1f} s)"}
 
 
+def cpu_config1_1thread(budget_s: float = 2.0):
+    """Oracle times of the fp32 smoke workload's attention calls with one BLAS thread: the
+    prefill of both prompts, and one decode step (ms per call, mean over repeats)."""
+    import workloads as W
+    import oracle
+    from threadpoolctl import threadpool_limits
+    wl = W.config(1)
+    vals = wl.kv_cache.double().numpy()
+    pre = [op for op in wl.phases[0] if isinstance(op, W.PrefillOp)][0]
+    dec = [op for op in wl.phases[1] if isinstance(op, W.DecodeOp)][0]
+    calls = {
+        "prefill": lambda: oracle.prefill_varlen(pre.query.double().numpy(), vals, pre.block_table, pre.cu_seqlens_q,
+                                                 pre.cu_seqlens_k, wl.scale, wl.num_kv_heads, wl.sliding_window),
+        "decode": lambda: oracle.decode(dec.query.double().numpy(), vals, dec.block_table, dec.seq_lens, wl.scale,
+                                        wl.num_kv_heads, wl.sliding_window),
+    }
+    out = {}
+    with threadpool_limits(limits=1):
+        for name, fn in calls.items():
+            n, t_used = 0, 0.0
+            while t_used < budget_s / len(calls) or n < 3:
+                t0 = time.perf_counter()
+                fn()
+                t_used += time.perf_counter() - t0
+                n += 1
+            out[name] = {"ms": round(1e3 * t_used / n, 4), "calls": n}
+    return {"ops": out, "cores": 1, "kind": "oracle",
+            "sample": "fp64 numpy oracle, one BLAS thread: the prefill of the two prompts (5 and 13 tokens) "
+                      "and the first decode step, each repeated"}
+
+
 # ----------------------------------------------------------------------------- traffic (PMC)
 
 
@@ -553,6 +585,8 @@ def main() -> int:
             for op in r["ops"].values():
                 op.pop("roofline", None)
             line["config1"][name] = {"workload": r["workload"], "ms_per_step": r["ms_per_step"], "ops": r["ops"]}
+        if with_cpu:
+            line["config1"]["cpu_baseline_1thread"] = cpu_config1_1thread()
         # the other two workloads, every op with its roofline (no CPU baseline): chunked prefill
         # with a 4096-key window and the decode after it (config 4), and the mixed step
         # copy_blocks -> store -> prefill -> decode (config 5)
