@@ -250,6 +250,11 @@ size_t pa_cascade_decode_workspace_size(const pa_cache_desc* cache, int32_t num_
  * physical blocks; the prefix is read through row 0.
  * Runs the prefix kernel, then the partition (+ merge) kernels of pa_decode on the keys
  * after the prefix, whose first piece of each sequence starts from the prefix's state.
+ * When it pays: the saving is the prefix's re-reads, which the device's last-level cache
+ * (256 MB) already serves cheaply for short prefixes.  Measured on MI355X (32/8 heads, head
+ * size 128, bf16, own keys U[0, 3072]): cascade beats pa_decode for prefixes of 4096 keys
+ * from 16 sequences, 2048 keys from 64, 1024 keys only at 256; with 512-key prefixes pa_decode
+ * is faster up to 256 sequences.  Both give the same attention, so a caller may pick by that.
  */
 int pa_cascade_decode(const pa_cache_desc* cache, void* out, const void* query,
                       const int32_t* block_table, int32_t max_blocks_per_seq,
