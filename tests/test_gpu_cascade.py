@@ -184,3 +184,35 @@ def test_shared_prefix_b256_p4096_sampled():
                                 wl.num_kv_heads, 0, picks)
     got = out.float().cpu().numpy()
     assert_close(np.stack([got[r, h] for r, h in picks]), ref, wl.dtype, "shared prefix b256")
+
+
+def test_cascade_empty_batch_and_all_context_shared():
+    """An empty batch is a no-op; a batch whose every context is exactly the shared prefix (no
+    own key anywhere: the own-keys pass has no step) gets the prefix attention alone, on both
+    prefix passes (split-key at B 6, the prefill kernel at B 160 x G 4 rows)."""
+    import paged_attention_block_amd as pa
+    wl = W.build("e0", 404, [W.SeqSpec(64, [1], ["decode"])], num_heads=8, num_kv_heads=2, head_size=128,
+                 block_size=16, dtype=torch.bfloat16, shared_prefix=64)
+    run = GpuRun(wl, DEV)
+    say("[cascade empty batch]")
+    q0 = torch.empty((0, 8, 128), dtype=torch.bfloat16, device=DEV)
+    out0 = pa.pa_cascade_decode(q0, run.cache, torch.zeros((0, 4), dtype=torch.int32, device=DEV),
+                                torch.zeros((0,), dtype=torch.int32, device=DEV), 0, wl.scale, wl.num_kv_heads, 64)
+    torch.cuda.synchronize()
+    assert out0.shape == (0, 8, 128)
+    for B, P in ((6, 256), (160, 512)):
+        seqs = [W.SeqSpec(P - 1, [1], ["decode"]) for _ in range(B)]
+        wl = W.build(f"allshared{B}", 405, seqs, num_heads=32, num_kv_heads=8, head_size=128, block_size=16,
+                     dtype=torch.bfloat16, shared_prefix=P - 16)
+        run = GpuRun(wl, DEV)
+        store, dec = wl.phases[0]
+        run.run(store)
+        lens = np.full(B, P - 16, dtype=np.int32)  # every context = the shared blocks only
+        for part in (0, 64):
+            say(f"[cascade all shared B {B} P {P - 16} p{part}]")
+            out = _cascade(run, dec, P - 16, lens=lens, partition_size=part)
+            torch.cuda.synchronize()
+            vals = host_values(run.cache.cpu())
+            ref = oracle.cascade_decode(host_values(dec.query), vals, dec.block_table, lens, wl.scale,
+                                        wl.num_kv_heads, P - 16)
+            assert_close(out.float().cpu().numpy(), ref, wl.dtype, f"all shared B {B} p{part}")
