@@ -569,6 +569,16 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const PrefillArgs 
                 const bf16x8 kf = *(const bf16x8*)(kt + kw[t] + 32 * b * D * 2);
                 sw[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qw[t], sw[b], 0, 0, 0);
             }
+        // operand reads well ahead of their MFMAs (the default order issued them one or two
+        // MFMAs ahead, less than the LDS latency): eight first, then one per MFMA
+        constexpr int NR = 2 * (D / 16);
+#pragma unroll
+        for (int r = 0; r < 8; ++r) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+        for (int m = 0; m < NR; ++m) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (m + 8 < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
     };
     // mask, online softmax of the lane's row, P^T packed straight from the accumulators: the
     // B operand of 16-key step (b, sg) is accumulator values 8 sg .. 8 sg + 7 of block b
