@@ -660,6 +660,16 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const PrefillArgs 
                     ow[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, __builtin_bit_cast(bf16x8, pw[b][sg]), ow[c], 0, 0, 0);
                 }
             }
+        // V operand reads ahead of their MFMAs as for K: eight first (four MFMAs' worth), then two
+        // per MFMA
+        constexpr int NM = 4 * (D / 32);
+#pragma unroll
+        for (int r = 0; r < 8; ++r) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (m + 4 < NM) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
     };
 
     // ---------------------------------------------------------------- fused store
