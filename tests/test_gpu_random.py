@@ -4,7 +4,8 @@ checked too (group sizes 1-16, head size 64/128, block sizes 1-256, windows, chu
 offsets, ALiBi, FP8 caches with a kv_scale, the fused store, decode partition sizes), against
 the oracle on every output element and every cache byte.  (2) Shared-prefix (cascade) decode at
 random prefix lengths, batches on both sides of the prefix-pass switch, bf16 and FP8 caches,
-against the oracle's cascade decode."""
+against the oracle's cascade decode.  (3) Large prefill chunks (256-2048 rows over contexts up to
+8192 keys) on sampled rows."""
 
 from __future__ import annotations
 
@@ -191,3 +192,54 @@ def test_random_cascade(seed):
                                 wl.num_kv_heads, P)
     err = assert_close(out.float().cpu().numpy(), ref, torch.bfloat16, f"random cascade {seed}")
     say(f"[random cascade {seed}] max abs err {err:.3e}")
+
+
+N_LARGE = int(os.environ.get("PA_RANDOM_LARGE_CASES", "16"))
+
+
+def draw_large(seed: int) -> dict:
+    """Sweep case ``seed`` of large prefill chunks (host logic, deterministic)."""
+    rng = np.random.default_rng(7000 + seed)
+    G = int(rng.choice([1, 2, 4, 5, 8]))
+    Hkv = int(rng.choice([1, 2, 8])) if G < 8 else int(rng.choice([1, 2]))
+    B = int(rng.integers(1, 5))
+    seqs = [(int(rng.integers(0, 8193)) if rng.random() < 0.6 else 0, int(rng.integers(256, 2049))) for _ in range(B)]
+    return {"seed": seed, "G": G, "Hkv": Hkv, "H": G * Hkv, "D": int(rng.choice([64, 128])),
+            "BS": int(rng.choice([16, 64, 256])), "window": int(rng.choice([0, 0, 1024, 4096])),
+            "seqs": seqs, "fp8": bool(rng.random() < 0.25), "alibi": bool(rng.random() < 0.25),
+            "kv_scale": 0.5}
+
+
+@pytest.mark.parametrize("seed", range(N_LARGE))
+def test_random_large_prefill_sampled(seed):
+    """Chunks of 256-2048 rows over contexts up to 8192 keys: many q-tiles and key tiles per
+    sequence; sampled rows (tile edges, first/last rows, random) against the oracle."""
+    from tests.gpu_helpers import sample_picks
+    c = draw_large(seed)
+    say(f"[random large {seed}] H {c['H']}/{c['Hkv']} D {c['D']} BS {c['BS']} W {c['window']} fp8 {c['fp8']} "
+        f"alibi {c['alibi']} seqs {c['seqs']}")
+    specs = [W.SeqSpec(ctx, [q], ["prefill"]) for ctx, q in c["seqs"]]
+    wl = W.build(f"rlarge{seed}", 4000 + seed, specs, num_heads=c["H"], num_kv_heads=c["Hkv"], head_size=c["D"],
+                 block_size=c["BS"], dtype=torch.bfloat16, sliding_window=c["window"],
+                 cache_dtype=F8 if c["fp8"] else None)
+    run = GpuRun(wl, DEV)
+    if c["fp8"]:
+        run.kv_scale = c["kv_scale"]
+    if c["alibi"]:
+        run.alibi = np.array([2.0 ** (-8.0 * (i + 1) / c["H"]) for i in range(c["H"])])
+    store, op = wl.phases[0]
+    before = bits(wl.kv_cache)
+    run.run(store)
+    out = run.run(op)
+    torch.cuda.synchronize()
+    if c["fp8"]:
+        vals = fp8.dequantize(fp8.store_kv_fp8(before, store.key.float().numpy(), store.value.float().numpy(),
+                                               store.slot_mapping, c["kv_scale"]), c["kv_scale"])
+    else:
+        vals = host_values(run.cache.cpu())
+    picks = sample_picks(op, wl.num_heads, np.random.default_rng(seed), n_random=64)
+    ref = oracle.attention_rows(host_values(op.query), vals, op.block_table, op.cu_seqlens_q, op.cu_seqlens_k,
+                                wl.scale, wl.num_kv_heads, wl.sliding_window, picks, run.alibi)
+    got = out.float().cpu().numpy()
+    err = assert_close(np.stack([got[r, h] for r, h in picks]), ref, torch.bfloat16, f"random large {seed}")
+    say(f"[random large {seed}] {len(picks)} rows, max abs err {err:.3e}")
