@@ -194,3 +194,20 @@ def test_fp8_cache_checks(lib):
     assert lib.pa_cascade_decode_workspace_size(d8, 64, 32, 4097, 1024, 0) == lib.pa_cascade_decode_workspace_size(b8, 64, 32, 4097, 1024, 0)
     # bf16-kernel limits apply: block_size >= 16
     assert lib.pa_decode(desc(bs=8, dtype=2, kv_scale=1.0), FAKE, FAKE, FAKE, 4, FAKE, 2, 30, 4, 0.1, 0, None, 0, FAKE, 1 << 20, None) == 2
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """Without libpa.so every entry point raises (no CPU or oracle fallback on the product path)."""
+    import torch
+    import paged_attention_block_amd as pa
+    monkeypatch.setattr(pa, "_lib", None)
+    monkeypatch.setattr(pa, "lib_path", lambda: str(tmp_path / "libpa.so"))
+    with pytest.raises(RuntimeError, match="is missing"):
+        pa.load()
+    cache = torch.zeros((2, 4, 16, 2, 64), dtype=torch.bfloat16)
+    key = torch.zeros((3, 2, 64), dtype=torch.bfloat16)
+    with pytest.raises(RuntimeError, match="is missing"):
+        pa.pa_store_kv(key, key, cache, torch.zeros(3, dtype=torch.int32))
+    with pytest.raises(RuntimeError, match="is missing"):
+        pa.pa_decode(torch.zeros((1, 4, 64), dtype=torch.bfloat16), cache, torch.zeros((1, 4), dtype=torch.int32),
+                     torch.ones(1, dtype=torch.int32), 1, 0.125, 2)
