@@ -12,8 +12,9 @@ Default run (one JSON line on stdout):
   * ``prefill``: varlen causal prefill, 16 prompts of U[128, 2048] tokens, same heads;
     one step = store every prompt token, then prefill.  TFLOP/s of algorithmic FLOPs.
   * ``secondary``: chunked prefill of 512-token chunks over long contexts with a 4096-key
-    window and the decode after it (config 4), and the mixed step copy_blocks -> store ->
-    prefill -> decode (config 5); every op with its roofline.
+    window and the decode after it (8 sequences, contexts U[4096, 32768], H 40/8), and the mixed
+    step copy_blocks -> store -> prefill -> decode (4 chunks + 252 decodes, H 64/8); every op
+    with its roofline.
   * ``roofline`` per op: algorithmic bytes (decode) or FLOPs (prefill) of one launch over
     its mean duration, timed with HIP events on the stream the library launches on.
   * ``cpu_baseline``: the fp64 numpy oracle on the host, on a bounded sample of the same
@@ -416,7 +417,7 @@ def _workload(n):
     import torch
     import workloads as W
     if n == "fp8_decode":
-        # the config-2 sequences with an FP8 cache
+        # the headline decode sequences (B 64, contexts U[512, 4096]) with an FP8 cache
         c2 = W.config(2)
         return W.build("config2_fp8", 2, c2.seqs, num_heads=c2.num_heads, num_kv_heads=c2.num_kv_heads,
                        head_size=c2.head_size, block_size=c2.block_size, dtype=torch.bfloat16,
@@ -517,7 +518,7 @@ def main() -> int:
                          "reference kernel for scaling HBM byte counters")
     ap.add_argument("--no-prefill", action="store_true", help="skip the secondary prefill measurement")
     ap.add_argument("--no-secondary", action="store_true",
-                    help="skip the chunked-prefill (config 4) and mixed-step (config 5) measurements")
+                    help="skip the chunked-prefill and mixed-step measurements")
     ap.add_argument("--flush-mb", type=int, default=1024,
                     help="untimed read of this many MiB before every step to evict the caches (0 = off)")
     args = ap.parse_args()
@@ -578,7 +579,7 @@ def main() -> int:
         for name in ("decode", "prefill"):
             r = bench_workload(name, 20, 5, dev, False, flush_mb=args.flush_mb, alibi=True)
             line["alibi"][name] = {"workload": r["workload"], "ms_per_step": r["ms_per_step"], "ops": r["ops"]}
-        # config 1 (fp32 correctness path): times only
+        # the fp32 smoke workload (correctness path): times only
         line["config1"] = {}
         for name in ("smoke", "smoke_decode"):
             r = bench_workload(name, 20, 5, dev, False, flush_mb=args.flush_mb)
@@ -588,8 +589,8 @@ def main() -> int:
         if with_cpu:
             line["config1"]["cpu_baseline_1thread"] = cpu_config1_1thread()
         # the other two workloads, every op with its roofline (no CPU baseline): chunked prefill
-        # with a 4096-key window and the decode after it (config 4), and the mixed step
-        # copy_blocks -> store -> prefill -> decode (config 5)
+        # with a 4096-key window and the decode after it, and the mixed step
+        # copy_blocks -> store -> prefill -> decode
         # the headline decode step over an FP8 cache
         r = bench_workload("fp8_decode", 30, 5, dev, False, flush_mb=args.flush_mb)
         line["fp8"] = {"workload": r["workload"], "ms_per_step": r["ms_per_step"], "step_GB/s": r["step_GB/s"],

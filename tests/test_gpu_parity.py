@@ -416,7 +416,8 @@ def test_config1_fp32_all_phases_with_store():
 
 @pytest.mark.parametrize("n", [3, 4, 5])
 def test_config_with_store_sampled(n):
-    """Configs 3-5 with every store fused into its attention call (config 4: both phases)."""
+    """The causal, chunked-window and mixed workloads with every store fused into its attention
+    call (the chunked-window one: both its prefill and its decode phase)."""
     wl = _config(n)
     run = GpuRun(wl, DEV)
     ref = bits(wl.kv_cache)
