@@ -213,8 +213,11 @@ int pa_decode(const pa_cache_desc* cache, void* out, const void* query,
  * pa_decode_with_store — pa_store_kv of each sequence's new token, then pa_decode, as one
  * call (same source as pa_prefill_varlen_with_store).  key, value [num_seqs][num_kv_heads]
  * [head_size] and slot_mapping [num_seqs]: the token just produced by each sequence, which
- * seq_lens already counts.  Other arguments as pa_decode.  Runs the store kernel and the decode
- * kernels back to back on the stream.
+ * seq_lens already counts.  Other arguments as pa_decode.  With a bf16 cache it is one partition
+ * launch (plus the merge): the workgroup holding a sequence's last key takes that key's K/V from
+ * key/value rather than the cache, and writes the rows to slot_mapping[s] (negative: not written;
+ * the attention still uses the given rows, as pa_prefill_varlen_with_store does).  With a float32
+ * or FP8 cache the store kernel runs first, then the decode kernels.
  */
 int pa_decode_with_store(const pa_cache_desc* cache, void* out, const void* query, const void* key,
                          const void* value, const int32_t* slot_mapping, const int32_t* block_table,

@@ -132,6 +132,43 @@ __device__ __forceinline__ void load_step(int k0, int kb, int ke, const int32_t*
     }
 }
 
+// load_step for the step holding a sequence's new token (key kn) when the store is fused: the
+// lanes whose K or V row is that key read it from the caller's row (knew_row / vnew_row: KV head
+// g's D elements) instead of the cache slot, which the store has not written yet.  bf16 only.
+template <int D>
+__device__ __forceinline__ void load_step_new(int k0, int kb, int ke, const int32_t* __restrict__ table,
+                                              int shift, int BS, int64_t row_elems, int g,
+                                              const char* __restrict__ kplane,
+                                              const char* __restrict__ vplane, uint32_t k_off,
+                                              uint32_t v_off, uint32_t row_bytes, int col, int grp, int kn,
+                                              const char* knew_row, const char* vnew_row,
+                                              u32x4 (&kr)[2][D / 32], typename VRow<D>::T (&vr)[8]) {
+    int64_t gb[2];
+    bool gv[2];
+#pragma unroll
+    for (int ga = 0; ga < 2; ++ga) {
+        const int j0 = k0 + 16 * ga;
+        gv[ga] = (j0 < ke) && (j0 + 16 > kb);
+        const int blk = gv[ga] ? table[j0 >> shift] : 0;
+        gb[ga] = (((int64_t)blk * BS + (j0 & (BS - 1))) * row_elems + (int64_t)g * D) * 2;
+    }
+    if (!gv[0]) gb[0] = gb[1];
+    if (!gv[1]) gb[1] = gb[0];
+#pragma unroll
+    for (int ga = 0; ga < 2; ++ga) {
+        const char* p = (k0 + 16 * ga + col == kn) ? knew_row + 16 * grp : kplane + gb[ga] + k_off;
+#pragma unroll
+        for (int t = 0; t < D / 32; ++t) kr[ga][t] = *(const u32x4*)(p + 64 * t);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int key = k0 + 16 * (j >> 2) + 4 * grp + (j & 3);
+        const char* p = key == kn ? vnew_row + 2 * (D / 16) * col
+                                  : vplane + gb[j >> 2] + (int64_t)(j & 3) * row_bytes + v_off;
+        vr[j] = *(const typename VRow<D>::T*)p;
+    }
+}
+
 // FP8 step registers widened to the bf16 layout the MFMAs take.
 template <int D>
 __device__ __forceinline__ void widen_step(const u32x2 (&k8)[2][D / 32], const typename VRow8<D>::T (&v8)[8],
@@ -329,8 +366,9 @@ __device__ __forceinline__ void fold_prefix(const DecodeArgs& a, int s, int head
 // CASCADE: shared-prefix decode.  Every sequence's steps then start at key_start, the first
 // piece of a sequence folds the prefix's state into its own, and a sequence with no own key
 // writes the prefix's result.
-template <int D, bool ALIBI, bool CASCADE, bool FP8>
+template <int D, bool ALIBI, bool CASCADE, bool FP8, bool FUSED>
 __global__ __launch_bounds__(512) void decode_bf16_kernel(const DecodeArgs a) {
+    static_assert(!FUSED || (!FP8 && !CASCADE), "the fused store serves the plain bf16 decode");
     constexpr int KS = D / 32;   // k-slices of q.K^T
     constexpr int DPL = D / 16;  // dims per lane chunk of a V row = PV MFMAs per step
 
@@ -423,6 +461,11 @@ __global__ __launch_bounds__(512) void decode_bf16_kernel(const DecodeArgs a) {
             const int kb = step_begin > lo ? step_begin : lo;  // first live key of the segment
             const int ke = min(n, base + 32 * le);             // one past the last
             const int32_t* __restrict__ table = a.table + (int64_t)s * a.max_blocks;
+            // fused store: this workgroup holds the sequence's last step (the new token's key)
+            const bool new_here = FUSED && le == steps;
+            const int k_last = base + 32 * (steps - 1);
+            const char* knew_row = FUSED ? (const char*)a.knew + ((int64_t)s * Hkv + g) * D * 2 : nullptr;
+            const char* vnew_row = FUSED ? (const char*)a.vnew + ((int64_t)s * Hkv + g) * D * 2 : nullptr;
 
             // Q^T operand: head col, the dims of k-slice t (q_slice)
             bf16x8 qf[KS];
@@ -450,21 +493,41 @@ __global__ __launch_bounds__(512) void decode_bf16_kernel(const DecodeArgs a) {
             typename StepT<D, FP8>::K kA[2][KS], kB[2][KS];
             typename StepT<D, FP8>::V vA[8], vB[8];
             int k0 = step_begin;
-            load_step<D, FP8>(k0, kb, ke, table, shift, BS, row_elems, g, kplane, vplane, k_off, v_off, row_bytes, kA, vA);
+            auto ld = [&](int k, auto& kr, auto& vr) {
+                if constexpr (FUSED) {
+                    if (new_here && k == k_last) {
+                        load_step_new<D>(k, kb, ke, table, shift, BS, row_elems, g, kplane, vplane, k_off, v_off,
+                                         row_bytes, col, grp, n - 1, knew_row, vnew_row, kr, vr);
+                        return;
+                    }
+                }
+                load_step<D, FP8>(k, kb, ke, table, shift, BS, row_elems, g, kplane, vplane, k_off, v_off, row_bytes, kr, vr);
+            };
+            ld(k0, kA, vA);
             while (true) {
                 __syncthreads();
                 const int n1 = k0 + 32 < ke ? k0 + 32 : k0;
-                load_step<D, FP8>(n1, kb, ke, table, shift, BS, row_elems, g, kplane, vplane, k_off, v_off, row_bytes, kB, vB);
+                ld(n1, kB, vB);
                 compute_step<D, ALIBI, FP8>(k0, kb, ke, grp, c_log2, sl2, n - 1, qf, kA, vA, oacc, m_run, l_run);
                 k0 += 32;
                 if (k0 >= ke) break;
                 const int n2 = k0 + 32 < ke ? k0 + 32 : k0;
-                load_step<D, FP8>(n2, kb, ke, table, shift, BS, row_elems, g, kplane, vplane, k_off, v_off, row_bytes, kA, vA);
+                ld(n2, kA, vA);
                 compute_step<D, ALIBI, FP8>(k0, kb, ke, grp, c_log2, sl2, n - 1, qf, kB, vB, oacc, m_run, l_run);
                 k0 += 32;
                 if (k0 >= ke) break;
             }
 
+            if constexpr (FUSED) {  // the new token's rows into its cache slot (KV head g's part)
+                if (new_here && wave_ok && lane < D / 8) {
+                    const int slot = a.slots[s];
+                    if (slot >= 0) {
+                        const int64_t dst = ((int64_t)slot * Hkv + g) * D * 2 + 16 * lane;
+                        *(u32x4*)((char*)a.c.kv + dst) = *(const u32x4*)(knew_row + 16 * lane);
+                        *(u32x4*)((char*)a.c.kv + a.c.plane_elems * 2 + dst) = *(const u32x4*)(vnew_row + 16 * lane);
+                    }
+                }
+            }
             if constexpr (CASCADE) {  // the sequence's first piece also holds the prefix
                 if (ls == 0) fold_prefix<D>(a, s, head_ok ? head : g * G, grp, oacc, m_run, l_run);
             }
@@ -742,8 +805,8 @@ int decode_resident_slots(int head_size, int num_kv_heads) {
         hipError_t e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
         if (e == hipSuccess)
             e = head_size == 128
-                    ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_bf16_kernel<128, false, false, false>, 64 * waves, 0)
-                    : hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_bf16_kernel<64, false, false, false>, 64 * waves, 0);
+                    ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_bf16_kernel<128, false, false, false, false>, 64 * waves, 0)
+                    : hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_bf16_kernel<64, false, false, false, false>, 64 * waves, 0);
         if (e != hipSuccess || ncu <= 0 || nb <= 0) {
             (void)hipGetLastError();
             return 256;
@@ -755,15 +818,15 @@ int decode_resident_slots(int head_size, int num_kv_heads) {
 }
 
 // Partition kernel (+ merge kernel when the batch is cut into more than one chunk).
-template <bool ALIBI, bool CASCADE, bool FP8>
+template <bool ALIBI, bool CASCADE, bool FP8, bool FUSED = false>
 static void launch_partition_merge(const DecodeArgs& a, hipStream_t st) {
     const int hkv = a.c.num_kv_heads;
     const dim3 grid(a.nw, (hkv + 7) / 8);
     const dim3 block(64 * (hkv < 8 ? hkv : 8));
     if (a.c.head_size == 128)
-        hipLaunchKernelGGL((decode_bf16_kernel<128, ALIBI, CASCADE, FP8>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((decode_bf16_kernel<128, ALIBI, CASCADE, FP8, FUSED>), grid, block, 0, st, a);
     else
-        hipLaunchKernelGGL((decode_bf16_kernel<64, ALIBI, CASCADE, FP8>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((decode_bf16_kernel<64, ALIBI, CASCADE, FP8, FUSED>), grid, block, 0, st, a);
     if (a.nw > 1) {
         const dim3 mg(a.num_seqs, (a.num_heads + 3) / 4);
         const bool many = a.nw > 8 * a.num_seqs;  // more than ~8 pieces per sequence
@@ -779,6 +842,11 @@ static void launch_partition_merge(const DecodeArgs& a, hipStream_t st) {
 
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t st) {
     const bool fp8 = a.c.dtype == 2;
+    if (a.knew != nullptr && !fp8) {  // the store fused into the partition kernel
+        if (a.alibi) launch_partition_merge<true, false, false, true>(a, st);
+        else launch_partition_merge<false, false, false, true>(a, st);
+        return hipGetLastError();
+    }
     if (a.alibi) {
         if (fp8) launch_partition_merge<true, false, true>(a, st);
         else launch_partition_merge<true, false, false>(a, st);

@@ -387,6 +387,9 @@ static int decode_args(const pa_cache_desc* cache, void* out, const void* query,
     a.ws_o = nullptr;
     a.ws_ml = nullptr;
     a.key_start = key_start;
+    a.knew = nullptr;
+    a.vnew = nullptr;
+    a.slots = nullptr;
     a.prefix_chunks = 0;
     a.prefix_mfma = 0;
     a.pre_o = nullptr;
@@ -445,6 +448,12 @@ int pa_decode_with_store(const pa_cache_desc* cache, void* out, const void* quer
     if (empty) { g_last_error[0] = 0; return PA_OK; }
     if (!key || !value || !slot_mapping) return fail(PA_ERR_INVALID_ARG, "key, value and slot_mapping must be non-NULL");
     hipStream_t s = (hipStream_t)stream;
+    if (a.c.dtype == PA_BF16) {  // one launch: the decode kernel reads and stores the new rows
+        a.knew = key;
+        a.vnew = value;
+        a.slots = slot_mapping;
+        return launch_status(pa::launch_decode_bf16(a, s));
+    }
     pa::StoreArgs sa;
     sa.c = a.c;
     sa.key = key;

@@ -140,6 +140,12 @@ struct DecodeArgs {
     int32_t prefix_mfma; // 1: the prefix pass runs on the prefill kernel, 0: the split-key kernel
     float* pre_o;        // [prefix_chunks][num_seqs][H][D]
     float* pre_ml;       // [prefix_chunks][num_seqs][H][2]
+    // decode with the store fused (bf16 cache): each sequence's new token, its key n - 1, is
+    // read from knew / vnew ([num_seqs][Hkv][D]) instead of the cache, and written to cache slot
+    // slots[s] (negative: not written) by the workgroup holding that key; null knew: no store
+    const void* knew;
+    const void* vnew;
+    const int32_t* slots;
 };
 
 // Host launchers (return hipGetLastError() of the launches).
