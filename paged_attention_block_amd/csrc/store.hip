@@ -3,28 +3,54 @@
 //
 // Store (MinivLLM API docs, "Attention", store_kvcache; vLLM learning book section 10 Q2):
 // the flat slot index equals the row index of the [NB*BS] token rows of a cache plane, so a
-// token's destination row is simply `slot`, with no division.  One workgroup per token:
-// threads cover the K and V rows in consecutive 16-byte chunks, so every wave writes whole
-// contiguous rows (2 KB per plane for 8 KV heads x 128 bf16).
+// token's destination row is simply `slot`, with no division.  A workgroup takes a few
+// consecutive tokens; its threads cover the K and V rows in consecutive 16-byte chunks, so
+// every wave writes whole contiguous rows (2 KB per plane for 8 KV heads x 128 bf16).
 #include "pa_internal.hpp"
 
 namespace pa {
 
-__global__ __launch_bounds__(256) void store_kernel(uint4* __restrict__ cache,
-                                                    const uint4* __restrict__ key,
-                                                    const uint4* __restrict__ value,
+// Holds every chunk of a batch until its load has arrived: one wait after all the loads
+// of the batch are in flight, instead of the compiler sinking each load into its store's
+// branch, where it waits for that load alone.  (Two tokens per workgroup measure 10% faster
+// than one on a 13894-token store; four are no faster, eight slower.)
+template <int N>
+__device__ inline void hold(u32x4 (&x)[N]) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) asm volatile("" : "+v"(x[i]));
+}
+
+template <int TPW>
+__global__ __launch_bounds__(256) void store_kernel(u32x4* __restrict__ cache,
+                                                    const u32x4* __restrict__ key,
+                                                    const u32x4* __restrict__ value,
                                                     const int32_t* __restrict__ slots,
-                                                    int32_t row_chunks, int64_t plane_chunks) {
-    const int32_t t = blockIdx.x;
-    const int32_t slot = slots[t];
-    if (slot < 0) return;
-    const int64_t src = (int64_t)t * row_chunks;
-    const int64_t dst = (int64_t)slot * row_chunks;
+                                                    int32_t num_tokens, int32_t row_chunks,
+                                                    int64_t plane_chunks) {
+    // TPW tokens per workgroup: a thread issues the loads of its chunk of every token before
+    // the first store, so each thread keeps TPW 16-byte reads in flight.  A token past the
+    // end reads the last token's row, and a token with a negative slot is read but not
+    // stored.
+    const int32_t t0 = blockIdx.x * TPW;
+    int32_t slot[TPW];
+    int64_t row[TPW];
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+        slot[i] = t0 + i < num_tokens ? slots[t0 + i] : -1;
+        row[i] = (int64_t)min(t0 + i, num_tokens - 1) * row_chunks;
+    }
     for (int32_t c = threadIdx.x; c < 2 * row_chunks; c += blockDim.x) {
         const bool is_v = c >= row_chunks;
         const int32_t cc = is_v ? c - row_chunks : c;
-        const uint4 x = is_v ? value[src + cc] : key[src + cc];
-        cache[(is_v ? plane_chunks : 0) + dst + cc] = x;
+        const u32x4* src = is_v ? value : key;
+        u32x4* dst = cache + (is_v ? plane_chunks : 0) + cc;
+        u32x4 x[TPW];
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) x[i] = src[row[i] + cc];
+        hold(x);
+#pragma unroll
+        for (int i = 0; i < TPW; ++i)
+            if (slot[i] >= 0) dst[(int64_t)slot[i] * row_chunks] = x[i];
     }
 }
 
@@ -90,9 +116,10 @@ hipError_t launch_store(const StoreArgs& a, hipStream_t s) {
     const int64_t plane_chunks = a.c.plane_elems * elt / 16;
     int threads = 2 * row_chunks;
     threads = threads > 256 ? 256 : ((threads + 63) / 64) * 64;
-    hipLaunchKernelGGL(store_kernel, dim3(a.num_tokens), dim3(threads), 0, s,
-                       (uint4*)a.c.kv, (const uint4*)a.key, (const uint4*)a.value, a.slots,
-                       row_chunks, plane_chunks);
+    constexpr int kTpw = 2;
+    hipLaunchKernelGGL(store_kernel<kTpw>, dim3((int32_t)(((int64_t)a.num_tokens + kTpw - 1) / kTpw)),
+                       dim3(threads), 0, s, (u32x4*)a.c.kv, (const u32x4*)a.key, (const u32x4*)a.value, a.slots,
+                       a.num_tokens, row_chunks, plane_chunks);
     return hipGetLastError();
 }
 
