@@ -127,6 +127,33 @@ def test_store_worked_example_gpu():
     assert torch.equal(cache.cpu(), exp)
 
 
+@pytest.mark.parametrize("hkv,d,dtype,num_tokens", [
+    (8, 128, torch.bfloat16, 1), (8, 128, torch.bfloat16, 2), (8, 128, torch.bfloat16, 3),
+    (8, 128, torch.bfloat16, 257), (16, 128, torch.bfloat16, 65),   # rows of 512 16-byte pieces
+    (1, 64, torch.bfloat16, 33),                                   # rows of 8 pieces: idle lanes
+    (3, 64, torch.float32, 31), (8, 128, torch.float32, 18)])
+def test_store_shapes_gpu(hkv, d, dtype, num_tokens):
+    """Whole cache bit for bit against the oracle's store: odd token counts (a pair of tokens
+    split at the end), negative slots first, last and in between, and rows shorter or longer
+    than one workgroup's pass."""
+    import paged_attention_block_amd as pa
+    rng = np.random.default_rng(num_tokens * 131 + hkv * 7 + d)
+    nb, bs = (num_tokens + 15) // 16 + 3, 16
+    slots = rng.permutation(nb * bs)[:num_tokens].astype(np.int32)
+    neg = rng.random(num_tokens) < 0.2
+    if num_tokens > 2:
+        neg[0] = neg[-1] = True
+    slots[neg] = -1
+    g = torch.Generator().manual_seed(num_tokens)
+    k = torch.randn(num_tokens, hkv, d, generator=g).to(dtype)
+    v = torch.randn(num_tokens, hkv, d, generator=g).to(dtype)
+    cache0 = torch.randn(2, nb, bs, hkv, d, generator=g).to(dtype)
+    cache = cache0.to(DEV)
+    pa.pa_store_kv(k.to(DEV), v.to(DEV), cache, torch.from_numpy(slots).to(DEV))
+    exp = oracle.store_kv(bits(cache0), bits(k), bits(v), slots)
+    assert np.array_equal(bits(cache.cpu()), exp)
+
+
 # ----------------------------------------------------------------------------- small ragged cases
 
 PREFILL_CASES = {
