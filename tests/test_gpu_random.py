@@ -25,8 +25,10 @@ pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
 F8 = torch.float8_e4m3fn
 # case counts (PA_RANDOM_CASES / PA_RANDOM_CASCADE_CASES widen a run; the defaults are what the
-# suite runs)
+# suite runs); PA_RANDOM_SEED0 starts every sweep at another seed, so a run can draw cases the
+# default range does not
 N_CASES = int(os.environ.get("PA_RANDOM_CASES", "160"))
+SEED0 = int(os.environ.get("PA_RANDOM_SEED0", "0"))
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -71,7 +73,7 @@ def draw_case(seed: int) -> dict:
 
 
 def test_sweep_draws_cover_the_options():
-    cases = [draw_case(i) for i in range(N_CASES)]
+    cases = [draw_case(i) for i in range(SEED0, SEED0 + N_CASES)]
     for key in ("fp8", "alibi", "fused"):
         assert any(c[key] for c in cases) and not all(c[key] for c in cases), key
     assert {c["kind"] for c in cases} == {"prefill", "decode"}
@@ -81,7 +83,7 @@ def test_sweep_draws_cover_the_options():
     assert len({c["BS"] for c in cases}) >= 5
 
 
-@pytest.mark.parametrize("seed", range(N_CASES))
+@pytest.mark.parametrize("seed", range(SEED0, SEED0 + N_CASES))
 def test_random_step(seed):
     c = draw_case(seed)
     say(f"[random {seed}] {c['kind']} {str(c['dtype'])[6:]}{' fp8' if c['fp8'] else ''} H {c['H']}/{c['Hkv']} "
@@ -160,7 +162,7 @@ def test_cascade_draws_reach_both_prefix_passes():
     assert any(c["fp8"] for c in cases) and not all(c["fp8"] for c in cases)
 
 
-@pytest.mark.parametrize("seed", range(N_CASCADE))
+@pytest.mark.parametrize("seed", range(SEED0, SEED0 + N_CASCADE))
 def test_random_cascade(seed):
     import paged_attention_block_amd as pa
     c = draw_cascade(seed)
@@ -210,7 +212,7 @@ def draw_large(seed: int) -> dict:
             "kv_scale": 0.5}
 
 
-@pytest.mark.parametrize("seed", range(N_LARGE))
+@pytest.mark.parametrize("seed", range(SEED0, SEED0 + N_LARGE))
 def test_random_large_prefill_sampled(seed):
     """Chunks of 256-2048 rows over contexts up to 8192 keys: many q-tiles and key tiles per
     sequence; sampled rows (tile edges, first/last rows, random) against the oracle."""
