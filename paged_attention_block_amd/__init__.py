@@ -2,7 +2,9 @@
 
 Thin ctypes binding of ``libpa.so`` (C ABI in ``include/pa.h``).  The functions carry the
 C names; they only marshal torch tensors (device memory) and the current HIP stream into
-the C calls, and raise ``PaError`` on a non-OK status.  Every step of the computation runs
+the C calls, and raise ``PaError`` on a non-OK status.  ``validate=True`` (every call) first
+checks the contents of the index arrays on host copies (``validate.py``: slots, block-table
+entries, lengths), raising ``ValueError`` before any launch; it synchronises with the device.  Every step of the computation runs
 in the library's HIP kernels; there is no fallback path: if ``libpa.so`` has not been built
 or cannot be loaded, every call raises.
 
@@ -18,6 +20,8 @@ import os
 from typing import Optional
 
 import torch
+
+from . import validate as _v
 
 __all__ = [
     "PaError", "lib_path", "load", "pa_store_kv", "pa_copy_blocks", "pa_prefill_varlen",
@@ -151,7 +155,7 @@ def _need(t: torch.Tensor, name: str, dtype, device, dims: Optional[int] = None)
 
 
 def pa_store_kv(key: torch.Tensor, value: torch.Tensor, kv_cache: torch.Tensor,
-                slot_mapping: torch.Tensor, kv_scale: float = 1.0) -> None:
+                slot_mapping: torch.Tensor, kv_scale: float = 1.0, validate: bool = False) -> None:
     """Scatter ``key``/``value`` ``[T, Hkv, D]`` into ``kv_cache`` at ``slot_mapping`` (-1 skips);
     an FP8 cache stores e4m3(x / kv_scale)."""
     lib = load()
@@ -162,17 +166,21 @@ def pa_store_kv(key: torch.Tensor, value: torch.Tensor, kv_cache: torch.Tensor,
     _need(slot_mapping, "slot_mapping", torch.int32, dev, 1)
     if key.shape != value.shape or key.shape[1:] != kv_cache.shape[3:] or key.shape[0] != slot_mapping.shape[0]:
         raise ValueError("key/value must be [num_tokens, num_kv_heads, head_size] matching slot_mapping and the cache")
+    if validate:
+        _v.check_store(slot_mapping, kv_cache.shape[1], kv_cache.shape[2])
     _check(lib.pa_store_kv(ctypes.byref(desc), _ptr(key), _ptr(value), _ptr(slot_mapping),
                            key.shape[0], _stream(kv_cache)), "pa_store_kv")
 
 
-def pa_copy_blocks(kv_cache: torch.Tensor, block_pairs: torch.Tensor) -> None:
+def pa_copy_blocks(kv_cache: torch.Tensor, block_pairs: torch.Tensor, validate: bool = False) -> None:
     """``kv_cache[:, dst] = kv_cache[:, src]`` for each row ``(src, dst)`` of ``block_pairs``."""
     lib = load()
     desc = _desc(kv_cache)
     _need(block_pairs, "block_pairs", torch.int32, kv_cache.device, 2)
     if block_pairs.shape[1] != 2:
         raise ValueError("block_pairs must be [num_pairs, 2]")
+    if validate:
+        _v.check_copy_blocks(block_pairs, kv_cache.shape[1])
     _check(lib.pa_copy_blocks(ctypes.byref(desc), _ptr(block_pairs), block_pairs.shape[0],
                               _stream(kv_cache)), "pa_copy_blocks")
 
@@ -181,7 +189,8 @@ def pa_prefill_varlen(query: torch.Tensor, kv_cache: torch.Tensor, block_table: 
                       cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor, max_seqlen_q: int,
                       max_seqlen_k: int, scale: float, num_kv_heads: int, sliding_window: int = 0,
                       out: Optional[torch.Tensor] = None,
-                      alibi_slopes: Optional[torch.Tensor] = None, kv_scale: float = 1.0) -> torch.Tensor:
+                      alibi_slopes: Optional[torch.Tensor] = None, kv_scale: float = 1.0,
+                      validate: bool = False) -> torch.Tensor:
     """Varlen causal attention of packed ``query [Tq, H, D]`` over the cached keys
     (``alibi_slopes``: optional float32 ``[H]`` ALiBi slopes on the cache's device;
     ``kv_scale``: the scale of an FP8 cache)."""
@@ -205,6 +214,9 @@ def pa_prefill_varlen(query: torch.Tensor, kv_cache: torch.Tensor, block_table: 
         _need(out, "out", _act(kv_cache), dev, 3)
         if out.shape != query.shape:
             raise ValueError("out must match query's shape")
+    if validate:
+        _v.check_prefill(cu_seqlens_q, cu_seqlens_k, block_table, max_seqlen_q, max_seqlen_k, sliding_window,
+                         kv_cache.shape[1], kv_cache.shape[2], query.shape[0])
     _check(lib.pa_prefill_varlen(ctypes.byref(desc), _ptr(out), _ptr(query), _ptr(block_table),
                                  block_table.shape[1], _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
                                  num_seqs, int(max_seqlen_q), int(max_seqlen_k), query.shape[1],
@@ -232,7 +244,8 @@ def pa_decode(query: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Te
               seq_lens: torch.Tensor, max_seq_len: int, scale: float, num_kv_heads: int,
               sliding_window: int = 0, out: Optional[torch.Tensor] = None,
               workspace: Optional[torch.Tensor] = None, partition_size: int = 0,
-              alibi_slopes: Optional[torch.Tensor] = None, kv_scale: float = 1.0) -> torch.Tensor:
+              alibi_slopes: Optional[torch.Tensor] = None, kv_scale: float = 1.0,
+              validate: bool = False) -> torch.Tensor:
     """One query per sequence (``query [B, H, D]``) over its ``seq_lens[s]`` cached keys.
 
     ``workspace`` is a device byte buffer of at least ``pa_decode_workspace_size(...)``
@@ -266,6 +279,9 @@ def pa_decode(query: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Te
     if workspace is not None and workspace.device != dev:
         raise ValueError("workspace must be on the cache's device")
     with (torch.cuda.device(dev) if dev.type == "cuda" else contextlib.nullcontext()):
+        if validate:
+            _v.check_decode(seq_lens, block_table, int(max_seq_len), int(sliding_window), kv_cache.shape[1],
+                            kv_cache.shape[2])
         _check(lib.pa_decode(ctypes.byref(desc), _ptr(out), _ptr(query), _ptr(block_table),
                              block_table.shape[1], _ptr(seq_lens), num_seqs, int(max_seq_len),
                              query.shape[1], float(scale), int(sliding_window),
@@ -289,7 +305,7 @@ def pa_cascade_decode(query: torch.Tensor, kv_cache: torch.Tensor, block_table: 
                       seq_lens: torch.Tensor, max_seq_len: int, scale: float, num_kv_heads: int,
                       common_prefix_len: int, out: Optional[torch.Tensor] = None,
                       workspace: Optional[torch.Tensor] = None, partition_size: int = 0,
-                      kv_scale: float = 1.0) -> torch.Tensor:
+                      kv_scale: float = 1.0, validate: bool = False) -> torch.Tensor:
     """Decode of a batch whose block-table rows all start with the same
     ``common_prefix_len / block_size`` physical blocks: the shared prefix is attended once
     for every query, then each sequence's own keys (arguments otherwise as ``pa_decode``)."""
@@ -320,6 +336,9 @@ def pa_cascade_decode(query: torch.Tensor, kv_cache: torch.Tensor, block_table: 
     if workspace is not None and workspace.device != dev:
         raise ValueError("workspace must be on the cache's device")
     with (torch.cuda.device(dev) if dev.type == "cuda" else contextlib.nullcontext()):
+        if validate:
+            _v.check_cascade(seq_lens, block_table, int(max_seq_len), int(common_prefix_len), kv_cache.shape[1],
+                             kv_cache.shape[2])
         _check(lib.pa_cascade_decode(ctypes.byref(desc), _ptr(out), _ptr(query), _ptr(block_table),
                                      block_table.shape[1], _ptr(seq_lens), num_seqs, int(max_seq_len),
                                      query.shape[1], float(scale), int(common_prefix_len),
@@ -346,7 +365,7 @@ def pa_prefill_varlen_with_store(query: torch.Tensor, key: torch.Tensor, value: 
                                  scale: float, num_kv_heads: int, sliding_window: int = 0,
                                  out: Optional[torch.Tensor] = None,
                                  alibi_slopes: Optional[torch.Tensor] = None,
-                                 kv_scale: float = 1.0) -> torch.Tensor:
+                                 kv_scale: float = 1.0, validate: bool = False) -> torch.Tensor:
     """Store the batch's new tokens (``key``/``value [Tq, Hkv, D]`` at ``slot_mapping``) and run
     the varlen causal attention of ``query [Tq, H, D]`` in one call (one kernel for bf16)."""
     lib = load()
@@ -370,6 +389,10 @@ def pa_prefill_varlen_with_store(query: torch.Tensor, key: torch.Tensor, value: 
         _need(out, "out", _act(kv_cache), dev, 3)
         if out.shape != query.shape:
             raise ValueError("out must match query's shape")
+    if validate:
+        _v.check_prefill_with_store(slot_mapping, cu_seqlens_q, cu_seqlens_k, block_table, max_seqlen_q,
+                                    max_seqlen_k, sliding_window, kv_cache.shape[1], kv_cache.shape[2],
+                                    query.shape[0])
     _check(lib.pa_prefill_varlen_with_store(ctypes.byref(desc), _ptr(out), _ptr(query), _ptr(key), _ptr(value),
                                             _ptr(slot_mapping), query.shape[0], _ptr(block_table),
                                             block_table.shape[1], _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
@@ -385,7 +408,8 @@ def pa_decode_with_store(query: torch.Tensor, key: torch.Tensor, value: torch.Te
                          seq_lens: torch.Tensor, max_seq_len: int, scale: float, num_kv_heads: int,
                          sliding_window: int = 0, out: Optional[torch.Tensor] = None,
                          workspace: Optional[torch.Tensor] = None, partition_size: int = 0,
-                         alibi_slopes: Optional[torch.Tensor] = None, kv_scale: float = 1.0) -> torch.Tensor:
+                         alibi_slopes: Optional[torch.Tensor] = None, kv_scale: float = 1.0,
+                         validate: bool = False) -> torch.Tensor:
     """Store each sequence's new token (``key``/``value [B, Hkv, D]`` at ``slot_mapping``) and
     decode ``query [B, H, D]`` over the ``seq_lens[s]`` keys that include it, in one call."""
     lib = load()
@@ -416,6 +440,9 @@ def pa_decode_with_store(query: torch.Tensor, key: torch.Tensor, value: torch.Te
     if workspace is not None and workspace.device != dev:
         raise ValueError("workspace must be on the cache's device")
     with (torch.cuda.device(dev) if dev.type == "cuda" else contextlib.nullcontext()):
+        if validate:
+            _v.check_decode_with_store(slot_mapping, seq_lens, block_table, int(max_seq_len), int(sliding_window),
+                                       kv_cache.shape[1], kv_cache.shape[2])
         _check(lib.pa_decode_with_store(ctypes.byref(desc), _ptr(out), _ptr(query), _ptr(key), _ptr(value),
                                         _ptr(slot_mapping), _ptr(block_table), block_table.shape[1],
                                         _ptr(seq_lens), num_seqs, int(max_seq_len), query.shape[1],

@@ -495,3 +495,34 @@ def test_config_alibi_sampled(n):
     run.alibi = _slopes(wl.num_heads) / 16.0     # long contexts: a gentler bias keeps many keys alive
     _check_phase(run, wl.phases[0], bits(wl.kv_cache), picks_rng=np.random.default_rng(200 + n),
                  label=f"config{n}/alibi")
+
+
+def test_validate_flag_gpu():
+    """validate=True: valid calls give the same results; a broken precondition raises
+    ValueError before any launch (the cache is left as it was)."""
+    import paged_attention_block_amd as pa
+    g = torch.Generator().manual_seed(5)
+    k = torch.randn(3, 2, 64, generator=g).to(DEV)
+    v = torch.randn(3, 2, 64, generator=g).to(DEV)
+    cache = torch.zeros(2, 4, 16, 2, 64, device=DEV)
+    with pytest.raises(ValueError, match="write race"):
+        pa.pa_store_kv(k, v, cache, torch.tensor([0, 5, 5], dtype=torch.int32, device=DEV), validate=True)
+    with pytest.raises(ValueError, match="both a destination and a source"):
+        pa.pa_copy_blocks(cache, torch.tensor([[0, 1], [1, 2]], dtype=torch.int32, device=DEV), validate=True)
+    assert int(torch.count_nonzero(cache)) == 0
+    pa.pa_store_kv(k, v, cache, torch.tensor([16, 17, 18], dtype=torch.int32, device=DEV), validate=True)
+    q = torch.randn(1, 4, 64, generator=g).to(DEV)
+    table = torch.tensor([[1, -1]], dtype=torch.int32, device=DEV)
+    lens = torch.tensor([3], dtype=torch.int32, device=DEV)
+    a = pa.pa_decode(q, cache, table, lens, 3, 0.125, 2)
+    b = pa.pa_decode(q, cache, table, lens, 3, 0.125, 2, validate=True)
+    assert torch.equal(a, b)
+    with pytest.raises(ValueError, match=r"block_table\[0, 1\] = -1"):
+        pa.pa_decode(q, cache, table, torch.tensor([17], dtype=torch.int32, device=DEV), 32, 0.125, 2,
+                     validate=True)
+    cu = torch.tensor([0, 1], dtype=torch.int32, device=DEV)
+    c = pa.pa_prefill_varlen(q, cache, table, cu, torch.tensor([0, 3], dtype=torch.int32, device=DEV), 1, 3,
+                             0.125, 2, validate=True)
+    # the decode query as the last row of a 3-key prefill: another kernel, the same result
+    torch.testing.assert_close(c, a, rtol=1e-5, atol=1e-5)
+    torch.cuda.synchronize()
