@@ -67,23 +67,36 @@ __device__ inline uint32_t e4m3x4(uint32_t lo, uint32_t hi, float r) {
     return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sat_e4m3(c), sat_e4m3(d), (int)w, true);
 }
 
+template <int TPW>
 __global__ __launch_bounds__(256) void store_fp8_kernel(u32x2* __restrict__ cache,
-                                                        const uint4* __restrict__ key,
-                                                        const uint4* __restrict__ value,
+                                                        const u32x4* __restrict__ key,
+                                                        const u32x4* __restrict__ value,
                                                         const int32_t* __restrict__ slots,
-                                                        int32_t row_chunks, int64_t plane_chunks,
-                                                        float r) {
-    // row_chunks: 16-byte pieces of an input row = 8-byte pieces of a cache row
-    const int32_t t = blockIdx.x;
-    const int32_t slot = slots[t];
-    if (slot < 0) return;
-    const int64_t src = (int64_t)t * row_chunks;
-    const int64_t dst = (int64_t)slot * row_chunks;
+                                                        int32_t num_tokens, int32_t row_chunks,
+                                                        int64_t plane_chunks, float r) {
+    // row_chunks: 16-byte pieces of an input row = 8-byte pieces of a cache row.  TPW tokens
+    // per workgroup, loads first, as in store_kernel.
+    const int32_t t0 = blockIdx.x * TPW;
+    int32_t slot[TPW];
+    int64_t row[TPW];
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+        slot[i] = t0 + i < num_tokens ? slots[t0 + i] : -1;
+        row[i] = (int64_t)min(t0 + i, num_tokens - 1) * row_chunks;
+    }
     for (int32_t c = threadIdx.x; c < 2 * row_chunks; c += blockDim.x) {
         const bool is_v = c >= row_chunks;
         const int32_t cc = is_v ? c - row_chunks : c;
-        const uint4 x = is_v ? value[src + cc] : key[src + cc];
-        cache[(is_v ? plane_chunks : 0) + dst + cc] = u32x2{e4m3x4(x.x, x.y, r), e4m3x4(x.z, x.w, r)};
+        const u32x4* src = is_v ? value : key;
+        u32x2* dst = cache + (is_v ? plane_chunks : 0) + cc;
+        u32x4 x[TPW];
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) x[i] = src[row[i] + cc];
+        hold(x);
+#pragma unroll
+        for (int i = 0; i < TPW; ++i)
+            if (slot[i] >= 0)
+                dst[(int64_t)slot[i] * row_chunks] = u32x2{e4m3x4(x[i][0], x[i][1], r), e4m3x4(x[i][2], x[i][3], r)};
     }
 }
 
@@ -106,9 +119,10 @@ hipError_t launch_store(const StoreArgs& a, hipStream_t s) {
         const int64_t plane_chunks = a.c.plane_elems / 8;
         int threads = 2 * row_chunks;
         threads = threads > 256 ? 256 : ((threads + 63) / 64) * 64;
-        hipLaunchKernelGGL(store_fp8_kernel, dim3(a.num_tokens), dim3(threads), 0, s, (u32x2*)a.c.kv,
-                           (const uint4*)a.key, (const uint4*)a.value, a.slots, row_chunks, plane_chunks,
-                           a.c.kv_inv_scale);
+        constexpr int kTpw = 2;
+        hipLaunchKernelGGL(store_fp8_kernel<kTpw>, dim3((int32_t)(((int64_t)a.num_tokens + kTpw - 1) / kTpw)),
+                           dim3(threads), 0, s, (u32x2*)a.c.kv, (const u32x4*)a.key, (const u32x4*)a.value,
+                           a.slots, a.num_tokens, row_chunks, plane_chunks, a.c.kv_inv_scale);
         return hipGetLastError();
     }
     const int elt = cache_elt(a.c.dtype);
