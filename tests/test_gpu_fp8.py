@@ -12,7 +12,7 @@ import torch
 import oracle
 from oracle import fp8
 import workloads as W
-from tests.gpu_helpers import GpuRun, assert_close, bits, host_values, sample_picks, say
+from tests.gpu_helpers import GpuRun, assert_close, bits, host_values, say
 
 pytestmark = pytest.mark.gpu
 
@@ -158,8 +158,9 @@ def test_fp8_cascade_decode(part):
     assert_close(out.float().cpu().numpy(), ref, torch.bfloat16, f"fp8 cascade p{part}")
 
 
-def test_fp8_decode_gqa_full_size_sampled():
-    """The GQA decode shape (B 64, contexts U[512, 4096], H 32/8, D 128) over an FP8 cache."""
+def test_fp8_decode_gqa_full_size():
+    """The GQA decode shape (B 64, contexts U[512, 4096], H 32/8, D 128) over an FP8 cache:
+    every output against the oracle."""
     rng = np.random.default_rng(2)
     ctx = rng.integers(512, 4096 + 1, size=64)
     wl = _fp8_decode_workload("fp8_gqa", 503, [int(c) for c in ctx], 32, 8, 128, 16)
@@ -170,13 +171,8 @@ def test_fp8_decode_gqa_full_size_sampled():
     say("[fp8 decode full size]")
     out = run.run(dec)
     torch.cuda.synchronize()
-    picks = sample_picks(dec, wl.num_heads, np.random.default_rng(9), n_random=48)
-    cu_q = np.arange(len(dec.seq_lens) + 1)
-    cu_k = np.concatenate([[0], np.cumsum(dec.seq_lens)])
-    ref = oracle.attention_rows(host_values(dec.query), vals, dec.block_table, cu_q, cu_k, wl.scale,
-                                wl.num_kv_heads, 0, picks)
-    got = out.float().cpu().numpy()
-    assert_close(np.stack([got[r, h] for r, h in picks]), ref, torch.bfloat16, "fp8 decode full")
+    ref = oracle.decode(host_values(dec.query), vals, dec.block_table, dec.seq_lens, wl.scale, wl.num_kv_heads)
+    assert_close(out.float().cpu().numpy(), ref, torch.bfloat16, "fp8 decode full")
 
 
 PREFILL_CASES = {
@@ -230,8 +226,8 @@ def test_fp8_prefill_with_store_alibi():
     assert_close(out.float().cpu().numpy(), ref, torch.bfloat16, "fp8 prefill with store")
 
 
-def test_fp8_prefill_varlen_full_size_sampled():
-    """16 prompts U[128, 2048], H 32/8, D 128 over an FP8 cache: sampled rows."""
+def test_fp8_prefill_varlen_full_size():
+    """16 prompts U[128, 2048], H 32/8, D 128 over an FP8 cache: every output."""
     rng = np.random.default_rng(3)
     lens = rng.integers(128, 2048 + 1, size=16)
     wl = W.build("fp8_prefill", 507, [W.SeqSpec(0, [int(n)], ["prefill"]) for n in lens], num_heads=32,
@@ -243,11 +239,9 @@ def test_fp8_prefill_varlen_full_size_sampled():
     say("[fp8 prefill full size]")
     out = run.run(pre)
     torch.cuda.synchronize()
-    picks = sample_picks(pre, wl.num_heads, np.random.default_rng(10), n_random=64)
-    ref = oracle.attention_rows(host_values(pre.query), vals, pre.block_table, pre.cu_seqlens_q, pre.cu_seqlens_k,
-                                wl.scale, wl.num_kv_heads, 0, picks)
-    got = out.float().cpu().numpy()
-    assert_close(np.stack([got[r, h] for r, h in picks]), ref, torch.bfloat16, "fp8 prefill full")
+    ref = oracle.prefill_varlen(host_values(pre.query), vals, pre.block_table, pre.cu_seqlens_q, pre.cu_seqlens_k,
+                                wl.scale, wl.num_kv_heads, 0)
+    assert_close(out.float().cpu().numpy(), ref, torch.bfloat16, "fp8 prefill full")
 
 
 def test_fp8_cascade_decode_prefill_kernel_prefix():

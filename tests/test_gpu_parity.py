@@ -2,9 +2,8 @@
 
 Store and copy_blocks are compared bit for bit over the whole cache; attention outputs
 elementwise within |err| <= 2e-2 + 1e-2*|oracle| (bf16) or 1e-5 + 1e-5*|oracle| (fp32).
-Small ragged cases are checked on every output; the five full-size workloads on every
-output where the oracle is quick, else on sampled rows (first/last rows of each sequence,
-tile boundaries, random rows).
+Small ragged cases and the five full-size workloads (and their fused-store and ALiBi
+variants) are checked on every output element.
 """
 
 from __future__ import annotations
@@ -18,7 +17,7 @@ import torch
 import oracle
 import workloads as W
 from tests.gpu_helpers import (GpuRun, assert_close, bits, host_values, oracle_attention,
-                               relayout, sample_picks, say)
+                               relayout, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -40,7 +39,7 @@ def _config(n):
     return W.config(n)
 
 
-def _check_phase(run: GpuRun, ops, cache_ref_bits, *, picks_rng=None, partition_size=0, label=""):
+def _check_phase(run: GpuRun, ops, cache_ref_bits, *, partition_size=0, label=""):
     """Run ops on the GPU and on the oracle; returns updated oracle cache bits."""
     wl = run.wl
     for op in ops:
@@ -57,19 +56,13 @@ def _check_phase(run: GpuRun, ops, cache_ref_bits, *, picks_rng=None, partition_
         else:
             vals = host_values(run.cache.cpu())
             got = out.float().cpu().numpy()
-            if picks_rng is None:
-                ref = oracle_attention(wl, op, vals, alibi=run.alibi)
-                err = assert_close(got, ref, wl.dtype, f"{label} {name}")
-            else:
-                picks = sample_picks(op, wl.num_heads, picks_rng)
-                ref = oracle_attention(wl, op, vals, picks, alibi=run.alibi)
-                sel = np.stack([got[r, h] for r, h in picks])
-                err = assert_close(sel, ref, wl.dtype, f"{label} {name} (sampled {len(picks)})")
+            ref = oracle_attention(wl, op, vals, alibi=run.alibi)
+            err = assert_close(got, ref, wl.dtype, f"{label} {name}")
             say(f"[{label}] {name} max abs err {err:.3e}")
     return cache_ref_bits
 
 
-def _check_phase_with_store(run: GpuRun, ops, cache_ref_bits, *, picks_rng=None, partition_size=0, label=""):
+def _check_phase_with_store(run: GpuRun, ops, cache_ref_bits, *, partition_size=0, label=""):
     """Like _check_phase, but each attention op runs fused with the store of its own rows of
     the phase's StoreOp (pa_*_with_store); the oracle is the store followed by the op."""
     wl = run.wl
@@ -93,14 +86,8 @@ def _check_phase_with_store(run: GpuRun, ops, cache_ref_bits, *, picks_rng=None,
         np.testing.assert_array_equal(bits(host), cache_ref_bits)
         vals = host_values(host)
         got = out.float().cpu().numpy()
-        if picks_rng is None:
-            ref = oracle_attention(wl, op, vals, alibi=run.alibi)
-            err = assert_close(got, ref, wl.dtype, f"{label} {name}")
-        else:
-            picks = sample_picks(op, wl.num_heads, picks_rng)
-            ref = oracle_attention(wl, op, vals, picks, alibi=run.alibi)
-            sel = np.stack([got[r, h] for r, h in picks])
-            err = assert_close(sel, ref, wl.dtype, f"{label} {name} (sampled {len(picks)})")
+        ref = oracle_attention(wl, op, vals, alibi=run.alibi)
+        err = assert_close(got, ref, wl.dtype, f"{label} {name}")
         say(f"[{label}] {name} with store: max abs err {err:.3e}")
     return cache_ref_bits
 
@@ -383,28 +370,27 @@ def test_config2_decode_partition_sizes(part):
     run = GpuRun(wl, DEV)
     store, dec = wl.phases[0]
     run.run(store)
-    _check_phase(run, [dec], None, picks_rng=np.random.default_rng(part), partition_size=part,
-                 label=f"config2 p{part}")
+    _check_phase(run, [dec], None, partition_size=part, label=f"config2 p{part}")
 
 
-def test_config3_prefill_sampled():
+def test_config3_prefill_full():
     wl = _config(3)
     run = GpuRun(wl, DEV)
-    _check_phase(run, wl.phases[0], bits(wl.kv_cache), picks_rng=np.random.default_rng(3), label="config3")
+    _check_phase(run, wl.phases[0], bits(wl.kv_cache), label="config3")
 
 
 def test_config4_chunked_window_then_decode():
     wl = _config(4)
     run = GpuRun(wl, DEV)
     ref = bits(wl.kv_cache)
-    ref = _check_phase(run, wl.phases[0], ref, picks_rng=np.random.default_rng(4), label="config4 prefill")
+    ref = _check_phase(run, wl.phases[0], ref, label="config4 prefill")
     _check_phase(run, wl.phases[1], ref, label="config4 decode")
 
 
 def test_config5_mixed_step():
     wl = _config(5)
     run = GpuRun(wl, DEV)
-    _check_phase(run, wl.phases[0], bits(wl.kv_cache), picks_rng=np.random.default_rng(5), label="config5")
+    _check_phase(run, wl.phases[0], bits(wl.kv_cache), label="config5")
 
 
 # ----------------------------------------------------------------------------- store fused into the call
@@ -442,15 +428,14 @@ def test_config1_fp32_all_phases_with_store():
 
 
 @pytest.mark.parametrize("n", [3, 4, 5])
-def test_config_with_store_sampled(n):
+def test_config_with_store_full(n):
     """The causal, chunked-window and mixed workloads with every store fused into its attention
     call (the chunked-window one: both its prefill and its decode phase)."""
     wl = _config(n)
     run = GpuRun(wl, DEV)
     ref = bits(wl.kv_cache)
     for i, ph in enumerate(wl.phases):
-        ref = _check_phase_with_store(run, ph, ref, picks_rng=np.random.default_rng(100 + n),
-                                      label=f"config{n} phase {i} fused")
+        ref = _check_phase_with_store(run, ph, ref, label=f"config{n} phase {i} fused")
 
 
 # ----------------------------------------------------------------------------- ALiBi
@@ -489,12 +474,11 @@ def test_small_decode_alibi(name, part):
 
 
 @pytest.mark.parametrize("n", [2, 3])
-def test_config_alibi_sampled(n):
+def test_config_alibi_full(n):
     wl = _config(n)
     run = GpuRun(wl, DEV)
     run.alibi = _slopes(wl.num_heads) / 16.0     # long contexts: a gentler bias keeps many keys alive
-    _check_phase(run, wl.phases[0], bits(wl.kv_cache), picks_rng=np.random.default_rng(200 + n),
-                 label=f"config{n}/alibi")
+    _check_phase(run, wl.phases[0], bits(wl.kv_cache), label=f"config{n}/alibi")
 
 
 def test_validate_flag_gpu():
