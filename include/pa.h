@@ -266,6 +266,31 @@ int pa_cascade_decode(const pa_cache_desc* cache, void* out, const void* query,
                       int32_t partition_size, void* workspace, size_t workspace_bytes,
                       void* stream);
 
+/*
+ * pa_decode_no_alloc — pa_decode with no workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  It calls no allocating routine.  The split's partial states go to a
+ * scratch array that the library keeps in device memory, PA_DECODE_NO_ALLOC_SCRATCH_BYTES
+ * (32 MiB) on each GPU it runs on, held from the library's load on that GPU until the
+ * process ends.  Its device address is looked up once per device, on the first call with
+ * that device current.
+ *
+ * Arguments and results as pa_decode (the caller still passes every input and output); the
+ * call runs on the current device, which must be the device of the tensors and the stream.
+ * Sizes whose split needs more scratch than the maximum (pa_decode_workspace_size(...)
+ * > PA_DECODE_NO_ALLOC_SCRATCH_BYTES: e.g. many heads with a small partition_size) return
+ * PA_ERR_WORKSPACE before any launch; pa_decode with a caller-owned workspace serves them.
+ * Every call on one GPU shares that GPU's array and leaves its contents behind (the kernels
+ * need none cleared): calls that overlap on one GPU (concurrent streams, or host threads)
+ * race on it and give wrong results, so a caller serialises them.
+ */
+#define PA_DECODE_NO_ALLOC_SCRATCH_BYTES (32u << 20)
+int pa_decode_no_alloc(const pa_cache_desc* cache, void* out, const void* query,
+                       const int32_t* block_table, int32_t max_blocks_per_seq,
+                       const int32_t* seq_lens, int32_t num_seqs, int32_t max_seq_len,
+                       int32_t num_heads, float scale, int32_t sliding_window,
+                       const float* alibi_slopes, int32_t partition_size, void* stream);
+
 /* Fixed text for a status code. */
 const char* pa_status_string(int status);
 

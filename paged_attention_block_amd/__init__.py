@@ -26,8 +26,12 @@ from . import validate as _v
 __all__ = [
     "PaError", "lib_path", "load", "pa_store_kv", "pa_copy_blocks", "pa_prefill_varlen",
     "pa_decode", "pa_decode_workspace_size", "pa_prefill_varlen_with_store", "pa_decode_with_store",
-    "pa_cascade_decode", "pa_cascade_decode_workspace_size",
+    "pa_cascade_decode", "pa_cascade_decode_workspace_size", "pa_decode_no_alloc",
+    "DECODE_NO_ALLOC_SCRATCH_BYTES",
 ]
+
+# pa_decode_no_alloc's per-GPU scratch (PA_DECODE_NO_ALLOC_SCRATCH_BYTES in pa.h)
+DECODE_NO_ALLOC_SCRATCH_BYTES = 32 << 20
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libpa.so"
@@ -84,8 +88,10 @@ def load() -> ctypes.CDLL:
     lib.pa_cascade_decode_workspace_size.argtypes = [D, I32, I32, I32, I32, I32]
     lib.pa_cascade_decode_workspace_size.restype = SZ
     lib.pa_cascade_decode.argtypes = [D, P, P, P, I32, P, I32, I32, I32, F32, I32, I32, P, SZ, P]
+    lib.pa_decode_no_alloc.argtypes = [D, P, P, P, I32, P, I32, I32, I32, F32, I32, P, I32, P]
     for name in ("pa_store_kv", "pa_copy_blocks", "pa_prefill_varlen", "pa_decode",
-                 "pa_prefill_varlen_with_store", "pa_decode_with_store", "pa_cascade_decode"):
+                 "pa_prefill_varlen_with_store", "pa_decode_with_store", "pa_cascade_decode",
+                 "pa_decode_no_alloc"):
         getattr(lib, name).restype = ctypes.c_int
     lib.pa_status_string.argtypes = [ctypes.c_int]
     lib.pa_status_string.restype = ctypes.c_char_p
@@ -287,6 +293,46 @@ def pa_decode(query: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Te
                              query.shape[1], float(scale), int(sliding_window),
                              _alibi(alibi_slopes, query, dev), int(partition_size),
                              _ptr(workspace), ws_bytes, _stream(kv_cache)), "pa_decode")
+    return out
+
+
+def pa_decode_no_alloc(query: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
+                       seq_lens: torch.Tensor, max_seq_len: int, scale: float, num_kv_heads: int,
+                       sliding_window: int = 0, out: Optional[torch.Tensor] = None, partition_size: int = 0,
+                       alibi_slopes: Optional[torch.Tensor] = None, kv_scale: float = 1.0,
+                       validate: bool = False) -> torch.Tensor:
+    """``pa_decode`` without a workspace: the library's per-GPU scratch holds the split's
+    partial states, so the call allocates nothing when ``out`` is given (calls on one GPU
+    must not overlap).  Raises ``PaError`` (workspace status) when the split needs more
+    than ``DECODE_NO_ALLOC_SCRATCH_BYTES``."""
+    lib = load()
+    desc = _desc(kv_cache, kv_scale)
+    dev = kv_cache.device
+    if num_kv_heads != kv_cache.shape[3]:
+        raise ValueError(f"num_kv_heads {num_kv_heads} != cache's {kv_cache.shape[3]}")
+    _need(query, "query", _act(kv_cache), dev, 3)
+    _need(block_table, "block_table", torch.int32, dev, 2)
+    _need(seq_lens, "seq_lens", torch.int32, dev, 1)
+    num_seqs = query.shape[0]
+    if seq_lens.shape[0] != num_seqs or block_table.shape[0] < num_seqs:
+        raise ValueError("seq_lens must be [num_seqs] and block_table [num_seqs, max_blocks]")
+    if query.shape[2] != kv_cache.shape[4]:
+        raise ValueError("query head_size does not match the cache")
+    if out is None:
+        out = torch.empty_like(query)
+    else:
+        _need(out, "out", _act(kv_cache), dev, 3)
+        if out.shape != query.shape:
+            raise ValueError("out must match query's shape")
+    with (torch.cuda.device(dev) if dev.type == "cuda" else contextlib.nullcontext()):
+        if validate:
+            _v.check_decode(seq_lens, block_table, int(max_seq_len), int(sliding_window), kv_cache.shape[1],
+                            kv_cache.shape[2])
+        _check(lib.pa_decode_no_alloc(ctypes.byref(desc), _ptr(out), _ptr(query), _ptr(block_table),
+                                      block_table.shape[1], _ptr(seq_lens), num_seqs, int(max_seq_len),
+                                      query.shape[1], float(scale), int(sliding_window),
+                                      _alibi(alibi_slopes, query, dev), int(partition_size), _stream(kv_cache)),
+               "pa_decode_no_alloc")
     return out
 
 

@@ -7,6 +7,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "pa.h"
 #include "pa_internal.hpp"
 
@@ -176,6 +178,33 @@ DecodePlan decode_plan(const pa_cache_desc* cache, int32_t num_seqs, int32_t num
         p.prefix_bytes = (size_t)p.prefix_chunks * num_seqs * num_heads * ((size_t)cache->head_size + 2) * sizeof(float);
     }
     return p;
+}
+
+// Scratch of pa_decode_no_alloc: one array on each GPU the library's code is loaded on.
+// In host code its name is a host-side stand-in, not a device address; the address comes
+// from hipGetSymbolAddress, looked up once per device with that device current.
+static __device__ __align__(256) char scratch[PA_DECODE_NO_ALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+
+// Device address of `scratch` on the current device.  Concurrent first calls on one device
+// may each look it up; they store the same address.
+int scratch_address(void** ptr) {
+    static std::atomic<void*> addr[kMaxDevices];
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "hipGetDevice failed: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(PA_ERR_UNSUPPORTED, "device %d out of range", dev);
+    void* p = addr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || p == nullptr)
+            return fail(PA_ERR_LAUNCH, "no device address for the decode scratch on device %d: %s", dev,
+                        hipGetErrorString(e));
+        addr[dev].store(p, std::memory_order_release);
+    }
+    *ptr = p;
+    return PA_OK;
 }
 
 }  // namespace
@@ -427,6 +456,39 @@ int pa_decode(const pa_cache_desc* cache, void* out, const void* query, const in
     int st = decode_args(cache, out, query, block_table, max_blocks_per_seq, seq_lens, num_seqs, max_seq_len,
                          num_heads, scale, sliding_window, alibi_slopes, partition_size, workspace,
                          workspace_bytes, &a, &empty);
+    if (st) return st;
+    if (empty) { g_last_error[0] = 0; return PA_OK; }
+    hipStream_t s = (hipStream_t)stream;
+    return launch_status(a.c.dtype == PA_F32 ? pa::launch_decode_f32(a, s) : pa::launch_decode_bf16(a, s));
+}
+
+int pa_decode_no_alloc(const pa_cache_desc* cache, void* out, const void* query, const int32_t* block_table,
+                       int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t num_seqs,
+                       int32_t max_seq_len, int32_t num_heads, float scale, int32_t sliding_window,
+                       const float* alibi_slopes, int32_t partition_size, void* stream) {
+    pa::DecodeArgs a;
+    bool empty;
+    // the split's size first (0 for invalid arguments, which decode_args then rejects)
+    const size_t need = pa_decode_workspace_size(cache, num_seqs, num_heads, max_seq_len, sliding_window,
+                                                 partition_size);
+    if (need > PA_DECODE_NO_ALLOC_SCRATCH_BYTES) {
+        // any other invalid argument is reported first, as pa_decode would
+        const int st = decode_args(cache, out, query, block_table, max_blocks_per_seq, seq_lens, num_seqs,
+                                   max_seq_len, num_heads, scale, sliding_window, alibi_slopes, partition_size,
+                                   nullptr, 0, &a, &empty);
+        if (st != PA_OK && st != PA_ERR_WORKSPACE) return st;
+        return fail(PA_ERR_WORKSPACE,
+                    "pa_decode_no_alloc: this split needs %zu bytes of scratch, more than its maximum of %u "
+                    "(pa_decode with a workspace serves it)", need, (unsigned)PA_DECODE_NO_ALLOC_SCRATCH_BYTES);
+    }
+    void* ws = nullptr;
+    if (need > 0) {
+        const int st = scratch_address(&ws);
+        if (st) return st;
+    }
+    int st = decode_args(cache, out, query, block_table, max_blocks_per_seq, seq_lens, num_seqs, max_seq_len,
+                         num_heads, scale, sliding_window, alibi_slopes, partition_size, ws,
+                         need > 0 ? (size_t)PA_DECODE_NO_ALLOC_SCRATCH_BYTES : 0, &a, &empty);
     if (st) return st;
     if (empty) { g_last_error[0] = 0; return PA_OK; }
     hipStream_t s = (hipStream_t)stream;

@@ -211,3 +211,17 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     with pytest.raises(RuntimeError, match="is missing"):
         pa.pa_decode(torch.zeros((1, 4, 64), dtype=torch.bfloat16), cache, torch.zeros((1, 4), dtype=torch.int32),
                      torch.ones(1, dtype=torch.int32), 1, 0.125, 2)
+
+
+def test_decode_no_alloc_refuses_splits_beyond_its_scratch(lib):
+    """pa_decode_no_alloc holds PA_DECODE_NO_ALLOC_SCRATCH_BYTES of scratch per GPU: a split
+    needing more is refused on the host (workspace status) before any HIP call; zero work is
+    a no-op."""
+    d = desc(nb=1000, bs=16, hkv=8, d=128)
+    need = lib.pa_decode_workspace_size(d, 512, 128, 4096, 0, 32)
+    assert need == 512 * 128 * 2 * 128 * 130 * 4 > pa.DECODE_NO_ALLOC_SCRATCH_BYTES
+    assert lib.pa_decode_no_alloc(d, FAKE, FAKE, FAKE, 300, FAKE, 512, 4096, 128, 0.1, 0, None, 32, None) == 3
+    assert b"scratch" in lib.pa_last_error()
+    assert lib.pa_decode_no_alloc(d, None, None, None, 1, None, 0, 0, 32, 1.0, 0, None, 0, None) == 0
+    # bad scalars are still rejected as by pa_decode
+    assert lib.pa_decode_no_alloc(d, FAKE, FAKE, FAKE, 300, FAKE, 64, 4097, 32, 0.1, 0, None, 48, None) == 1
