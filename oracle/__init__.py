@@ -11,6 +11,7 @@ from .paged_attention import (  # noqa: F401
     attention_probs,
     attention_rows,
     cascade_decode,
+    cascade_prefill_varlen,
     cascade_split,
     copy_blocks,
     decode,

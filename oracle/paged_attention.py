@@ -71,6 +71,7 @@ __all__ = [
     "merge_partials",
     "cascade_split",
     "cascade_decode",
+    "cascade_prefill_varlen",
 ]
 
 
@@ -371,3 +372,62 @@ def cascade_decode(query, kv_cache, block_table, seq_lens, scale, num_kv_heads,
             own = partial_attention(q[s, h], ko, vo, scale)
             out[s, h] = merge_partials([shared[s], own])
     return out
+
+
+def cascade_prefill_varlen(query, kv_cache, block_table, cu_seqlens_q, cu_seqlens_k, scale,
+                           num_kv_heads, common_prefix_len) -> np.ndarray:
+    """Shared-prefix varlen attention, ``[total_q, num_heads, head_size]`` fp64.
+
+    vLLM learning book, section 8 (Cascade Attention) and self-check question 4, with the
+    cascade fields of section 4 FlashAttentionMetadata (``cu_prefix_query_lens``,
+    ``prefix_kv_lens``, ``suffix_kv_lens``): (1) the shared segment: every query row of the
+    batch, taken together as one block of rows, attends the one prefix ``[0, P)``, read once
+    through the first sequence's block table; (2) each sequence's own segment: its rows attend
+    its keys from ``P`` on under the causal rule of ``prefill_varlen`` (diagonal offset by
+    ``seqlen_k - seqlen_q``); (3) the two parts are combined (``merge_partials``).
+
+    Reading: the pages give the shared segment no mask.  That holds because every query row
+    sits at or after the prefix's last key (``seqlen_k - seqlen_q >= P - 1``: the prefix lies in
+    the sequence's cached context, or ends at its first new token; for one query per sequence
+    this is ``seq_lens >= P`` as in ``cascade_decode``), so it may attend all of the prefix.  The
+    prefix is whole blocks and every block-table row starts with the same prefix blocks;
+    anything else raises ``ValueError``.  No sliding window and no ALiBi.
+    """
+    q = np.asarray(query, dtype=np.float64)
+    total_q, num_heads, head_size = q.shape
+    block_size = kv_cache.shape[2]
+    P = int(common_prefix_len)
+    if P < 0 or P % block_size != 0:
+        raise ValueError("common_prefix_len must be a non-negative multiple of block_size")
+    num_seqs = len(cu_seqlens_q) - 1
+    nb = P // block_size
+    for s in range(num_seqs):
+        seqlen_q = int(cu_seqlens_q[s + 1] - cu_seqlens_q[s])
+        seqlen_k = int(cu_seqlens_k[s + 1] - cu_seqlens_k[s])
+        if seqlen_k - seqlen_q + 1 < P:
+            raise ValueError(f"sequence {s}: its first query row lies inside the shared prefix")
+        if not np.array_equal(block_table[s, :nb], block_table[0, :nb]):
+            raise ValueError(f"sequence {s} does not share the prefix blocks")
+    out = np.zeros((total_q, num_heads, head_size), dtype=np.float64)
+    # (1) the shared segment's keys, once for the whole batch
+    pre_pos, _ = cascade_split(P, P)
+    shared_kv = [gather_kv(kv_cache, block_table[0], pre_pos, g) for g in range(num_kv_heads)]
+    for s in range(num_seqs):
+        q0 = int(cu_seqlens_q[s])
+        seqlen_q = int(cu_seqlens_q[s + 1]) - q0
+        seqlen_k = int(cu_seqlens_k[s + 1] - cu_seqlens_k[s])
+        own_kv = [gather_kv(kv_cache, block_table[s], range(P, seqlen_k), g) for g in range(num_kv_heads)]
+        for i in range(seqlen_q):
+            lo, hi = key_range(i, seqlen_q, seqlen_k, 0)
+            for h in range(num_heads):
+                g = kv_head_of(h, num_heads, num_kv_heads)
+                kp, vp = shared_kv[g]
+                ko, vo = own_kv[g]
+                prefix_pos, own_pos = cascade_split(hi + 1, P)
+                own_idx = np.asarray(own_pos, dtype=np.int64) - P
+                shared = partial_attention(q[q0 + i, h], kp[np.asarray(prefix_pos, dtype=np.int64)],
+                                           vp[np.asarray(prefix_pos, dtype=np.int64)], scale)
+                own = partial_attention(q[q0 + i, h], ko[own_idx], vo[own_idx], scale)
+                out[q0 + i, h] = merge_partials([shared, own])
+    return out
+

@@ -512,3 +512,81 @@ def test_cascade_rejects_what_is_not_a_shared_prefix():
     bad = table.copy(); bad[1, 1] = table[1, 2]
     with pytest.raises(ValueError):
         oracle.cascade_decode(q, cache, bad, np.array([9, 12]), 0.5, Hkv, P)        # block not shared
+
+
+# ----------------------------------------------------------------------------- cascade prefill pins
+
+
+def _shared_prefix_chunks(seed, specs, P, H, Hkv, D, BS):
+    """Query chunks over sequences that share their first ``P`` keys (prefix blocks shared by
+    every block-table row): specs = [(seqlen_q, seqlen_k)], each with seqlen_k - seqlen_q >= P."""
+    lens = [sk for _, sk in specs]
+    q_all, cache, table, ks, vs = _shared_prefix_case(seed, lens, P, H, Hkv, D, BS)
+    rng = np.random.default_rng(seed + 1000)
+    q = rng.standard_normal((sum(sq for sq, _ in specs), H, D))
+    cu_q = np.concatenate([[0], np.cumsum([sq for sq, _ in specs])]).astype(np.int64)
+    cu_k = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    return q, cache, table, cu_q, cu_k, ks, vs
+
+
+CASCADE_PREFILL_SPECS = {
+    # name: (P, [(seqlen_q, seqlen_k)])
+    "chunks": (8, [(4, 12), (1, 9), (7, 30), (3, 11)]),
+    "long_prefix": (16, [(5, 21), (2, 40)]),
+    "no_prefix": (0, [(3, 3), (5, 9)]),
+    "exact_context": (12, [(6, 18), (12, 24)]),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CASCADE_PREFILL_SPECS))
+def test_cascade_prefill_equals_sdpa_and_plain_prefill(name):
+    # vLLM learning book, section 8: the split into the shared segment (all queries of the batch
+    # together) and each request's own segment is mathematically equivalent to plain attention;
+    # checked against torch SDPA on the contiguous keys with the bottom-right causal mask, and
+    # against plain prefill_varlen on the same paged cache
+    P, specs = CASCADE_PREFILL_SPECS[name]
+    H, Hkv, D, BS = 6, 2, 8, 4
+    q, cache, table, cu_q, cu_k, ks, vs = _shared_prefix_chunks(120 + P, specs, P, H, Hkv, D, BS)
+    out = oracle.cascade_prefill_varlen(q, cache, table, cu_q, cu_k, 0.45, Hkv, P)
+    for s, (sq, sk) in enumerate(specs):
+        k = np.repeat(ks[s], H // Hkv, axis=1); v = np.repeat(vs[s], H // Hkv, axis=1)
+        allowed = np.tril(np.ones((sq, sk), dtype=bool), k=sk - sq)
+        ref = _sdpa(q[cu_q[s]:cu_q[s + 1]], k, v, allowed, 0.45)
+        np.testing.assert_allclose(out[cu_q[s]:cu_q[s + 1]], ref, rtol=1e-12, atol=1e-12)
+    plain = oracle.prefill_varlen(q, cache, table, cu_q, cu_k, 0.45, Hkv)
+    np.testing.assert_allclose(out, plain, rtol=1e-12, atol=1e-12)
+
+
+def test_cascade_prefill_uniform_weights_closed_form():
+    # q = 0 gives every visible key the same weight: row i of a sequence (position p) is the
+    # mean of value rows 0..p, so the shared segment counts P / (p + 1) of it
+    H, Hkv, D, BS, P = 4, 4, 8, 4, 12
+    specs = [(3, 15), (5, 20), (1, 13)]
+    q, cache, table, cu_q, cu_k, ks, vs = _shared_prefix_chunks(131, specs, P, H, Hkv, D, BS)
+    out = oracle.cascade_prefill_varlen(np.zeros_like(q), cache, table, cu_q, cu_k, 0.8, Hkv, P)
+    for s, (sq, sk) in enumerate(specs):
+        for i in range(sq):
+            p = sk - sq + i
+            np.testing.assert_allclose(out[cu_q[s] + i], vs[s][:p + 1].mean(axis=0), rtol=1e-13, atol=1e-13)
+
+
+def test_cascade_prefill_of_single_queries_is_cascade_decode():
+    # one query per sequence: the decode form of the same split
+    H, Hkv, D, BS, P = 6, 3, 8, 4, 8
+    specs = [(1, 9), (1, 8), (1, 30)]
+    q, cache, table, cu_q, cu_k, _, _ = _shared_prefix_chunks(141, specs, P, H, Hkv, D, BS)
+    a = oracle.cascade_prefill_varlen(q, cache, table, cu_q, cu_k, 0.5, Hkv, P)
+    b = oracle.cascade_decode(q, cache, table, np.array([sk for _, sk in specs]), 0.5, Hkv, P)
+    np.testing.assert_allclose(a, b, rtol=1e-13, atol=1e-13)
+
+
+def test_cascade_prefill_rejects_what_is_not_a_shared_cached_prefix():
+    H, Hkv, D, BS, P = 4, 2, 8, 4, 8
+    q, cache, table, cu_q, cu_k, _, _ = _shared_prefix_chunks(151, [(2, 12), (4, 14)], P, H, Hkv, D, BS)
+    with pytest.raises(ValueError):
+        oracle.cascade_prefill_varlen(q, cache, table, cu_q, cu_k, 0.5, Hkv, 6)    # not whole blocks
+    with pytest.raises(ValueError):
+        oracle.cascade_prefill_varlen(q, cache, table, cu_q, cu_k, 0.5, Hkv, 12)   # 14 - 4 < 12
+    bad = table.copy(); bad[1, 1] = table[1, 2]
+    with pytest.raises(ValueError):
+        oracle.cascade_prefill_varlen(q, cache, bad, cu_q, cu_k, 0.5, Hkv, P)      # block not shared

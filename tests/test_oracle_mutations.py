@@ -29,6 +29,8 @@ PIN_FUNCS = [
     lambda gd: pins.test_cascade_equals_dense_attention_and_plain_decode(8, [8, 9, 21, 30]),
     lambda gd: pins.test_cascade_uniform_weights_closed_form(),
     lambda gd: pins.test_merge_partials_of_any_split_is_the_whole_softmax(),
+    lambda gd: pins.test_cascade_prefill_equals_sdpa_and_plain_prefill("chunks"),
+    lambda gd: pins.test_cascade_prefill_uniform_weights_closed_form(),
 ]
 
 
@@ -92,6 +94,14 @@ def _split_overlapping(seq_len, common_prefix_len):
 
 
 _orig_gather = pa.gather_kv
+_orig_split = pa.cascade_split
+
+
+def _shared_segment_causal(seq_len, common_prefix_len):
+    # the shared segment cut at the row's own position relative to the prefix, as if the
+    # prefix were the start of each query chunk
+    pre, own = _orig_split(seq_len, common_prefix_len)
+    return range(0, min(common_prefix_len, max(1, seq_len - common_prefix_len))), own
 
 MUTATIONS = {
     "window_off_by_one": ("key_range", _window_off_by_one),
@@ -105,6 +115,7 @@ MUTATIONS = {
     "alibi_half_slope": ("alibi_bias", _alibi_half_slope),
     "cascade_merge_equal_weights": ("merge_partials", _merge_equal_weights),
     "cascade_parts_overlap": ("cascade_split", _split_overlapping),
+    "cascade_shared_segment_causal": ("cascade_split", _shared_segment_causal),
 }
 
 
