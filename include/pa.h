@@ -267,6 +267,45 @@ int pa_cascade_decode(const pa_cache_desc* cache, void* out, const void* query,
                       void* stream);
 
 /*
+ * pa_cascade_prefill_varlen_workspace_size — bytes of device workspace pa_cascade_prefill_varlen
+ * needs: the prefix pass's states, num_tokens * num_heads * (head_size + 2) floats per prefix
+ * chunk (0 for float32 caches and for common_prefix_len 0).
+ */
+size_t pa_cascade_prefill_varlen_workspace_size(const pa_cache_desc* cache, int32_t num_tokens,
+                                                int32_t num_heads, int32_t common_prefix_len);
+
+/*
+ * pa_cascade_prefill_varlen — varlen causal attention (as pa_prefill_varlen, no window) of a
+ * batch whose sequences share their first common_prefix_len keys through the same physical
+ * blocks, with query chunks of any length (chunked prefill, mixed prefill/decode batches).
+ *
+ * vLLM learning book, "05. Attention Backends", section 8 (Cascade Attention), the cascade
+ * fields of section 4 FlashAttentionMetadata (common_prefix_len, cu_prefix_query_lens,
+ * prefix_kv_lens, suffix_kv_lens) and self-check question 4: the shared segment is attended
+ * by every query row of the batch together (the prefix's K/V read once for all of them), each
+ * sequence's rows then attend its own keys from common_prefix_len on under the causal rule,
+ * and the two parts are combined by log-sum-exp.  The result equals pa_prefill_varlen (up to
+ * rounding).  Runs the prefix pass (the packed query rows as one block against the prefix),
+ * then the prefill kernel over the own keys, folding the prefix states into each row.
+ *
+ *   common_prefix_len  a multiple of block_size, at most max_seqlen_k; 0 runs pa_prefill_varlen
+ *   num_tokens         the packed query rows, == cu_seqlens_q[num_seqs] (sizes the prefix pass)
+ *   workspace          16-byte aligned, >= pa_cascade_prefill_varlen_workspace_size(...) bytes;
+ *                      contents need no initialisation
+ *   (other arguments as pa_prefill_varlen; bf16 or FP8 caches, no ALiBi)
+ * Preconditions on device data (not checked): every sequence's first query row sits at or
+ * after the prefix's last key (seqlen_k - seqlen_q >= common_prefix_len - 1), and entries
+ * [0, common_prefix_len / block_size) of every block-table row are the same physical blocks
+ * (the prefix is read through row 0).
+ */
+int pa_cascade_prefill_varlen(const pa_cache_desc* cache, void* out, const void* query,
+                              const int32_t* block_table, int32_t max_blocks_per_seq,
+                              const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t num_seqs,
+                              int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t num_heads, float scale,
+                              int32_t common_prefix_len, int32_t num_tokens, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/*
  * pa_decode_no_alloc — pa_decode with no workspace argument, for callers that cannot
  * allocate device memory: code under HIP graph capture, tight serving loops, harnesses that
  * forbid hipMalloc.  It calls no allocating routine.  The split's partial states go to a

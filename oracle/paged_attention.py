@@ -424,10 +424,11 @@ def cascade_prefill_varlen(query, kv_cache, block_table, cu_seqlens_q, cu_seqlen
                 kp, vp = shared_kv[g]
                 ko, vo = own_kv[g]
                 prefix_pos, own_pos = cascade_split(hi + 1, P)
-                own_idx = np.asarray(own_pos, dtype=np.int64) - P
-                shared = partial_attention(q[q0 + i, h], kp[np.asarray(prefix_pos, dtype=np.int64)],
-                                           vp[np.asarray(prefix_pos, dtype=np.int64)], scale)
-                own = partial_attention(q[q0 + i, h], ko[own_idx], vo[own_idx], scale)
+                # the parts are ranges of positions: the rows gathered above, sliced
+                shared = partial_attention(q[q0 + i, h], kp[prefix_pos.start:prefix_pos.stop],
+                                           vp[prefix_pos.start:prefix_pos.stop], scale)
+                own = partial_attention(q[q0 + i, h], ko[own_pos.start - P:own_pos.stop - P],
+                                        vo[own_pos.start - P:own_pos.stop - P], scale)
                 out[q0 + i, h] = merge_partials([shared, own])
     return out
 

@@ -27,6 +27,7 @@ __all__ = [
     "PaError", "lib_path", "load", "pa_store_kv", "pa_copy_blocks", "pa_prefill_varlen",
     "pa_decode", "pa_decode_workspace_size", "pa_prefill_varlen_with_store", "pa_decode_with_store",
     "pa_cascade_decode", "pa_cascade_decode_workspace_size", "pa_decode_no_alloc",
+    "pa_cascade_prefill_varlen", "pa_cascade_prefill_varlen_workspace_size",
     "DECODE_NO_ALLOC_SCRATCH_BYTES",
 ]
 
@@ -89,9 +90,12 @@ def load() -> ctypes.CDLL:
     lib.pa_cascade_decode_workspace_size.restype = SZ
     lib.pa_cascade_decode.argtypes = [D, P, P, P, I32, P, I32, I32, I32, F32, I32, I32, P, SZ, P]
     lib.pa_decode_no_alloc.argtypes = [D, P, P, P, I32, P, I32, I32, I32, F32, I32, P, I32, P]
+    lib.pa_cascade_prefill_varlen_workspace_size.argtypes = [D, I32, I32, I32]
+    lib.pa_cascade_prefill_varlen_workspace_size.restype = SZ
+    lib.pa_cascade_prefill_varlen.argtypes = [D, P, P, P, I32, P, P, I32, I32, I32, I32, F32, I32, I32, P, SZ, P]
     for name in ("pa_store_kv", "pa_copy_blocks", "pa_prefill_varlen", "pa_decode",
                  "pa_prefill_varlen_with_store", "pa_decode_with_store", "pa_cascade_decode",
-                 "pa_decode_no_alloc"):
+                 "pa_decode_no_alloc", "pa_cascade_prefill_varlen"):
         getattr(lib, name).restype = ctypes.c_int
     lib.pa_status_string.argtypes = [ctypes.c_int]
     lib.pa_status_string.restype = ctypes.c_char_p
@@ -390,6 +394,64 @@ def pa_cascade_decode(query: torch.Tensor, kv_cache: torch.Tensor, block_table: 
                                      query.shape[1], float(scale), int(common_prefix_len),
                                      int(partition_size), _ptr(workspace), ws_bytes, _stream(kv_cache)),
                "pa_cascade_decode")
+    return out
+
+
+def pa_cascade_prefill_varlen_workspace_size(kv_cache: torch.Tensor, num_tokens: int, num_heads: int,
+                                             common_prefix_len: int) -> int:
+    """Workspace bytes ``pa_cascade_prefill_varlen`` needs for ``num_tokens`` packed query rows."""
+    lib = load()
+    desc = _desc(kv_cache)
+    return int(lib.pa_cascade_prefill_varlen_workspace_size(ctypes.byref(desc), int(num_tokens), int(num_heads),
+                                                            int(common_prefix_len)))
+
+
+def pa_cascade_prefill_varlen(query: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
+                              cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor, max_seqlen_q: int,
+                              max_seqlen_k: int, scale: float, num_kv_heads: int, common_prefix_len: int,
+                              out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                              kv_scale: float = 1.0, validate: bool = False) -> torch.Tensor:
+    """Varlen causal attention of packed ``query [Tq, H, D]`` whose sequences share their first
+    ``common_prefix_len`` keys (block-table rows starting with the same blocks): the shared
+    prefix is attended once for every query row, then each sequence's own keys (arguments
+    otherwise as ``pa_prefill_varlen``; no window, no ALiBi)."""
+    lib = load()
+    desc = _desc(kv_cache, kv_scale)
+    dev = kv_cache.device
+    if num_kv_heads != kv_cache.shape[3]:
+        raise ValueError(f"num_kv_heads {num_kv_heads} != cache's {kv_cache.shape[3]}")
+    _need(query, "query", _act(kv_cache), dev, 3)
+    _need(block_table, "block_table", torch.int32, dev, 2)
+    _need(cu_seqlens_q, "cu_seqlens_q", torch.int32, dev, 1)
+    _need(cu_seqlens_k, "cu_seqlens_k", torch.int32, dev, 1)
+    num_seqs = cu_seqlens_q.shape[0] - 1
+    if cu_seqlens_k.shape[0] != num_seqs + 1 or block_table.shape[0] < num_seqs:
+        raise ValueError("cu_seqlens_q/k must be [num_seqs + 1] and block_table [num_seqs, max_blocks]")
+    if query.shape[2] != kv_cache.shape[4]:
+        raise ValueError("query head_size does not match the cache")
+    if out is None:
+        out = torch.empty_like(query)
+    else:
+        _need(out, "out", _act(kv_cache), dev, 3)
+        if out.shape != query.shape:
+            raise ValueError("out must match query's shape")
+    num_tokens = query.shape[0]
+    need = pa_cascade_prefill_varlen_workspace_size(kv_cache, num_tokens, query.shape[1], int(common_prefix_len))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if workspace is not None and workspace.device != dev:
+        raise ValueError("workspace must be on the cache's device")
+    with (torch.cuda.device(dev) if dev.type == "cuda" else contextlib.nullcontext()):
+        if validate:
+            _v.check_cascade_prefill(cu_seqlens_q, cu_seqlens_k, block_table, max_seqlen_q, max_seqlen_k,
+                                     int(common_prefix_len), kv_cache.shape[1], kv_cache.shape[2], num_tokens)
+        _check(lib.pa_cascade_prefill_varlen(ctypes.byref(desc), _ptr(out), _ptr(query), _ptr(block_table),
+                                             block_table.shape[1], _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
+                                             num_seqs, int(max_seqlen_q), int(max_seqlen_k), query.shape[1],
+                                             float(scale), int(common_prefix_len), num_tokens, _ptr(workspace),
+                                             ws_bytes, _stream(kv_cache)),
+               "pa_cascade_prefill_varlen")
     return out
 
 

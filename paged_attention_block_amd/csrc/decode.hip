@@ -857,12 +857,10 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t st) {
     return hipGetLastError();
 }
 
-hipError_t launch_cascade_decode_bf16(const DecodeArgs& a, hipStream_t st) {
+hipError_t launch_prefix_pass(const DecodeArgs& a, hipStream_t st) {
     const bool fp8 = a.c.dtype == 2;
-    if (a.prefix_mfma) {
-        const hipError_t e = launch_prefix_states(a, st);
-        if (e != hipSuccess) return e;
-    } else {
+    if (a.prefix_mfma) return launch_prefix_states(a, st);
+    {
         const int row_groups = (a.num_seqs * a.group + 15) / 16;
         const int units = a.c.num_kv_heads * a.prefix_chunks;
         const dim3 grid((unsigned)(8LL * row_groups * ((units + 7) / 8)));
@@ -874,6 +872,13 @@ hipError_t launch_cascade_decode_bf16(const DecodeArgs& a, hipStream_t st) {
             else hipLaunchKernelGGL((cascade_prefix_kernel<64, false>), grid, dim3(512), 0, st, a, row_groups);
         }
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_cascade_decode_bf16(const DecodeArgs& a, hipStream_t st) {
+    const bool fp8 = a.c.dtype == 2;
+    const hipError_t e = launch_prefix_pass(a, st);
+    if (e != hipSuccess) return e;
     if (fp8) launch_partition_merge<false, true, true>(a, st);
     else launch_partition_merge<false, true, false>(a, st);
     return hipGetLastError();

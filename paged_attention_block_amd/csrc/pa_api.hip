@@ -296,6 +296,8 @@ static int prefill_args(const pa_cache_desc* cache, void* out, const void* query
     a.prefix_chunks = 0;
     a.pre_o = nullptr;
     a.pre_ml = nullptr;
+    a.cascade = 0;
+    a.prefix_rows = 0;
     return PA_OK;
 }
 
@@ -525,6 +527,78 @@ int pa_decode_with_store(const pa_cache_desc* cache, void* out, const void* quer
     hipError_t e = pa::launch_store(sa, s);
     if (e != hipSuccess) return launch_status(e);
     return launch_status(a.c.dtype == PA_F32 ? pa::launch_decode_f32(a, s) : pa::launch_decode_bf16(a, s));
+}
+
+size_t pa_cascade_prefill_varlen_workspace_size(const pa_cache_desc* cache, int32_t num_tokens, int32_t num_heads,
+                                                int32_t common_prefix_len) {
+    if (!cache || num_tokens <= 0 || num_heads <= 0 || common_prefix_len <= 0) return 0;
+    if (cache->num_kv_heads <= 0 || num_heads % cache->num_kv_heads != 0 || cache->dtype == PA_F32) return 0;
+    const PrefixPlan pp = cascade_prefix_plan(num_tokens, num_heads / cache->num_kv_heads, cache->num_kv_heads,
+                                              common_prefix_len);
+    return (size_t)pp.chunks * num_tokens * num_heads * ((size_t)cache->head_size + 2) * sizeof(float);
+}
+
+int pa_cascade_prefill_varlen(const pa_cache_desc* cache, void* out, const void* query,
+                              const int32_t* block_table, int32_t max_blocks_per_seq,
+                              const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t num_seqs,
+                              int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t num_heads, float scale,
+                              int32_t common_prefix_len, int32_t num_tokens, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+    if (cache && cache->dtype == PA_F32)
+        return fail(PA_ERR_UNSUPPORTED, "shared-prefix prefill needs a bf16 or FP8 cache");
+    if (cache && (cache->block_size <= 0 || common_prefix_len < 0 || common_prefix_len % cache->block_size != 0))
+        return fail(PA_ERR_INVALID_ARG, "common_prefix_len must be a non-negative multiple of block_size (got %d)",
+                    common_prefix_len);
+    pa::PrefillArgs a;
+    bool empty;
+    int st = prefill_args(cache, out, query, block_table, max_blocks_per_seq, cu_seqlens_q, cu_seqlens_k,
+                          num_seqs, max_seqlen_q, max_seqlen_k, num_heads, scale, 0, nullptr, &a, &empty);
+    if (st) return st;
+    if (num_tokens < 0) return fail(PA_ERR_INVALID_ARG, "num_tokens must be >= 0 (got %d)", num_tokens);
+    if (empty || num_tokens == 0) {
+        if (num_tokens == 0 && !empty) return fail(PA_ERR_INVALID_ARG, "num_tokens is 0 but the batch has query rows");
+        g_last_error[0] = 0;
+        return PA_OK;
+    }
+    if (common_prefix_len > max_seqlen_k)
+        return fail(PA_ERR_INVALID_ARG, "common_prefix_len %d exceeds max_seqlen_k %d", common_prefix_len, max_seqlen_k);
+    hipStream_t s = (hipStream_t)stream;
+    if (common_prefix_len == 0) return launch_status(pa::launch_prefill_bf16(a, s));
+    const PrefixPlan pp = cascade_prefix_plan(num_tokens, a.group, a.c.num_kv_heads, common_prefix_len);
+    const size_t need = (size_t)pp.chunks * num_tokens * num_heads * ((size_t)a.c.head_size + 2) * sizeof(float);
+    if (!workspace || workspace_bytes < need)
+        return fail(PA_ERR_WORKSPACE, "shared-prefix prefill needs %zu workspace bytes, got %zu", need,
+                    workspace ? workspace_bytes : 0);
+    if (((uintptr_t)workspace & 15) != 0) return fail(PA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    if ((int64_t)8 * (((int64_t)num_tokens * a.group + 15) / 16) * (((int64_t)a.c.num_kv_heads * pp.chunks + 7) / 8) >
+        0x7fffffff)
+        return fail(PA_ERR_INVALID_ARG, "num_tokens * num_heads too large for the prefix pass");
+    // the prefix pass: every packed query row against the shared prefix, read through table row 0
+    pa::DecodeArgs d;
+    memset(&d, 0, sizeof(d));
+    d.c = a.c;
+    d.q = query;
+    d.table = block_table;
+    d.max_blocks = max_blocks_per_seq;
+    d.num_seqs = num_tokens;
+    d.num_heads = num_heads;
+    d.group = a.group;
+    d.scale = scale;
+    d.key_start = common_prefix_len;
+    d.prefix_chunks = pp.chunks;
+    d.prefix_mfma = pp.mfma ? 1 : 0;
+    d.pre_o = (float*)workspace;
+    d.pre_ml = d.pre_o + (size_t)pp.chunks * num_tokens * num_heads * a.c.head_size;
+    hipError_t e = pa::launch_prefix_pass(d, s);
+    if (e != hipSuccess) return launch_status(e);
+    // each sequence's own keys, folding the prefix states in
+    a.cascade = 1;
+    a.prefix_len = common_prefix_len;
+    a.prefix_chunks = pp.chunks;
+    a.prefix_rows = num_tokens;
+    a.pre_o = d.pre_o;
+    a.pre_ml = d.pre_ml;
+    return launch_status(pa::launch_prefill_bf16(a, s));
 }
 
 int pa_cascade_decode(const pa_cache_desc* cache, void* out, const void* query, const int32_t* block_table,

@@ -113,6 +113,12 @@ struct PrefillArgs {
     int32_t prefix_chunks;
     float* pre_o;        // [prefix_chunks][num_seqs][H][D]
     float* pre_ml;       // [prefix_chunks][num_seqs][H][2]
+    // shared-prefix prefill (cascade != 0): every sequence's keys [0, prefix_len) are one
+    // shared prefix, already attended by the prefix pass for all prefix_rows packed query rows
+    // (states in pre_o / pre_ml, indexed by packed row); this call attends keys from
+    // prefix_len on and folds those states in
+    int32_t cascade;
+    int32_t prefix_rows;
 };
 
 struct DecodeArgs {
@@ -160,6 +166,9 @@ hipError_t launch_cascade_decode_bf16(const DecodeArgs& a, hipStream_t s);
 // The prefix pass of shared-prefix decode on the prefill kernel: the decode queries of the
 // batch against the prefix chunks, states into a.pre_o / a.pre_ml.
 hipError_t launch_prefix_states(const DecodeArgs& a, hipStream_t s);
+// The prefix pass alone (prefill kernel or split-key kernel, by a.prefix_mfma): the a.num_seqs
+// query rows of a.q against the shared prefix [0, a.key_start), states into a.pre_o / a.pre_ml.
+hipError_t launch_prefix_pass(const DecodeArgs& a, hipStream_t s);
 // 64-key tiles of the prefill kernel's prefix pass per chunk, and its workgroups per chunk.
 int prefix_tiles(int prefix_len);
 int prefix_workgroups_per_chunk(int num_seqs, int group, int num_kv_heads);

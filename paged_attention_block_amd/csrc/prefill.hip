@@ -131,7 +131,11 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 // (chunk, row, head) leaves its unnormalised state (O, m, l) in pre_o / pre_ml instead of a
 // bf16 output row.  Work item numbering treats (chunk, KV head) as the (sequence, KV head)
 // index, so the q-tiles of one chunk and KV head share its K/V through one XCD's L2.
-template <int D, int NBR, int BN, int NBUF, bool ALIBI, bool FP8, bool PREFIX, bool W32>
+//
+// CASC: the own-keys pass of shared-prefix prefill.  Each sequence attends only its keys from
+// prefix_len on (keys below it are masked like a window's), and the epilogue folds in, by
+// log-sum-exp, the states the prefix pass left for the same packed query row and head.
+template <int D, int NBR, int BN, int NBUF, bool ALIBI, bool FP8, bool PREFIX, bool W32, bool CASC>
 __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const PrefillArgs a, const PrefillGrid pg) {
     constexpr int NGA = BN / 16;      // 16-key groups per K/V tile
     constexpr int NCC = BN / 32;      // 32-key chunks per K/V tile (PV MFMA k-steps)
@@ -148,6 +152,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const PrefillArgs 
     constexpr int ELT = FP8 ? 1 : 2;  // bytes per cache element
     static_assert(!FP8 || NBUF == 2, "the FP8 copy stages one tile in registers");
     static_assert(!W32 || BN == 64, "the 32x32x16 form takes 64-key tiles as two 32-key blocks");
+    static_assert(!CASC || (W32 && !PREFIX), "the shared-prefix own-keys pass uses the 32x32x16 form");
 
     // NBUF K and NBUF V buffers as distinct objects, so the compiler can tell a copy into one
     // from a read of another and does not wait for in-flight copies before every LDS read
@@ -194,6 +199,10 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const PrefillArgs 
     const int off = sk - sq;
     const int W = PREFIX ? 0 : a.window;
     const int rows_end = sq;
+    // first key this pass attends (CASC: the keys after the shared prefix); has_lo: keys below
+    // a row's first key exist in visited tiles and take an element mask
+    const int kstart = CASC ? a.prefix_len : 0;
+    const bool has_lo = W > 0 || kstart > 0;
 
     const int tid = threadIdx.x;
     const int nwaves = blockDim.x >> 6;
@@ -209,7 +218,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const PrefillArgs 
     const int Hkv = a.c.num_kv_heads;
 
     // key range of the whole workgroup (union over its rows)
-    const int wg_lo = PREFIX ? kc0 : (W > 0 ? max(0, off + wg_row0 - W + 1) : 0);
+    const int wg_lo = PREFIX ? kc0 : max(kstart, W > 0 ? max(0, off + wg_row0 - W + 1) : 0);
     const int wg_hi = PREFIX ? kc1 - 1 : min(off + wg_row_end - 1, sk - 1);
     // this wave's rows and key range
     const int r0 = i0 + RPW * (pair / G);
@@ -217,8 +226,8 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const PrefillArgs 
     const bool wave_active = wave_ok && r0 < rows_end;
     // (PREFIX: every row sees keys [kc0, kc1); the mask then only cuts at kc1)
     const int wv_hi = PREFIX ? kc1 - 1 : min(off + r_last, sk - 1);
-    const int wv_lo = PREFIX ? kc0 : (W > 0 ? max(0, off + r0 - W + 1) : 0);
-    const int wv_lo_max = PREFIX ? kc0 : (W > 0 ? max(0, off + r_last - W + 1) : 0);
+    const int wv_lo = PREFIX ? kc0 : max(kstart, W > 0 ? max(0, off + r0 - W + 1) : 0);
+    const int wv_lo_max = PREFIX ? kc0 : max(kstart, W > 0 ? max(0, off + r_last - W + 1) : 0);
     const int wv_p_min = PREFIX ? kc1 - 1 : off + r0;
 
     const float c_log2 = a.scale * (FP8 ? a.c.kv_scale : 1.f) * 1.4426950408889634f;
@@ -250,7 +259,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const PrefillArgs 
             qf[nb][t] = __builtin_bit_cast(bf16x8, ok ? x : (u32x4)(0u));
         }
         prow[nb] = PREFIX ? kc1 - 1 : off + row;
-        plo[nb] = W > 0 ? max(0, off + row - W + 1) : 0;
+        plo[nb] = max(kstart, W > 0 ? max(0, off + row - W + 1) : 0);
     }
 
     // 32x32x16 form (W32): lane l owns query row r0 + l % 32 of the wave's 32 rows; its operand
@@ -272,7 +281,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const PrefillArgs 
             qw[t] = __builtin_bit_cast(bf16x8, ok ? x : (u32x4)(0u));
         }
         prw = PREFIX ? kc1 - 1 : off + row;
-        plw = W > 0 ? max(0, off + row - W + 1) : 0;
+        plw = max(kstart, W > 0 ? max(0, off + row - W + 1) : 0);
 #pragma unroll
         for (int c = 0; c < D / 32; ++c) ow[c] = (f32x16)(0.f);
     }
@@ -458,7 +467,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const PrefillArgs 
 
     // mask, online softmax, P^T pack; returns whether O needs rescaling
     auto softmax = [&](int k0, f32x4 (&sacc)[NGA][NBR], u32x4 (&pk)[NCC][NBR], float (&alpha)[NBR]) {
-        const bool edge = (k0 + BN - 1 > wv_p_min) || (W > 0 && k0 < wv_lo_max);
+        const bool edge = (k0 + BN - 1 > wv_p_min) || (has_lo && k0 < wv_lo_max);
         if (edge) {
 #pragma unroll
             for (int ga = 0; ga < NGA; ++ga)
@@ -583,7 +592,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const PrefillArgs 
     // mask, online softmax of the lane's row, P^T packed straight from the accumulators: the
     // B operand of 16-key step (b, sg) is accumulator values 8 sg .. 8 sg + 7 of block b
     auto softmax_w = [&](int k0, f32x16 (&sw)[2], u32x4 (&pw)[2][2], float& alpha) {
-        const bool edge = (k0 + BN - 1 > wv_p_min) || (W > 0 && k0 < wv_lo_max);
+        const bool edge = (k0 + BN - 1 > wv_p_min) || (has_lo && k0 < wv_lo_max);
         if (edge) {
 #pragma unroll
             for (int b = 0; b < 2; ++b)
@@ -808,7 +817,35 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const PrefillArgs 
             if (lh == 0) *(f32x2*)(a.pre_ml + st * 2) = f32x2{mw, lt};
             return;
         }
-        const float inv = lt > 0.f ? (FP8 ? a.c.kv_scale : 1.f) / lt : 0.f;  // FP8: V / kv_scale in the cache
+        float lsum = lt;
+        if constexpr (CASC) {
+            // the prefix pass's states of this packed row and head (one per prefix chunk), folded
+            // in by log-sum-exp: both parts are in the same log2 units
+            const int64_t per_chunk = (int64_t)a.prefix_rows * H;
+            const int64_t st = (int64_t)(q0 + row) * H + h;
+            float M = mw;
+            for (int c = 0; c < a.prefix_chunks; ++c) M = fmaxf(M, a.pre_ml[(c * per_chunk + st) * 2]);
+            const float msub = M == -INFINITY ? 0.f : M;
+            const float al = __builtin_amdgcn_exp2f(mw - msub);
+            lsum *= al;
+#pragma unroll
+            for (int c = 0; c < D / 32; ++c) ow[c] *= al;
+            for (int c = 0; c < a.prefix_chunks; ++c) {
+                const f32x2 ml = *(const f32x2*)(a.pre_ml + (c * per_chunk + st) * 2);
+                const float w = __builtin_amdgcn_exp2f(ml[0] - msub);
+                lsum = fmaf(w, ml[1], lsum);
+                const float* po = a.pre_o + (c * per_chunk + st) * D + 4 * lh;
+#pragma unroll
+                for (int cc = 0; cc < D / 32; ++cc)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const f32x4 x = *(const f32x4*)(po + 32 * cc + 8 * q);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) ow[cc][4 * q + e] = fmaf(w, x[e], ow[cc][4 * q + e]);
+                    }
+            }
+        }
+        const float inv = lsum > 0.f ? (FP8 ? a.c.kv_scale : 1.f) / lsum : 0.f;  // FP8: V / kv_scale in the cache
         __bf16* dst = (__bf16*)a.out + ((int64_t)(q0 + row) * H + h) * D + 4 * lh;
 #pragma unroll
         for (int c = 0; c < D / 32; ++c)
@@ -870,8 +907,12 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t st) {
     const dim3 grid((unsigned)(nsg_pad * pg.n_tiles));
     const bool alibi = a.alibi != nullptr;
     const bool fp8 = a.c.dtype == 2;
-#define PA_PREFILL(DD, AL, F8) hipLaunchKernelGGL((prefill_bf16_kernel<DD, 2, kPrefillBN, kPrefillNBUF, AL, F8, false, kPrefillW32>), grid, dim3(256), 0, st, a, pg)
-    if (a.c.head_size == 128) {
+#define PA_PREFILL(DD, AL, F8) hipLaunchKernelGGL((prefill_bf16_kernel<DD, 2, kPrefillBN, kPrefillNBUF, AL, F8, false, kPrefillW32, false>), grid, dim3(256), 0, st, a, pg)
+#define PA_CASC(DD, F8) hipLaunchKernelGGL((prefill_bf16_kernel<DD, 2, kPrefillBN, kPrefillNBUF, false, F8, false, true, true>), grid, dim3(256), 0, st, a, pg)
+    if (a.cascade) {  // shared-prefix own-keys pass (no ALiBi, no fused store)
+        if (a.c.head_size == 128) { if (fp8) PA_CASC(128, true); else PA_CASC(128, false); }
+        else { if (fp8) PA_CASC(64, true); else PA_CASC(64, false); }
+    } else if (a.c.head_size == 128) {
         if (fp8) { if (alibi) PA_PREFILL(128, true, true); else PA_PREFILL(128, false, true); }
         else { if (alibi) PA_PREFILL(128, true, false); else PA_PREFILL(128, false, false); }
     } else {
@@ -879,6 +920,7 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t st) {
         else { if (alibi) PA_PREFILL(64, true, false); else PA_PREFILL(64, false, false); }
     }
 #undef PA_PREFILL
+#undef PA_CASC
     return hipGetLastError();
 }
 
@@ -921,11 +963,13 @@ hipError_t launch_prefix_states(const DecodeArgs& d, hipStream_t st) {
     a.prefix_chunks = d.prefix_chunks;
     a.pre_o = d.pre_o;
     a.pre_ml = d.pre_ml;
+    a.cascade = 0;
+    a.prefix_rows = d.num_seqs;
     const PrefillGrid pg = prefix_grid(d.num_seqs, d.group, d.c.num_kv_heads, d.prefix_chunks);
     const int64_t nsg_pad = ((int64_t)pg.n_sg + 7) / 8 * 8;
     const dim3 grid((unsigned)(nsg_pad * pg.n_tiles));
     const bool fp8 = a.c.dtype == 2;
-#define PA_PREFIX(DD, F8) hipLaunchKernelGGL((prefill_bf16_kernel<DD, 2, kPrefillBN, kPrefillNBUF, false, F8, true, kPrefillW32>), grid, dim3(256), 0, st, a, pg)
+#define PA_PREFIX(DD, F8) hipLaunchKernelGGL((prefill_bf16_kernel<DD, 2, kPrefillBN, kPrefillNBUF, false, F8, true, kPrefillW32, false>), grid, dim3(256), 0, st, a, pg)
     if (a.c.head_size == 128) {
         if (fp8) PA_PREFIX(128, true); else PA_PREFIX(128, false);
     } else {

@@ -198,3 +198,31 @@ def check_cascade(seq_lens, block_table, max_seq_len: int, common_prefix_len: in
         c = int(np.argmax(table[s, :nb] != table[0, :nb]))
         raise ValueError(f"block_table[{s}, {c}] = {int(table[s, c])} differs from row 0's "
                          f"{int(table[0, c])} inside the shared prefix")
+
+
+def check_cascade_prefill(cu_seqlens_q, cu_seqlens_k, block_table, max_seqlen_q: int, max_seqlen_k: int,
+                          common_prefix_len: int, num_blocks: int, block_size: int, query_rows: int) -> None:
+    """pa_cascade_prefill_varlen's device-content preconditions: those of pa_prefill_varlen, every
+    sequence's first query row at or after the prefix's last key, and the prefix blocks shared by
+    every block-table row."""
+    check_prefill(cu_seqlens_q, cu_seqlens_k, block_table, max_seqlen_q, max_seqlen_k, 0, num_blocks, block_size,
+                  query_rows)
+    if common_prefix_len <= 0:
+        return
+    cq = _host(cu_seqlens_q).astype(np.int64).reshape(-1)
+    ck = _host(cu_seqlens_k).astype(np.int64).reshape(-1)
+    table = _host(block_table).astype(np.int64)
+    num_seqs = cq.shape[0] - 1
+    first = (ck[1:] - ck[:-1]) - (cq[1:] - cq[:-1])
+    early = np.nonzero(first + 1 < common_prefix_len)[0]
+    if early.size:
+        s = int(early[0])
+        raise ValueError(f"sequence {s}: its first query row (position {int(first[s])}) lies inside the shared "
+                         f"prefix of {common_prefix_len} keys")
+    nb = common_prefix_len // block_size
+    diff = np.nonzero((table[:num_seqs, :nb] != table[0, :nb]).any(axis=1))[0]
+    if diff.size:
+        s = int(diff[0])
+        c = int(np.argmax(table[s, :nb] != table[0, :nb]))
+        raise ValueError(f"block_table[{s}, {c}] = {int(table[s, c])} differs from row 0's "
+                         f"{int(table[0, c])} inside the shared prefix")

@@ -225,3 +225,27 @@ def test_decode_no_alloc_refuses_splits_beyond_its_scratch(lib):
     assert lib.pa_decode_no_alloc(d, None, None, None, 1, None, 0, 0, 32, 1.0, 0, None, 0, None) == 0
     # bad scalars are still rejected as by pa_decode
     assert lib.pa_decode_no_alloc(d, FAKE, FAKE, FAKE, 300, FAKE, 64, 4097, 32, 0.1, 0, None, 48, None) == 1
+
+
+def test_cascade_prefill_checks_and_workspace(lib):
+    """pa_cascade_prefill_varlen: host-side rejections before any HIP call, and the workspace
+    formula (states of every packed row and head per prefix chunk)."""
+    d = desc(nb=1000, bs=16, hkv=8, d=128)
+    P = ctypes.c_void_p
+    def call(dd=None, prefix=64, tokens=100, ws=None, nbytes=0, max_k=300, nseq=2, scale=0.1):
+        return lib.pa_cascade_prefill_varlen(dd or d, FAKE, FAKE, FAKE, 64, FAKE, FAKE, nseq, 80, max_k, 32,
+                                             scale, prefix, tokens, ws, nbytes, None)
+    assert call(desc(dtype=0)) == 2 and b"bf16" in lib.pa_last_error()
+    assert call(prefix=24) == 1 and b"multiple of block_size" in lib.pa_last_error()
+    assert call(prefix=320) == 1 and b"exceeds max_seqlen_k" in lib.pa_last_error()
+    assert call(scale=-1.0) == 1
+    assert call(tokens=-1) == 1
+    assert call(tokens=0) == 1 and b"num_tokens is 0" in lib.pa_last_error()
+    assert call(nseq=0, tokens=0) == 0                       # empty batch: no-op
+    need = lib.pa_cascade_prefill_varlen_workspace_size(d, 100, 32, 64)
+    assert need > 0 and need % (100 * 32 * 130 * 4) == 0     # whole prefix chunks of states
+    assert call(ws=FAKE, nbytes=need - 1) == 3
+    assert call(ws=None, nbytes=0) == 3
+    assert call(ws=FAKE + 4, nbytes=need) == 1 and b"aligned" in lib.pa_last_error()
+    assert lib.pa_cascade_prefill_varlen_workspace_size(d, 100, 32, 0) == 0
+    assert lib.pa_cascade_prefill_varlen_workspace_size(desc(dtype=0), 100, 32, 64) == 0

@@ -10,7 +10,7 @@ import torch
 
 import oracle
 import workloads as W
-from tests.gpu_helpers import GpuRun, assert_close, host_values, say
+from tests.gpu_helpers import GpuRun, assert_close, bits, host_values, say
 
 pytestmark = pytest.mark.gpu
 
@@ -206,3 +206,109 @@ def test_cascade_empty_batch_and_all_context_shared():
             ref = oracle.cascade_decode(host_values(dec.query), vals, dec.block_table, lens, wl.scale,
                                         wl.num_kv_heads, P - 16)
             assert_close(out.float().cpu().numpy(), ref, wl.dtype, f"all shared B {B} p{part}")
+
+
+# ----------------------------------------------------------------------------- query chunks
+
+
+CASCADE_PREFILL_CASES = {
+    # name: (H, Hkv, D, BS, shared prefix, [(context, query rows)])
+    "g4_d128_p48": (32, 8, 128, 16, 48, [(48, 1), (60, 37), (300, 64), (49, 130)]),
+    "g5_d128_p256": (10, 2, 128, 16, 256, [(256, 90), (500, 33), (270, 1), (1000, 200)]),
+    "g8_d64_bs32_p128": (16, 2, 64, 32, 128, [(128, 70), (200, 1), (129, 64)]),
+    "g1_d128_p64": (4, 4, 128, 16, 64, [(64, 100), (80, 31)]),
+    "g4_d128_many_rows_p512": (32, 8, 128, 16, 512, [(512 + 7 * i, 40 + 3 * i) for i in range(8)]),
+}
+
+
+def _cascade_prefill(run, op, P, workspace=None):
+    import paged_attention_block_amd as pa
+    wl = run.wl
+    return pa.pa_cascade_prefill_varlen(op.query.to(DEV), run.cache, run.i32(op.block_table),
+                                        run.i32(op.cu_seqlens_q), run.i32(op.cu_seqlens_k), op.max_seqlen_q,
+                                        op.max_seqlen_k, wl.scale, wl.num_kv_heads, P, workspace=workspace,
+                                        kv_scale=run.kv_scale, validate=True)
+
+
+def _prefill_case(name, seed, cache_dtype=None):
+    H, Hkv, D, BS, P, spec = CASCADE_PREFILL_CASES[name]
+    seqs = [W.SeqSpec(c, [q], ["prefill"]) for c, q in spec]
+    return W.build(name, seed, seqs, num_heads=H, num_kv_heads=Hkv, head_size=D, block_size=BS,
+                   dtype=torch.bfloat16, shared_prefix=P, cache_dtype=cache_dtype), P
+
+
+@pytest.mark.parametrize("name", sorted(CASCADE_PREFILL_CASES))
+def test_cascade_prefill_small(name):
+    """Every output against the cascade oracle (pinned to plain prefill and SDPA), and against
+    pa_prefill_varlen on the same cache.  The cases run both prefix passes (split-key below 512
+    (row, head) pairs per KV head, the prefill kernel above), prefixes that end inside a 64-key
+    tile, single-row chunks next to long ones, and head sizes 64 / 128."""
+    import paged_attention_block_amd as pa
+    wl, P = _prefill_case(name, 410)
+    run = GpuRun(wl, DEV)
+    store, pre = wl.phases[0]
+    run.run(store)
+    say(f"[cascade prefill {name}] rows {int(pre.cu_seqlens_q[-1])} prefix {P}")
+    out = _cascade_prefill(run, pre, P)
+    plain = run.run(pre)
+    torch.cuda.synchronize()
+    vals = host_values(run.cache.cpu())
+    ref = oracle.cascade_prefill_varlen(host_values(pre.query), vals, pre.block_table, pre.cu_seqlens_q,
+                                        pre.cu_seqlens_k, wl.scale, wl.num_kv_heads, P)
+    err = assert_close(out.float().cpu().numpy(), ref, wl.dtype, f"cascade prefill {name}")
+    assert_close(plain.float().cpu().numpy(), ref, wl.dtype, f"plain prefill {name}")
+    say(f"[cascade prefill {name}] max abs err {err:.3e}")
+
+
+def test_cascade_prefill_fp8():
+    from oracle import fp8
+    wl, P = _prefill_case("g5_d128_p256", 411, cache_dtype=torch.float8_e4m3fn)
+    run = GpuRun(wl, DEV)
+    run.kv_scale = 0.5
+    store, pre = wl.phases[0]
+    before = bits(wl.kv_cache)
+    run.run(store)
+    say("[cascade prefill fp8]")
+    out = _cascade_prefill(run, pre, P)
+    torch.cuda.synchronize()
+    vals = fp8.dequantize(fp8.store_kv_fp8(before, store.key.float().numpy(), store.value.float().numpy(),
+                                           store.slot_mapping, 0.5), 0.5)
+    ref = oracle.cascade_prefill_varlen(host_values(pre.query), vals, pre.block_table, pre.cu_seqlens_q,
+                                        pre.cu_seqlens_k, wl.scale, wl.num_kv_heads, P)
+    assert_close(out.float().cpu().numpy(), ref, torch.bfloat16, "cascade prefill fp8")
+
+
+def test_cascade_prefill_full_size():
+    """8 sequences sharing a 2048-key prefix, cached contexts U[2048, 4096], a 512-row chunk
+    each, H 32/8, D 128: every output against the oracle's plain prefill definition (which the
+    cascade oracle is pinned to equal; the row-by-row cascade oracle takes minutes here)."""
+    wl = W.shared_prefix_prefill()
+    run = GpuRun(wl, DEV)
+    store, pre = wl.phases[0]
+    run.run(store)
+    say("[cascade prefill full size] 8 x 512 rows, prefix 2048")
+    out = _cascade_prefill(run, pre, 2048)
+    torch.cuda.synchronize()
+    vals = host_values(run.cache.cpu())
+    ref = oracle.prefill_varlen(host_values(pre.query), vals, pre.block_table, pre.cu_seqlens_q,
+                                pre.cu_seqlens_k, wl.scale, wl.num_kv_heads)
+    err = assert_close(out.float().cpu().numpy(), ref, wl.dtype, "cascade prefill full size")
+    say(f"[cascade prefill full size] max abs err {err:.3e}")
+
+
+def test_cascade_prefill_workspace_needs_no_init_and_zero_prefix_is_plain():
+    import paged_attention_block_amd as pa
+    wl, P = _prefill_case("g4_d128_p48", 412)
+    run = GpuRun(wl, DEV)
+    store, pre = wl.phases[0]
+    run.run(store)
+    rows = int(pre.cu_seqlens_q[-1])
+    need = pa.pa_cascade_prefill_varlen_workspace_size(run.cache, rows, wl.num_heads, P)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device=DEV)
+    a = _cascade_prefill(run, pre, P, workspace=ws)
+    b = _cascade_prefill(run, pre, P)
+    zero = _cascade_prefill(run, pre, 0)
+    plain = run.run(pre)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert torch.equal(zero.view(torch.int16), plain.view(torch.int16))

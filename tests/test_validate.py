@@ -148,3 +148,21 @@ def test_cascade_violations():
     bad[1, 1] = 4
     with pytest.raises(ValueError, match=r"block_table\[1, 1\] = 4 differs"):
         V.check_cascade(np.array([40, 33], np.int32), bad, 48, 32, 8, 16)
+
+
+def test_cascade_prefill_workload_passes_and_violations_raise():
+    wl = W.shared_prefix_prefill(seed=7, num_seqs=3, prefix=64, lo=64, hi=150, chunk=20, num_heads=4,
+                                 num_kv_heads=2, head_size=64)
+    pre = wl.phases[0][1]
+    args = (pre.cu_seqlens_q, pre.cu_seqlens_k, pre.block_table, pre.max_seqlen_q, pre.max_seqlen_k)
+    V.check_cascade_prefill(*args, 64, wl.num_blocks, wl.block_size, pre.query.shape[0])
+    table = np.array([[2, 5, 6], [2, 5, 1]], np.int32)
+    cu_q = np.array([0, 4, 10], np.int32)
+    V.check_cascade_prefill(cu_q, np.array([0, 40, 80], np.int32), table, 6, 40, 32, 8, 16, 10)
+    # second sequence: 30 keys with 6 query rows -> first row at 24, inside a 32-key prefix
+    with pytest.raises(ValueError, match="inside the shared prefix"):
+        V.check_cascade_prefill(cu_q, np.array([0, 40, 70], np.int32), table, 6, 40, 32, 8, 16, 10)
+    bad = table.copy()
+    bad[1, 1] = 4
+    with pytest.raises(ValueError, match=r"block_table\[1, 1\] = 4 differs"):
+        V.check_cascade_prefill(cu_q, np.array([0, 40, 80], np.int32), bad, 6, 40, 32, 8, 16, 10)

@@ -2,5 +2,5 @@
 
 from .gen import (  # noqa: F401
     CONFIG_NAMES, CopyOp, DecodeOp, PrefillOp, SeqSpec, StoreOp, Workload, build, config,
-    cu_seqlens, shared_prefix_decode, slot_mapping,
+    cu_seqlens, shared_prefix_decode, shared_prefix_prefill, slot_mapping,
 )

@@ -29,6 +29,7 @@ import torch
 __all__ = [
     "SeqSpec", "StoreOp", "CopyOp", "PrefillOp", "DecodeOp", "Workload",
     "cu_seqlens", "slot_mapping", "build", "config", "CONFIG_NAMES", "shared_prefix_decode",
+    "shared_prefix_prefill",
 ]
 
 
@@ -284,3 +285,20 @@ def shared_prefix_decode(seed: int = 6, num_seqs: int = 64, prefix: int = 1024, 
     return build(f"shared_prefix{prefix}_b{num_seqs}", seed, seqs, num_heads=num_heads,
                  num_kv_heads=num_kv_heads, head_size=head_size, block_size=block_size, dtype=dtype,
                  rng=rng, shared_prefix=prefix, cache_dtype=cache_dtype)
+
+
+def shared_prefix_prefill(seed: int = 7, num_seqs: int = 8, prefix: int = 2048, lo: int = 2048,
+                          hi: int = 4096, chunk: int = 512, num_heads: int = 32, num_kv_heads: int = 8,
+                          head_size: int = 128, block_size: int = 16,
+                          dtype: torch.dtype = torch.bfloat16,
+                          cache_dtype: Optional[torch.dtype] = None) -> Workload:
+    """One chunked-prefill step of ``num_seqs`` sequences that share their first ``prefix``
+    keys (one system prompt from the prefix cache): cached contexts U[lo, hi] (at least
+    ``prefix``), each with a ``chunk``-token query chunk, the GQA shape otherwise."""
+    rng = np.random.default_rng(seed)
+    ctx = rng.integers(max(lo, prefix), hi + 1, size=num_seqs)
+    seqs = [SeqSpec(int(c), [chunk], ["prefill"]) for c in ctx]
+    return build(f"shared_prefix_prefill{prefix}_b{num_seqs}", seed, seqs, num_heads=num_heads,
+                 num_kv_heads=num_kv_heads, head_size=head_size, block_size=block_size, dtype=dtype,
+                 rng=rng, shared_prefix=prefix, cache_dtype=cache_dtype)
+
