@@ -170,6 +170,11 @@ class Step:
                 d.update(q=op.query.to(dev), table=i32(op.block_table), cuq=i32(op.cu_seqlens_q),
                          cuk=i32(op.cu_seqlens_k))
                 d["out"] = torch.empty_like(d["q"])
+                d["cascade"] = cascade
+                if cascade:
+                    need = pa.pa_cascade_prefill_varlen_workspace_size(self.cache, op.query.shape[0],
+                                                                       wl.num_heads, cascade)
+                    d["ws"] = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
             elif name == "DecodeOp":
                 d.update(q=op.query.to(dev), table=i32(op.block_table), lens=i32(op.seq_lens))
                 d["out"] = torch.empty_like(d["q"])
@@ -197,6 +202,10 @@ class Step:
                                             d["cuq"], d["cuk"], op.max_seqlen_q, op.max_seqlen_k, wl.scale,
                                             wl.num_kv_heads, wl.sliding_window, out=d["out"],
                                             alibi_slopes=self.slopes)
+        elif name == "PrefillOp" and d.get("cascade"):
+            pa.pa_cascade_prefill_varlen(d["q"], self.cache, d["table"], d["cuq"], d["cuk"], op.max_seqlen_q,
+                                         op.max_seqlen_k, wl.scale, wl.num_kv_heads, d["cascade"], out=d["out"],
+                                         workspace=d["ws"])
         elif name == "PrefillOp":
             pa.pa_prefill_varlen(d["q"], self.cache, d["table"], d["cuq"], d["cuk"], op.max_seqlen_q,
                                  op.max_seqlen_k, wl.scale, wl.num_kv_heads, wl.sliding_window, out=d["out"],
@@ -403,12 +412,17 @@ def roofline(achieved, peak, unit, bound, traffic=None):
             "frac": round(achieved / peak, 4), "traffic": traffic}
 
 
-# shared-prefix decode batches: name -> (sequences, shared prefix keys, context range)
-SHARED_PREFIX = {"b64_p1024": (64, 1024, 1024, 4096), "b256_p4096": (256, 4096, 4096, 8192)}
+# shared-prefix batches: name -> (sequences, shared prefix keys, context range, query rows per
+# sequence: 1 = a decode step, more = a chunked-prefill step)
+SHARED_PREFIX = {"b64_p1024": (64, 1024, 1024, 4096, 1), "b256_p4096": (256, 4096, 4096, 8192, 1),
+                 "prefill_b8_p2048": (8, 2048, 2048, 4096, 512)}
 
 
 def shared_prefix_name(key):
-    b, p, lo, hi = SHARED_PREFIX[key]
+    b, p, lo, hi, rows = SHARED_PREFIX[key]
+    if rows > 1:
+        return (f"shared-prefix chunked prefill: B {b} x {rows}-row chunks, prefix {p} keys shared, "
+                f"ctx U[{lo},{hi}], H 32/8, D 128, bs 16, bf16")
     return f"shared-prefix decode: B {b}, prefix {p} keys shared, ctx U[{lo},{hi}], H 32/8, D 128, bs 16, bf16"
 
 
@@ -423,7 +437,9 @@ def _workload(n):
                        head_size=c2.head_size, block_size=c2.block_size, dtype=torch.bfloat16,
                        cache_dtype=torch.float8_e4m3fn)
     if isinstance(n, str) and n in SHARED_PREFIX:
-        b, p, lo, hi = SHARED_PREFIX[n]
+        b, p, lo, hi, rows = SHARED_PREFIX[n]
+        if rows > 1:
+            return W.shared_prefix_prefill(num_seqs=b, prefix=p, lo=lo, hi=hi, chunk=rows)
         return W.shared_prefix_decode(num_seqs=b, prefix=p, lo=lo, hi=hi)
     return W.config(n)
 
@@ -477,7 +493,7 @@ def bench_workload(name, steps, warmup, dev, with_cpu, partition_size=0, flush_m
         elif n == "PrefillOp":
             f = prefill_flops(op, wl)
             total_flops += f
-            res["ops"]["prefill_with_store" if fused else "prefill"] = {
+            res["ops"]["prefill_with_store" if fused else ("cascade_prefill" if cascade else "prefill")] = {
                 "ms": round(t * 1e3, 4), "TFLOP/s": round(f / t / 1e12, 2), "flops": f,
                 "roofline": roofline(f / t / 1e12, BF16_PEAK_TFLOPS, "TFLOP/s", "mfma",
                                      read_traffic("prefill") if name == "prefill" and not fused and not alibi else None)}
@@ -609,11 +625,11 @@ def main() -> int:
         r = bench_workload("fp8_decode", 30, 5, dev, False, flush_mb=args.flush_mb)
         line["fp8"] = {"workload": r["workload"], "ms_per_step": r["ms_per_step"], "step_GB/s": r["step_GB/s"],
                        "ops": r["ops"]}
-        # batches sharing a prefix of cached blocks: plain decode, then cascade decode
+        # batches sharing a prefix of cached blocks: plain decode / prefill, then the cascade form
         line["shared_prefix"] = {}
         for key in SHARED_PREFIX:
             line["shared_prefix"][key] = {}
-            for kind, casc in (("decode", False), ("cascade", True)):
+            for kind, casc in (("plain", False), ("cascade", True)):
                 r = bench_workload(key, 20, 5, dev, False, flush_mb=args.flush_mb, cascade=casc)
                 line["shared_prefix"][key][kind] = {"workload": r["workload"], "ms_per_step": r["ms_per_step"],
                                                     "ops": r["ops"]}
