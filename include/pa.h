@@ -158,8 +158,11 @@ int pa_prefill_varlen(const pa_cache_desc* cache, void* out, const void* query,
  *   num_tokens    == cu_seqlens_q[num_seqs] (the rows of query, key and value)
  * Other arguments as pa_prefill_varlen.  Precondition (as in the paged layout everywhere):
  * the slot of the new token at key position j of sequence s is the block-table position of
- * j, so attending the stored cache and attending key/value give the same keys.  Result and
- * cache contents equal pa_store_kv followed by pa_prefill_varlen.
+ * j (in particular not negative), so attending the stored cache and attending key/value give
+ * the same keys.  Result and cache contents then equal pa_store_kv followed by
+ * pa_prefill_varlen.  Outside it, a negative slot leaves its token unstored and the rows that
+ * attend that key see the given key/value row (bf16 cache) or the cache's old contents at the
+ * key's position (float32 and FP8 caches, which run the store first).
  */
 int pa_prefill_varlen_with_store(const pa_cache_desc* cache, void* out, const void* query,
                                  const void* key, const void* value, const int32_t* slot_mapping,
@@ -215,9 +218,12 @@ int pa_decode(const pa_cache_desc* cache, void* out, const void* query,
  * [head_size] and slot_mapping [num_seqs]: the token just produced by each sequence, which
  * seq_lens already counts.  Other arguments as pa_decode.  With a bf16 cache it is one partition
  * launch (plus the merge): the workgroup holding a sequence's last key takes that key's K/V from
- * key/value rather than the cache, and writes the rows to slot_mapping[s] (negative: not written;
- * the attention still uses the given rows, as pa_prefill_varlen_with_store does).  With a float32
- * or FP8 cache the store kernel runs first, then the decode kernels.
+ * key/value rather than the cache, and writes the rows to slot_mapping[s].  With a float32 or FP8
+ * cache the store kernel runs first, then the decode kernels.  Precondition as
+ * pa_prefill_varlen_with_store: slot_mapping[s] is the block-table position of key
+ * seq_lens[s] - 1; a sequence with seq_lens[s] == 0 has no new token and takes a negative slot.
+ * Outside it, a negative slot leaves the token unstored and the query sees the given row (bf16)
+ * or the cache's old contents (float32, FP8).
  */
 int pa_decode_with_store(const pa_cache_desc* cache, void* out, const void* query, const void* key,
                          const void* value, const int32_t* slot_mapping, const int32_t* block_table,

@@ -134,7 +134,11 @@ def check_decode(seq_lens, block_table, max_seq_len: int, sliding_window: int, n
 def _check_slot_is_table_position(slot: int, table: np.ndarray, s: int, pos: int, block_size: int,
                                   what: str) -> None:
     if slot < 0:
-        return
+        # a fused call attends every new token it stores: leaving one unstored is outside its
+        # precondition (the rows attending that key would see the given row with a bf16 cache but
+        # the old cache row with float32 and FP8 caches, which store before attending)
+        raise ValueError(f"{what}: negative slot {slot}: the fused store-and-attend calls need a slot for every "
+                         f"new token (key position {pos} of sequence {s})")
     want = int(table[s, pos // block_size]) * block_size + pos % block_size
     if slot != want:
         raise ValueError(f"{what}: slot {slot}, but key position {pos} of sequence {s} sits at slot "

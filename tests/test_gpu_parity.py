@@ -510,3 +510,61 @@ def test_validate_flag_gpu():
     # the decode query as the last row of a 3-key prefill: another kernel, the same result
     torch.testing.assert_close(c, a, rtol=1e-5, atol=1e-5)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32", "fp8"])
+def test_fused_store_negative_slot_is_left_unstored(dt):
+    """Outside the fused calls' precondition: a negative slot leaves its token unstored, with
+    every cache dtype.  The whole cache equals the oracle's store (which skips the token) bit for
+    bit, and every query row that does not attend the unstored key matches the oracle's store +
+    attention (prefill: each sequence's last token unstored, which only its last row attends;
+    decode: one sequence's new token unstored, the other sequences checked)."""
+    from oracle import fp8
+    dtype = torch.float32 if dt == "f32" else torch.bfloat16
+    cdt = torch.float8_e4m3fn if dt == "fp8" else None
+    D = 64 if dt == "f32" else 128
+    kv_scale = 0.5 if dt == "fp8" else 1.0
+
+    def oracle_cache(before, store, slots):
+        if dt == "fp8":
+            enc = fp8.store_kv_fp8(before, store.key.float().numpy(), store.value.float().numpy(), slots, kv_scale)
+            return enc, fp8.dequantize(enc, kv_scale)
+        b = oracle.store_kv(before, bits(store.key), bits(store.value), slots)
+        return b, host_values(torch.from_numpy(b).view(wl.kv_cache.dtype))
+
+    # prefill: the last new token of every sequence gets slot -1
+    seqs = [W.SeqSpec(20, [37], ["prefill"]), W.SeqSpec(0, [50], ["prefill"]), W.SeqSpec(70, [1], ["prefill"])]
+    wl = W.build(f"negslot_p_{dt}", 700, seqs, num_heads=8, num_kv_heads=2, head_size=D, block_size=16,
+                 dtype=dtype, cache_dtype=cdt)
+    store, pre = wl.phases[0]
+    slots = store.slot_mapping.copy()
+    last_rows = [int(x) - 1 for x in pre.cu_seqlens_q[1:]]
+    slots[last_rows] = -1
+    run = GpuRun(wl, DEV)
+    run.kv_scale = kv_scale
+    say(f"[fused negative slot {dt}] prefill")
+    out = run.run_with_store(W.StoreOp(store.key, store.value, slots), pre)
+    torch.cuda.synchronize()
+    ref_bits, vals = oracle_cache(bits(wl.kv_cache), store, slots)
+    np.testing.assert_array_equal(bits(run.cache.cpu()), ref_bits)
+    ref = oracle.prefill_varlen(host_values(pre.query), vals, pre.block_table, pre.cu_seqlens_q, pre.cu_seqlens_k,
+                                wl.scale, wl.num_kv_heads)
+    keep = np.setdiff1d(np.arange(pre.query.shape[0]), last_rows)
+    assert_close(out.float().cpu().numpy()[keep], ref[keep], dtype, f"fused negative slot {dt} prefill")
+
+    # decode: sequence 1's new token gets slot -1
+    seqs = [W.SeqSpec(c, [1], ["decode"]) for c in (100, 30, 7)]
+    wl = W.build(f"negslot_d_{dt}", 701, seqs, num_heads=8, num_kv_heads=2, head_size=D, block_size=16,
+                 dtype=dtype, cache_dtype=cdt)
+    store, dec = wl.phases[0]
+    slots = store.slot_mapping.copy()
+    slots[1] = -1
+    run = GpuRun(wl, DEV)
+    run.kv_scale = kv_scale
+    say(f"[fused negative slot {dt}] decode")
+    out = run.run_with_store(W.StoreOp(store.key, store.value, slots), dec, partition_size=32)
+    torch.cuda.synchronize()
+    ref_bits, vals = oracle_cache(bits(wl.kv_cache), store, slots)
+    np.testing.assert_array_equal(bits(run.cache.cpu()), ref_bits)
+    ref = oracle.decode(host_values(dec.query), vals, dec.block_table, dec.seq_lens, wl.scale, wl.num_kv_heads)
+    assert_close(out.float().cpu().numpy()[[0, 2]], ref[[0, 2]], dtype, f"fused negative slot {dt} decode")

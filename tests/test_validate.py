@@ -128,7 +128,13 @@ def test_store_fused_violations():
     # prefill of 3 new tokens at positions 17..19 of a 20-key sequence: slots 5*16 + 1..3
     cq, ck = np.array([0, 3], np.int32), np.array([0, 20], np.int32)
     V.check_prefill_with_store(np.array([81, 82, 83], np.int32), cq, ck, table, 3, 20, 0, 8, 16, 3)
-    V.check_prefill_with_store(np.array([81, -1, 83], np.int32), cq, ck, table, 3, 20, 0, 8, 16, 3)
+    # a fused call stores every new token: a negative slot is outside its precondition
+    with pytest.raises(ValueError, match=r"slot_mapping\[1\]: negative slot -1"):
+        V.check_prefill_with_store(np.array([81, -1, 83], np.int32), cq, ck, table, 3, 20, 0, 8, 16, 3)
+    with pytest.raises(ValueError, match="negative slot"):
+        V.check_decode_with_store(np.array([-1], np.int32), np.array([20], np.int32), table, 32, 0, 8, 16)
+    V.check_decode_with_store(np.array([83, -1], np.int32), np.array([20, 0], np.int32),
+                              np.array([[2, 5], [1, 3]], np.int32), 32, 0, 8, 16)   # seq_len 0: no new token
     with pytest.raises(ValueError, match=r"slot_mapping\[2\]: slot 84"):
         V.check_prefill_with_store(np.array([81, 82, 84], np.int32), cq, ck, table, 3, 20, 0, 8, 16, 3)
     with pytest.raises(ValueError, match="new tokens but only"):
