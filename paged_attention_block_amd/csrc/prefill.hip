@@ -23,7 +23,7 @@
 // i/4 + 4j, so when source lane s addresses row base + s/4, dims d0 + 4*(s%4), lane i
 // receives 4 consecutive keys at dim d0 + i -- the MFMA layout, from a row-major tile.
 // LDS rows are packed; the 16-byte chunks of row r are XOR-swizzled (K: chunk ^ (r & 15),
-// V: chunk ^ 2*(r & 7)) so the operand reads hit distinct banks.  The swizzle is applied
+// V: chunk ^ 4*(r & 3)) so the operand reads hit distinct banks.  The swizzle is applied
 // on the global side: a lane fetches the global chunk that belongs at its fixed LDS slot.
 //
 // Tiles outside the union of the rows' live key ranges are never visited; inside a
@@ -148,7 +148,12 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const PrefillArgs 
     constexpr int NQ = BN / RPI;      // copy instructions per plane per tile
     constexpr int TILE = BN * D * 2;  // bytes of one plane of one tile
     constexpr int KSW = CPR >= 16 ? 15 : CPR - 1;        // K swizzle mask
-    constexpr int VSW = CPR >= 16 ? 14 : CPR - 2;        // V swizzle mask (even values)
+    // V swizzle: chunk c of row r sits at slot c ^ vswz(r).  The transposing V^T reads of
+    // lanes 0-31 cover rows r0..r0+3 and four consecutive chunks; XOR with 4 * (r & 3) puts the
+    // 16 (row, chunk) pairs on distinct slots of a 256-byte row span, which keeps these 8-byte
+    // reads free of LDS bank conflicts (counter: 0; the earlier 2 * (r & 7) pattern had two-way
+    // conflicts on a third of the LDS-active cycles)
+    auto vswz = [](int r) { return (4 * (r & 3)) & (CPR - 1); };
     constexpr int ELT = FP8 ? 1 : 2;  // bytes per cache element
     static_assert(!FP8 || NBUF == 2, "the FP8 copy stages one tile in registers");
     static_assert(!W32 || BN == 64, "the 32x32x16 form takes 64-key tiles as two 32-key blocks");
@@ -320,7 +325,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const PrefillArgs 
         const int ig = csub + nsub * jj;   // instruction within the group
         const int row = RPI * ig + crow;   // token row within the group (0..15)
         const int ck = cslot ^ (row & KSW);
-        const int cv = cslot ^ ((2 * row) & VSW);
+        const int cv = cslot ^ vswz(row);
         cgk[jj] = (uint32_t)(((row * Hkv + g) * D + ck * 8) * ELT);
         cgv[jj] = (uint32_t)(((row * Hkv + g) * D + cv * 8) * ELT);
         my_copies += (copier && ig < IPG) ? 2 : 0;
@@ -443,7 +448,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const PrefillArgs 
     // V^T: source lane col of group grp addresses row 32cc + 16hh + 4*grp + col/4, dims
     // 16*db + 4*(col%4) .. +4; the row's swizzle depends on (row & 7) = (4*grp + col/4) & 7
     const int vrow0 = 4 * grp + (col >> 2);
-    const int vsw = (2 * vrow0) & VSW;
+    const int vsw = vswz(vrow0);
     const uint32_t voff_base = (uint32_t)(vrow0 * D * 2 + 8 * (col & 1));
     const int vch = (col & 3) >> 1;  // chunk within the 16-dim block
 
@@ -647,7 +652,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const PrefillArgs 
     const int vsl = lane & 15;
     const int vroww = 4 * (vgw >> 1) + (vsl >> 2);
     const uint32_t vbasew = (uint32_t)(vroww * D * 2 + 8 * (vsl & 1));
-    const int vsww = (2 * vroww) & VSW;  // rows shifted by multiples of 8: same swizzle
+    const int vsww = vswz(vroww);  // rows shifted by multiples of 4: same swizzle
     auto pv_w = [&](const char* vt, const u32x4 (&pw)[2][2], float alpha) {
         if (__any(alpha != 1.f)) {
 #pragma unroll
@@ -709,7 +714,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const PrefillArgs 
             if (slot < 0) continue;
             const int r = key - k0;                            // row in the tile
             const u32x4 kx = *(const u32x4*)(kc + r * D * 2 + ((c ^ (r & KSW)) * 16));
-            const u32x4 vx = *(const u32x4*)(vc + r * D * 2 + ((c ^ ((2 * r) & VSW)) * 16));
+            const u32x4 vx = *(const u32x4*)(vc + r * D * 2 + ((c ^ vswz(r)) * 16));
             const int64_t dst = ((int64_t)slot * Hkv + g) * D * 2 + c * 16;
             *(u32x4*)((char*)a.c.kv + dst) = kx;
             *(u32x4*)((char*)a.c.kv + vdelta + dst) = vx;
