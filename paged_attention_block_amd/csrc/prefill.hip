@@ -88,13 +88,18 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Waves per workgroup (W): the workgroup's waves share each K/V tile staged in LDS.  Four
+// waves, two workgroups per CU, measured faster than one 8-wave workgroup per CU sharing
+// every tile (whose waves run the same stage at the same time on a SIMD).
+constexpr int kPrefillWaves = 4;
+
 // Work decomposition.  A q-tile is rb blocks of 32 query rows of one (sequence, KV head);
-// its (query head of the group, row block) pairs, row block major, are dealt four at a time
-// to 4-wave workgroups (rb = 4 / gcd(G, 4), so the G * rb pairs fill whole workgroups for
-// every group size G and no wave idles).
+// its (query head of the group, row block) pairs, row block major, are dealt W at a time to
+// W-wave workgroups (rb = W / gcd(G, W), so the G * rb pairs fill whole workgroups for every
+// group size G and no wave idles).
 struct PrefillGrid {
     int rb;             // 32-row blocks per q-tile
-    int wgs_per_tile;   // G * rb / 4
+    int wgs_per_tile;   // G * rb / W
     int n_sg;           // num_seqs * num_kv_heads
     int n_tiles;        // ceil(max_seqlen_q / (32 * rb)) * wgs_per_tile
 };
@@ -136,7 +141,8 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 // prefix_len on (keys below it are masked like a window's), and the epilogue folds in, by
 // log-sum-exp, the states the prefix pass left for the same packed query row and head.
 template <int D, int NBR, int BN, int NBUF, bool ALIBI, bool FP8, bool PREFIX, bool W32, bool CASC>
-__global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const PrefillArgs a, const PrefillGrid pg) {
+__global__ __launch_bounds__(64 * kPrefillWaves, 8 / kPrefillWaves) void prefill_bf16_kernel(const PrefillArgs a,
+                                                                                              const PrefillGrid pg) {
     constexpr int NGA = BN / 16;      // 16-key groups per K/V tile
     constexpr int NCC = BN / 32;      // 32-key chunks per K/V tile (PV MFMA k-steps)
     constexpr int RPW = 16 * NBR;     // query rows per wave (NBR blocks of 16)
@@ -189,10 +195,10 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const PrefillArgs 
     const int q0 = PREFIX ? 0 : a.cu_q[s];
     const int sq = PREFIX ? a.num_seqs : a.cu_q[s + 1] - q0;
     const int i0 = qt * 32 * pg.rb;
-    // the rows of this workgroup's pairs: row blocks (4 jw) / G .. (4 jw + 3) / G
-    const int wg_row0 = i0 + 32 * ((4 * jw) / G);
+    // the rows of this workgroup's pairs: row blocks (W jw) / G .. (W jw + W - 1) / G
+    const int wg_row0 = i0 + 32 * ((kPrefillWaves * jw) / G);
     if (wg_row0 >= sq) return;
-    const int wg_row_end = min(i0 + 32 * ((4 * jw + 3) / G + 1), sq);
+    const int wg_row_end = min(i0 + 32 * ((kPrefillWaves * jw + kPrefillWaves - 1) / G + 1), sq);
     // PREFIX: chunk pc of the prefix = 64-key tiles [tb, te), keys [kc0, kc1)
     int kc0 = 0, kc1 = 0;
     if constexpr (PREFIX) {
@@ -215,7 +221,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const PrefillArgs 
     const int lane = tid & 63;
     const int col = lane & 15;
     const int grp = lane >> 4;
-    const int pair = 4 * jw + wave;        // (head, row block) pair of this wave
+    const int pair = kPrefillWaves * jw + wave;  // (head, row block) pair of this wave
     const int hig = pair % G;              // head within the group
     const bool wave_ok = pair < G * pg.rb;
     const int h = g * G + hig;
@@ -709,7 +715,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const PrefillArgs 
             const int key = ks + idx / CH;
             const int c = idx % CH;
             const int i = key - off;                           // query row of the token
-            if (((i - i0) / 32 * G) / 4 != jw) continue;       // another workgroup's row block
+            if (((i - i0) / 32 * G) / kPrefillWaves != jw) continue;  // another workgroup's row block
             const int slot = lds_slots[i - i0];
             if (slot < 0) continue;
             const int r = key - k0;                            // row in the tile
@@ -896,24 +902,33 @@ constexpr int kPrefillNBUF = 2;
 // the 16-prompt causal batch, the chunked-window and the mixed prefills: 32x32x16 1-3% faster
 // with 18 fewer VGPRs.
 constexpr bool kPrefillW32 = true;
-// every 16-key group of a tile needs a wave of its own to copy it (4 waves per workgroup)
-static_assert(kPrefillBN / 16 <= 4, "fewer waves than key groups per tile");
+// every 16-key group of a tile needs a wave of its own to copy it
+static_assert(kPrefillBN / 16 <= kPrefillWaves, "fewer waves than key groups per tile");
+
+static int gcd_int(int x, int y) {
+    while (y) {
+        const int t = x % y;
+        x = y;
+        y = t;
+    }
+    return x;
+}
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t st) {
     const int G = a.group;
-    // 32 query rows per wave, 4 waves per workgroup, two workgroups per CU (measured: two
+    // 32 query rows per wave, kPrefillWaves waves per workgroup, 8 waves per CU (measured: two
     // independent 4-wave workgroups per CU beat one workgroup of 5..8 waves)
     PrefillGrid pg;
-    pg.rb = (G % 4 == 0) ? 1 : (G % 2 == 0 ? 2 : 4);
-    pg.wgs_per_tile = G * pg.rb / 4;
+    pg.rb = kPrefillWaves / gcd_int(G, kPrefillWaves);
+    pg.wgs_per_tile = G * pg.rb / kPrefillWaves;
     pg.n_sg = a.num_seqs * a.c.num_kv_heads;
     pg.n_tiles = (a.max_seqlen_q + 32 * pg.rb - 1) / (32 * pg.rb) * pg.wgs_per_tile;
     const int64_t nsg_pad = ((int64_t)pg.n_sg + 7) / 8 * 8;
     const dim3 grid((unsigned)(nsg_pad * pg.n_tiles));
     const bool alibi = a.alibi != nullptr;
     const bool fp8 = a.c.dtype == 2;
-#define PA_PREFILL(DD, AL, F8) hipLaunchKernelGGL((prefill_bf16_kernel<DD, 2, kPrefillBN, kPrefillNBUF, AL, F8, false, kPrefillW32, false>), grid, dim3(256), 0, st, a, pg)
-#define PA_CASC(DD, F8) hipLaunchKernelGGL((prefill_bf16_kernel<DD, 2, kPrefillBN, kPrefillNBUF, false, F8, false, true, true>), grid, dim3(256), 0, st, a, pg)
+#define PA_PREFILL(DD, AL, F8) hipLaunchKernelGGL((prefill_bf16_kernel<DD, 2, kPrefillBN, (F8 ? 2 : kPrefillNBUF), AL, F8, false, kPrefillW32, false>), grid, dim3(64 * kPrefillWaves), 0, st, a, pg)
+#define PA_CASC(DD, F8) hipLaunchKernelGGL((prefill_bf16_kernel<DD, 2, kPrefillBN, (F8 ? 2 : kPrefillNBUF), false, F8, false, true, true>), grid, dim3(64 * kPrefillWaves), 0, st, a, pg)
     if (a.cascade) {  // shared-prefix own-keys pass (no ALiBi, no fused store)
         if (a.c.head_size == 128) { if (fp8) PA_CASC(128, true); else PA_CASC(128, false); }
         else { if (fp8) PA_CASC(64, true); else PA_CASC(64, false); }
@@ -932,8 +947,8 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t st) {
 // q-tile pairs of the prefill grid for group size G (rb row blocks of 32 per q-tile)
 static PrefillGrid prefix_grid(int num_seqs, int group, int num_kv_heads, int chunks) {
     PrefillGrid pg;
-    pg.rb = (group % 4 == 0) ? 1 : (group % 2 == 0 ? 2 : 4);
-    pg.wgs_per_tile = group * pg.rb / 4;
+    pg.rb = kPrefillWaves / gcd_int(group, kPrefillWaves);
+    pg.wgs_per_tile = group * pg.rb / kPrefillWaves;
     pg.n_sg = chunks * num_kv_heads;
     pg.n_tiles = (num_seqs + 32 * pg.rb - 1) / (32 * pg.rb) * pg.wgs_per_tile;
     return pg;
@@ -974,7 +989,7 @@ hipError_t launch_prefix_states(const DecodeArgs& d, hipStream_t st) {
     const int64_t nsg_pad = ((int64_t)pg.n_sg + 7) / 8 * 8;
     const dim3 grid((unsigned)(nsg_pad * pg.n_tiles));
     const bool fp8 = a.c.dtype == 2;
-#define PA_PREFIX(DD, F8) hipLaunchKernelGGL((prefill_bf16_kernel<DD, 2, kPrefillBN, kPrefillNBUF, false, F8, true, kPrefillW32, false>), grid, dim3(256), 0, st, a, pg)
+#define PA_PREFIX(DD, F8) hipLaunchKernelGGL((prefill_bf16_kernel<DD, 2, kPrefillBN, (F8 ? 2 : kPrefillNBUF), false, F8, true, kPrefillW32, false>), grid, dim3(64 * kPrefillWaves), 0, st, a, pg)
     if (a.c.head_size == 128) {
         if (fp8) PA_PREFIX(128, true); else PA_PREFIX(128, false);
     } else {
