@@ -140,7 +140,7 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 // CASC: the own-keys pass of shared-prefix prefill.  Each sequence attends only its keys from
 // prefix_len on (keys below it are masked like a window's), and the epilogue folds in, by
 // log-sum-exp, the states the prefix pass left for the same packed query row and head.
-template <int D, int NBR, int BN, int NBUF, bool ALIBI, bool FP8, bool PREFIX, bool W32, bool CASC>
+template <int D, int NBR, int BN, int NBUF, bool ALIBI, bool FP8, bool PREFIX, bool W32, bool CASC, bool FUSED>
 __global__ __launch_bounds__(64 * kPrefillWaves, 8 / kPrefillWaves) void prefill_bf16_kernel(const PrefillArgs a,
                                                                                               const PrefillGrid pg) {
     constexpr int NGA = BN / 16;      // 16-key groups per K/V tile
@@ -346,7 +346,9 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 8 / kPrefillWaves) void prefill
     // the sequence's rows (rows past the last key are zeroed after the copy).
     const char* knew = (const char*)a.knew;
     const char* vnew = (const char*)a.vnew;
-    const bool fused = !FP8 && !PREFIX && knew != nullptr;  // an FP8 cache is stored by its own kernel first
+    // FUSED: the call stores the new tokens (an FP8 cache is stored by its own kernel first)
+    static_assert(!FUSED || (!FP8 && !PREFIX && !CASC), "the fused store is a bf16 prefill of its own");
+    constexpr bool fused = FUSED;
     struct GroupSrc {
         const char* k;   // uniform base (non-mixed) of the group's first row, KV head 0
         const char* v;
@@ -602,8 +604,8 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 8 / kPrefillWaves) void prefill
     };
     // mask, online softmax of the lane's row, P^T packed straight from the accumulators: the
     // B operand of 16-key step (b, sg) is accumulator values 8 sg .. 8 sg + 7 of block b
-    auto softmax_w = [&](int k0, f32x16 (&sw)[2], u32x4 (&pw)[2][2], float& alpha) {
-        const bool edge = (k0 + BN - 1 > wv_p_min) || (has_lo && k0 < wv_lo_max);
+    auto softmax_w = [&](int k0, f32x16 (&sw)[2], u32x4 (&pw)[2][2], float& alpha, bool inner) {
+        const bool edge = !inner && ((k0 + BN - 1 > wv_p_min) || (has_lo && k0 < wv_lo_max));
         if (edge) {
 #pragma unroll
             for (int b = 0; b < 2; ++b)
@@ -739,8 +741,17 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 8 / kPrefillWaves) void prefill
         constexpr int j = decltype(J)::value;
         return j == 0 ? lds_v0 : j == 1 ? lds_v1 : j == 2 ? lds_v2 : lds_v3;
     };
+    // Inner tiles [ia, ib): tiles every row of the workgroup sees in full, from the last
+    // first-key of its rows up to below its first row's own position (PREFIX: the chunk's
+    // whole tiles).  They need no mask and hold no dead rows, every active wave computes them,
+    // and they hold none of the workgroup's own new tokens: one test per tile skips those checks.
+    const int lo_all = PREFIX ? kc0 : max(kstart, W > 0 ? max(0, off + wg_row_end - W) : 0);
+    const int hi_all = PREFIX ? kc1 - 1 : off + wg_row0 - 1;
+    const int ia = (lo_all + BN - 1) / BN;
+    const int ib = (hi_all + 1) / BN;
     auto step = [&](int kt, int kt_end, auto J) {
         constexpr int j = decltype(J)::value;
+        const bool inner = kt >= ia && kt < ib;
         constexpr int jn = (j + NBUF - 1) % NBUF;  // buffer of tile kt + NBUF - 1
         char* kc = kbuf(J);
         char* vc = vbuf(J);
@@ -753,8 +764,10 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 8 / kPrefillWaves) void prefill
             const int later = min(NBUF - 2, kt_end - 1 - kt);
             wait_vmcnt(my_copies * later);
         }
-        zero_dead(k0, kc);
-        zero_dead(k0, vc);
+        if (!inner) {
+            zero_dead(k0, kc);
+            zero_dead(k0, vc);
+        }
         // all copies of tile kt visible; buffer jn (tile kt - 1) is free.  Not a fenced
         // barrier: that would also wait for the copies of the later tiles
         lds_barrier();
@@ -763,14 +776,14 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 8 / kPrefillWaves) void prefill
             issue(gs, false, cgk, kbuf(std::integral_constant<int, jn>{}));
             issue(gs, true, cgv, vbuf(std::integral_constant<int, jn>{}));
         }
-        if (fused) store_new_rows(k0, kc, vc);
-        if (wave_active && k0 <= wv_hi && k0 + BN - 1 >= wv_lo) {
+        if (!inner && fused) store_new_rows(k0, kc, vc);
+        if (inner ? wave_active : (wave_active && k0 <= wv_hi && k0 + BN - 1 >= wv_lo)) {
             if constexpr (W32) {
                 f32x16 sw[2];
                 u32x4 pw[2][2];
                 float alpha;
                 qk_w(kc, sw);
-                softmax_w(k0, sw, pw, alpha);
+                softmax_w(k0, sw, pw, alpha, inner);
                 pv_w(vc, pw, alpha);
             } else {
                 f32x4 sacc[NGA][NBR];
@@ -927,18 +940,22 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t st) {
     const dim3 grid((unsigned)(nsg_pad * pg.n_tiles));
     const bool alibi = a.alibi != nullptr;
     const bool fp8 = a.c.dtype == 2;
-#define PA_PREFILL(DD, AL, F8) hipLaunchKernelGGL((prefill_bf16_kernel<DD, 2, kPrefillBN, (F8 ? 2 : kPrefillNBUF), AL, F8, false, kPrefillW32, false>), grid, dim3(64 * kPrefillWaves), 0, st, a, pg)
-#define PA_CASC(DD, F8) hipLaunchKernelGGL((prefill_bf16_kernel<DD, 2, kPrefillBN, (F8 ? 2 : kPrefillNBUF), false, F8, false, true, true>), grid, dim3(64 * kPrefillWaves), 0, st, a, pg)
+    const bool fused = a.knew != nullptr;  // bf16 only: the FP8 path stores first
+#define PA_PREFILL(DD, AL, F8, FU) hipLaunchKernelGGL((prefill_bf16_kernel<DD, 2, kPrefillBN, (F8 ? 2 : kPrefillNBUF), AL, F8, false, kPrefillW32, false, FU>), grid, dim3(64 * kPrefillWaves), 0, st, a, pg)
+#define PA_PREFILL_BF16(DD, AL) do { if (fused) PA_PREFILL(DD, AL, false, true); else PA_PREFILL(DD, AL, false, false); } while (0)
+#define PA_CASC(DD, F8) hipLaunchKernelGGL((prefill_bf16_kernel<DD, 2, kPrefillBN, (F8 ? 2 : kPrefillNBUF), false, F8, false, true, true, false>), grid, dim3(64 * kPrefillWaves), 0, st, a, pg)
+    if (fused && (fp8 || a.cascade)) return hipErrorInvalidValue;
     if (a.cascade) {  // shared-prefix own-keys pass (no ALiBi, no fused store)
         if (a.c.head_size == 128) { if (fp8) PA_CASC(128, true); else PA_CASC(128, false); }
         else { if (fp8) PA_CASC(64, true); else PA_CASC(64, false); }
     } else if (a.c.head_size == 128) {
-        if (fp8) { if (alibi) PA_PREFILL(128, true, true); else PA_PREFILL(128, false, true); }
-        else { if (alibi) PA_PREFILL(128, true, false); else PA_PREFILL(128, false, false); }
+        if (fp8) { if (alibi) PA_PREFILL(128, true, true, false); else PA_PREFILL(128, false, true, false); }
+        else { if (alibi) PA_PREFILL_BF16(128, true); else PA_PREFILL_BF16(128, false); }
     } else {
-        if (fp8) { if (alibi) PA_PREFILL(64, true, true); else PA_PREFILL(64, false, true); }
-        else { if (alibi) PA_PREFILL(64, true, false); else PA_PREFILL(64, false, false); }
+        if (fp8) { if (alibi) PA_PREFILL(64, true, true, false); else PA_PREFILL(64, false, true, false); }
+        else { if (alibi) PA_PREFILL_BF16(64, true); else PA_PREFILL_BF16(64, false); }
     }
+#undef PA_PREFILL_BF16
 #undef PA_PREFILL
 #undef PA_CASC
     return hipGetLastError();
@@ -989,7 +1006,7 @@ hipError_t launch_prefix_states(const DecodeArgs& d, hipStream_t st) {
     const int64_t nsg_pad = ((int64_t)pg.n_sg + 7) / 8 * 8;
     const dim3 grid((unsigned)(nsg_pad * pg.n_tiles));
     const bool fp8 = a.c.dtype == 2;
-#define PA_PREFIX(DD, F8) hipLaunchKernelGGL((prefill_bf16_kernel<DD, 2, kPrefillBN, (F8 ? 2 : kPrefillNBUF), false, F8, true, kPrefillW32, false>), grid, dim3(64 * kPrefillWaves), 0, st, a, pg)
+#define PA_PREFIX(DD, F8) hipLaunchKernelGGL((prefill_bf16_kernel<DD, 2, kPrefillBN, (F8 ? 2 : kPrefillNBUF), false, F8, true, kPrefillW32, false, false>), grid, dim3(64 * kPrefillWaves), 0, st, a, pg)
     if (a.c.head_size == 128) {
         if (fp8) PA_PREFIX(128, true); else PA_PREFIX(128, false);
     } else {
