@@ -92,6 +92,11 @@ __device__ __forceinline__ void lds_barrier() {
 // waves, two workgroups per CU, measured faster than one 8-wave workgroup per CU sharing
 // every tile (whose waves run the same stage at the same time on a SIMD).
 constexpr int kPrefillWaves = 4;
+// Waves each SIMD holds at once (the register budget: 512 / this many VGPRs per wave).
+constexpr int kPrefillWavesPerSimd = 2;
+// Keys per compute step of the 32x32x16 form: a K/V tile is processed in steps of this many
+// keys (S^T, softmax and P.V of one step before the next), which bounds the live S registers.
+constexpr int kPrefillCB = 64;
 
 // Work decomposition.  A q-tile is rb blocks of 32 query rows of one (sequence, KV head);
 // its (query head of the group, row block) pairs, row block major, are dealt W at a time to
@@ -141,8 +146,8 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 // prefix_len on (keys below it are masked like a window's), and the epilogue folds in, by
 // log-sum-exp, the states the prefix pass left for the same packed query row and head.
 template <int D, int NBR, int BN, int NBUF, bool ALIBI, bool FP8, bool PREFIX, bool W32, bool CASC, bool FUSED>
-__global__ __launch_bounds__(64 * kPrefillWaves, 8 / kPrefillWaves) void prefill_bf16_kernel(const PrefillArgs a,
-                                                                                              const PrefillGrid pg) {
+__global__ __launch_bounds__(64 * kPrefillWaves, kPrefillWavesPerSimd) void prefill_bf16_kernel(const PrefillArgs a,
+                                                                                                 const PrefillGrid pg) {
     constexpr int NGA = BN / 16;      // 16-key groups per K/V tile
     constexpr int NCC = BN / 32;      // 32-key chunks per K/V tile (PV MFMA k-steps)
     constexpr int RPW = 16 * NBR;     // query rows per wave (NBR blocks of 16)
@@ -162,7 +167,10 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 8 / kPrefillWaves) void prefill
     auto vswz = [](int r) { return (4 * (r & 3)) & (CPR - 1); };
     constexpr int ELT = FP8 ? 1 : 2;  // bytes per cache element
     static_assert(!FP8 || NBUF == 2, "the FP8 copy stages one tile in registers");
-    static_assert(!W32 || BN == 64, "the 32x32x16 form takes 64-key tiles as two 32-key blocks");
+    static_assert(!W32 || BN == 64 || BN == 32, "the 32x32x16 form takes tiles of one or two 32-key blocks");
+    constexpr int CB = BN < kPrefillCB ? BN : kPrefillCB;  // keys per compute step (32x32x16 form)
+    static_assert(CB % 32 == 0 && BN % CB == 0, "compute steps of whole 32-key blocks");
+    constexpr int NB32 = CB / 32;     // 32-key blocks per compute step
     static_assert(!CASC || (W32 && !PREFIX), "the shared-prefix own-keys pass uses the 32x32x16 form");
 
     // NBUF K and NBUF V buffers as distinct objects, so the compiler can tell a copy into one
@@ -581,19 +589,19 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 8 / kPrefillWaves) void prefill
     uint32_t kw[D / 16];
 #pragma unroll
     for (int t = 0; t < D / 16; ++t) kw[t] = (uint32_t)(lrow * D * 2 + (((2 * t + lh) ^ (lrow & KSW)) * 16));
-    auto qk_w = [&](const char* kt, f32x16 (&sw)[2]) {
-        sw[0] = (f32x16)(0.f);
-        sw[1] = (f32x16)(0.f);
+    auto qk_w = [&](const char* kt, f32x16 (&sw)[NB32]) {
+#pragma unroll
+        for (int b = 0; b < NB32; ++b) sw[b] = (f32x16)(0.f);
 #pragma unroll
         for (int t = 0; t < D / 16; ++t)
 #pragma unroll
-            for (int b = 0; b < 2; ++b) {
+            for (int b = 0; b < NB32; ++b) {
                 const bf16x8 kf = *(const bf16x8*)(kt + kw[t] + 32 * b * D * 2);
                 sw[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qw[t], sw[b], 0, 0, 0);
             }
         // operand reads well ahead of their MFMAs (the default order issued them one or two
         // MFMAs ahead, less than the LDS latency): eight first, then one per MFMA
-        constexpr int NR = 2 * (D / 16);
+        constexpr int NR = NB32 * (D / 16);
 #pragma unroll
         for (int r = 0; r < 8; ++r) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
 #pragma unroll
@@ -604,11 +612,11 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 8 / kPrefillWaves) void prefill
     };
     // mask, online softmax of the lane's row, P^T packed straight from the accumulators: the
     // B operand of 16-key step (b, sg) is accumulator values 8 sg .. 8 sg + 7 of block b
-    auto softmax_w = [&](int k0, f32x16 (&sw)[2], u32x4 (&pw)[2][2], float& alpha, bool inner) {
-        const bool edge = !inner && ((k0 + BN - 1 > wv_p_min) || (has_lo && k0 < wv_lo_max));
+    auto softmax_w = [&](int k0, f32x16 (&sw)[NB32], u32x4 (&pw)[NB32][2], float& alpha, bool inner) {
+        const bool edge = !inner && ((k0 + CB - 1 > wv_p_min) || (has_lo && k0 < wv_lo_max));
         if (edge) {
 #pragma unroll
-            for (int b = 0; b < 2; ++b)
+            for (int b = 0; b < NB32; ++b)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const int key = k0 + 32 * b + 8 * (i >> 2) + 4 * lh + (i & 3);
@@ -619,7 +627,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 8 / kPrefillWaves) void prefill
         if constexpr (ALIBI) {
             const float base = sl2 * (float)(k0 + 4 * lh - prw);
 #pragma unroll
-            for (int b = 0; b < 2; ++b)
+            for (int b = 0; b < NB32; ++b)
 #pragma unroll
                 for (int i = 0; i < 16; ++i)
                     sw[b][i] = fmaf(sw[b][i], c_log2, fmaf(sl2, (float)(32 * b + 8 * (i >> 2) + (i & 3)), base));
@@ -627,7 +635,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 8 / kPrefillWaves) void prefill
         }
         float mx = fmaxf(sw[0][0], sw[0][1]);
 #pragma unroll
-        for (int x = 2; x < 32; x += 2) mx = fmaxf(fmaxf(mx, sw[x >> 4][x & 15]), sw[x >> 4][(x & 15) + 1]);
+        for (int x = 2; x < 16 * NB32; x += 2) mx = fmaxf(fmaxf(mx, sw[x >> 4][x & 15]), sw[x >> 4][(x & 15) + 1]);
         mx = half_max(mx);
         // the reference maximum moves only when the tile's maximum exceeds it by more than 8
         // (log2 units), as in the 16x16 form
@@ -639,7 +647,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 8 / kPrefillWaves) void prefill
         const float msub = m_new == -INFINITY ? 0.f : m_new;
         float ps = 0.f;
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+        for (int b = 0; b < NB32; ++b)
 #pragma unroll
             for (int sg = 0; sg < 2; ++sg) {
                 float pv[8];
@@ -661,13 +669,13 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 8 / kPrefillWaves) void prefill
     const int vroww = 4 * (vgw >> 1) + (vsl >> 2);
     const uint32_t vbasew = (uint32_t)(vroww * D * 2 + 8 * (vsl & 1));
     const int vsww = vswz(vroww);  // rows shifted by multiples of 4: same swizzle
-    auto pv_w = [&](const char* vt, const u32x4 (&pw)[2][2], float alpha) {
+    auto pv_w = [&](const char* vt, const u32x4 (&pw)[NB32][2], float alpha) {
         if (__any(alpha != 1.f)) {
 #pragma unroll
             for (int c = 0; c < D / 32; ++c) ow[c] *= alpha;
         }
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+        for (int b = 0; b < NB32; ++b)
 #pragma unroll
             for (int sg = 0; sg < 2; ++sg) {
                 const uint32_t rowoff = (uint32_t)((32 * b + 16 * sg) * D * 2);
@@ -684,7 +692,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 8 / kPrefillWaves) void prefill
             }
         // V operand reads ahead of their MFMAs as for K: eight first (four MFMAs' worth), then two
         // per MFMA
-        constexpr int NM = 4 * (D / 32);
+        constexpr int NM = 2 * NB32 * (D / 32);
 #pragma unroll
         for (int r = 0; r < 8; ++r) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
 #pragma unroll
@@ -703,7 +711,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 8 / kPrefillWaves) void prefill
     // the q-tile's slots, staged in LDS once (a global load inside the loop would make the
     // compiler wait for every copy in flight); filled right after the first tile's copies are
     // issued, so its wait overlaps theirs
-    __shared__ int lds_slots[128];
+    __shared__ int lds_slots[32 * kPrefillWaves];  // 32 rows per row block, rb <= waves
     auto stage_slots = [&]() {
         for (int i = tid; i < 32 * pg.rb; i += blockDim.x)
             lds_slots[i] = i0 + i < sq ? a.slots[q0 + i0 + i] : -1;
@@ -779,12 +787,15 @@ __global__ __launch_bounds__(64 * kPrefillWaves, 8 / kPrefillWaves) void prefill
         if (!inner && fused) store_new_rows(k0, kc, vc);
         if (inner ? wave_active : (wave_active && k0 <= wv_hi && k0 + BN - 1 >= wv_lo)) {
             if constexpr (W32) {
-                f32x16 sw[2];
-                u32x4 pw[2][2];
-                float alpha;
-                qk_w(kc, sw);
-                softmax_w(k0, sw, pw, alpha, inner);
-                pv_w(vc, pw, alpha);
+#pragma unroll
+                for (int hb = 0; hb < BN / CB; ++hb) {
+                    f32x16 sw[NB32];
+                    u32x4 pw[NB32][2];
+                    float alpha;
+                    qk_w(kc + hb * CB * D * 2, sw);
+                    softmax_w(k0 + hb * CB, sw, pw, alpha, inner);
+                    pv_w(vc + hb * CB * D * 2, pw, alpha);
+                }
             } else {
                 f32x4 sacc[NGA][NBR];
                 u32x4 pk[NCC][NBR];
