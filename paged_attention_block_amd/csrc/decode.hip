@@ -485,34 +485,36 @@ __global__ __launch_bounds__(512) void decode_bf16_kernel(const DecodeArgs a) {
             float l_run = 0.f;
 
             // Two register sets: the loads of step i+1 are in flight while step i computes.
-            // The prefetch is unconditional (the last step re-reads its own rows, which hit
-            // in cache) so that every iteration issues the same number of loads and the
-            // waits stay exact.  A workgroup barrier per two steps keeps the 8 waves, which
+            // The prefetch is unconditional so that every iteration issues the same number of
+            // loads and the waits stay exact: after the last step it is a dummy in which every
+            // lane reads the same few 16-byte pieces of rows the step already read (a re-read
+            // of the step's whole rows missed the L2 often enough to add ~4% to the traffic).  A workgroup barrier per two steps keeps the 8 waves, which
             // read adjacent 256-byte pieces of the same 2 KB token rows, close together in
             // the key walk (measured: 3% more bandwidth than free-running waves).
             typename StepT<D, FP8>::K kA[2][KS], kB[2][KS];
             typename StepT<D, FP8>::V vA[8], vB[8];
             int k0 = step_begin;
-            auto ld = [&](int k, auto& kr, auto& vr) {
+            auto ld = [&](int k, auto& kr, auto& vr, bool dummy) {
                 if constexpr (FUSED) {
-                    if (new_here && k == k_last) {
+                    if (!dummy && new_here && k == k_last) {
                         load_step_new<D>(k, kb, ke, table, shift, BS, row_elems, g, kplane, vplane, k_off, v_off,
                                          row_bytes, col, grp, n - 1, knew_row, vnew_row, kr, vr);
                         return;
                     }
                 }
-                load_step<D, FP8>(k, kb, ke, table, shift, BS, row_elems, g, kplane, vplane, k_off, v_off, row_bytes, kr, vr);
+                load_step<D, FP8>(k, kb, ke, table, shift, BS, row_elems, g, kplane, vplane, dummy ? 0u : k_off,
+                                  dummy ? 0u : v_off, row_bytes, kr, vr);
             };
-            ld(k0, kA, vA);
+            ld(k0, kA, vA, false);
             while (true) {
                 __syncthreads();
-                const int n1 = k0 + 32 < ke ? k0 + 32 : k0;
-                ld(n1, kB, vB);
+                const bool more1 = k0 + 32 < ke;
+                ld(more1 ? k0 + 32 : k0, kB, vB, !more1);
                 compute_step<D, ALIBI, FP8>(k0, kb, ke, grp, c_log2, sl2, n - 1, qf, kA, vA, oacc, m_run, l_run);
                 k0 += 32;
                 if (k0 >= ke) break;
-                const int n2 = k0 + 32 < ke ? k0 + 32 : k0;
-                ld(n2, kA, vA);
+                const bool more2 = k0 + 32 < ke;
+                ld(more2 ? k0 + 32 : k0, kA, vA, !more2);
                 compute_step<D, ALIBI, FP8>(k0, kb, ke, grp, c_log2, sl2, n - 1, qf, kB, vB, oacc, m_run, l_run);
                 k0 += 32;
                 if (k0 >= ke) break;
