@@ -463,6 +463,12 @@ def bench_workload(name, steps, warmup, dev, with_cpu, partition_size=0, flush_m
     res = {"workload": wname, "ms_per_step": round(step_t * 1e3, 4),
            "wall_ms_per_step": round(wall * 1e3, 4), "cache_eviction_MiB_per_step": flush_mb, "ops": {}}
     total_bytes, total_flops = 0.0, 0.0
+    def traffic(kind):
+        # committed counter summary of this op in this workload (plain calls only)
+        if fused or alibi or cascade:
+            return None
+        return read_traffic(kind if name == kind else f"{kind}_{name}")
+
     for op, t, d in zip(ops, per_op, step.prepared):
         n = type(op).__name__
         fused = bool(d.get("fused"))
@@ -488,25 +494,24 @@ def bench_workload(name, steps, warmup, dev, with_cpu, partition_size=0, flush_m
                 "ms": round(t * 1e3, 4), "GB/s": round((b + sb) / t / 1e9, 1),
                 "bytes": b + sb, "tokens_per_s": round(len(op.seq_lens) / t, 1),
                 "partition_size": d["part"] or "auto",
-                "roofline": roofline((b + sb) / t / 1e9, HBM_PEAK_GBS, "GB/s", "hbm",
-                                     read_traffic("decode") if name == "decode" and not fused and not alibi else None)}
+                "roofline": roofline((b + sb) / t / 1e9, HBM_PEAK_GBS, "GB/s", "hbm", traffic("decode"))}
         elif n == "PrefillOp":
             f = prefill_flops(op, wl)
             total_flops += f
             res["ops"]["prefill_with_store" if fused else ("cascade_prefill" if cascade else "prefill")] = {
                 "ms": round(t * 1e3, 4), "TFLOP/s": round(f / t / 1e12, 2), "flops": f,
-                "roofline": roofline(f / t / 1e12, BF16_PEAK_TFLOPS, "TFLOP/s", "mfma",
-                                     read_traffic("prefill") if name == "prefill" and not fused and not alibi else None)}
+                "roofline": roofline(f / t / 1e12, BF16_PEAK_TFLOPS, "TFLOP/s", "mfma", traffic("prefill"))}
         elif n == "StoreOp":
             b = store_bytes(op, wl)
             total_bytes += b
             res["ops"]["store"] = {"ms": round(t * 1e3, 4), "GB/s": round(b / t / 1e9, 1), "bytes": b,
-                                   "roofline": roofline(b / t / 1e9, HBM_PEAK_GBS, "GB/s", "hbm")}
+                                   "roofline": roofline(b / t / 1e9, HBM_PEAK_GBS, "GB/s", "hbm", traffic("store"))}
         elif n == "CopyOp":
             b = copy_bytes(op, wl)
             total_bytes += b
             res["ops"]["copy_blocks"] = {"ms": round(t * 1e3, 4), "GB/s": round(b / t / 1e9, 1), "bytes": b,
-                                         "roofline": roofline(b / t / 1e9, HBM_PEAK_GBS, "GB/s", "hbm")}
+                                         "roofline": roofline(b / t / 1e9, HBM_PEAK_GBS, "GB/s", "hbm",
+                                                              traffic("copy_blocks"))}
     for (med, lo), (opname, r) in zip(step.op_stats, res["ops"].items()):
         r["ms_median"] = round(med * 1e3, 4)
         r["ms_min"] = round(lo * 1e3, 4)
@@ -564,9 +569,10 @@ def main() -> int:
         line.update(value=main_res["step_GB/s"], unit="GB/s")
         line["roofline"] = main_res["ops"]["decode"]["roofline"]
         if line["roofline"]["traffic"] is not None:
-            line["traffic_note"] = ("roofline.traffic: HBM bytes per decode launch from the committed "
-                                    "FETCH_SIZE/WRITE_SIZE summary profiles/decode_traffic.txt, whose source "
-                                    "digest matches the built sources (not counted in this run)")
+            line["traffic_note"] = ("roofline.traffic (here and in every op that has one): HBM bytes per call "
+                                    "from the committed FETCH_SIZE/WRITE_SIZE summary profiles/<op>[_<workload>]"
+                                    "_traffic.txt, used only while its source digest matches the built "
+                                    "sources (not counted in this run)")
     else:
         line.update(value=main_res["step_TFLOP/s"], unit="TFLOP/s")
         line["roofline"] = main_res["ops"]["prefill"]["roofline"]
