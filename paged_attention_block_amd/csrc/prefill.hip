@@ -806,9 +806,13 @@ __global__ __launch_bounds__(64 * kPrefillWaves, kPrefillWavesPerSimd) void pref
             }
         }
     };
+    // a buffer pair no wave reads after the loop (the one before the last tile's; any when
+    // there is a single tile or none): the epilogue stages the output tiles there
+    int free_buf = 1;
     if (wg_hi >= wg_lo) {
         const int kt_begin = wg_lo / BN;
         const int kt_end = wg_hi / BN + 1;
+        free_buf = (kt_end - 1 - kt_begin + NBUF - 1) % NBUF;
         {
             GroupSrc gs = group_src(kt_begin * BN);
             issue(gs, false, cgk, lds_k0);
@@ -840,6 +844,66 @@ __global__ __launch_bounds__(64 * kPrefillWaves, kPrefillWavesPerSimd) void pref
     if constexpr (W32) {
         const float lt = half_sum(lw);  // before any lane leaves: both halves of the row
         const int row = r0 + lrow;
+        if constexpr (!PREFIX) {
+            // bf16 output: the wave's 32 x D tile goes through its 32 rows x 2D bytes of the free
+            // buffer (row-major, 16-byte chunk c of row r at slot c ^ (r & KSW)), so that each
+            // global store writes whole rows (the accumulator layout would store 8-byte pieces
+            // of 32 rows per instruction)
+            float lsum = lt;
+            if constexpr (CASC) {
+                // the prefix pass's states of this packed row and head (one per prefix chunk),
+                // folded in by log-sum-exp: both parts are in the same log2 units
+                if (row < rows_end) {
+                    const int64_t per_chunk = (int64_t)a.prefix_rows * H;
+                    const int64_t st = (int64_t)(q0 + row) * H + h;
+                    float M = mw;
+                    for (int c = 0; c < a.prefix_chunks; ++c) M = fmaxf(M, a.pre_ml[(c * per_chunk + st) * 2]);
+                    const float msub = M == -INFINITY ? 0.f : M;
+                    const float al = __builtin_amdgcn_exp2f(mw - msub);
+                    lsum *= al;
+#pragma unroll
+                    for (int c = 0; c < D / 32; ++c) ow[c] *= al;
+                    for (int c = 0; c < a.prefix_chunks; ++c) {
+                        const f32x2 ml = *(const f32x2*)(a.pre_ml + (c * per_chunk + st) * 2);
+                        const float w = __builtin_amdgcn_exp2f(ml[0] - msub);
+                        lsum = fmaf(w, ml[1], lsum);
+                        const float* po = a.pre_o + (c * per_chunk + st) * D + 4 * lh;
+#pragma unroll
+                        for (int cc = 0; cc < D / 32; ++cc)
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) {
+                                const f32x4 x = *(const f32x4*)(po + 32 * cc + 8 * q);
+#pragma unroll
+                                for (int e = 0; e < 4; ++e) ow[cc][4 * q + e] = fmaf(w, x[e], ow[cc][4 * q + e]);
+                            }
+                    }
+                }
+            }
+            const float inv = lsum > 0.f ? (FP8 ? a.c.kv_scale : 1.f) / lsum : 0.f;  // FP8: V / kv_scale in the cache
+            constexpr int TW = 32 * D * 2;  // bytes of one wave's output tile
+            static_assert(kPrefillWaves * TW <= 2 * TILE, "the free buffer pair holds every wave's output tile");
+            char* stg = (free_buf == 0 ? lds_k0 : free_buf == 1 ? lds_k1 : free_buf == 2 ? lds_k2 : lds_k3);
+            if (wave >= TILE / TW) stg = (free_buf == 0 ? lds_v0 : free_buf == 1 ? lds_v1 : free_buf == 2 ? lds_v2 : lds_v3);
+            stg += (wave % (TILE / TW)) * TW;
+            // lane (row lrow, half lh) holds dims 32c + 8q + 4lh .. +3: 16-byte chunk 4c + q, half lh
+#pragma unroll
+            for (int c = 0; c < D / 32; ++c)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    *(u32x2*)(stg + lrow * D * 2 + (((4 * c + q) ^ (lrow & KSW)) * 16) + 8 * lh) =
+                        u32x2{pack_bf16x2(ow[c][4 * q] * inv, ow[c][4 * q + 1] * inv),
+                              pack_bf16x2(ow[c][4 * q + 2] * inv, ow[c][4 * q + 3] * inv)};
+            // read back whole rows: lane l takes chunk l % CPR of row RPI * k + l / CPR
+#pragma unroll
+            for (int k = 0; k < 32 / RPI; ++k) {
+                const int rr = RPI * k + lane / CPR;
+                const int ch = lane % CPR;
+                const u32x4 x = *(const u32x4*)(stg + rr * D * 2 + ((ch ^ (rr & KSW)) * 16));
+                if (r0 + rr < rows_end)
+                    *(u32x4*)((__bf16*)a.out + ((int64_t)(q0 + r0 + rr) * H + h) * D + 8 * ch) = x;
+            }
+            return;
+        }
         if (row >= rows_end) return;
         if constexpr (PREFIX) {
             const int64_t st = ((int64_t)pc * a.num_seqs + row) * H + h;
@@ -852,43 +916,6 @@ __global__ __launch_bounds__(64 * kPrefillWaves, kPrefillWavesPerSimd) void pref
             if (lh == 0) *(f32x2*)(a.pre_ml + st * 2) = f32x2{mw, lt};
             return;
         }
-        float lsum = lt;
-        if constexpr (CASC) {
-            // the prefix pass's states of this packed row and head (one per prefix chunk), folded
-            // in by log-sum-exp: both parts are in the same log2 units
-            const int64_t per_chunk = (int64_t)a.prefix_rows * H;
-            const int64_t st = (int64_t)(q0 + row) * H + h;
-            float M = mw;
-            for (int c = 0; c < a.prefix_chunks; ++c) M = fmaxf(M, a.pre_ml[(c * per_chunk + st) * 2]);
-            const float msub = M == -INFINITY ? 0.f : M;
-            const float al = __builtin_amdgcn_exp2f(mw - msub);
-            lsum *= al;
-#pragma unroll
-            for (int c = 0; c < D / 32; ++c) ow[c] *= al;
-            for (int c = 0; c < a.prefix_chunks; ++c) {
-                const f32x2 ml = *(const f32x2*)(a.pre_ml + (c * per_chunk + st) * 2);
-                const float w = __builtin_amdgcn_exp2f(ml[0] - msub);
-                lsum = fmaf(w, ml[1], lsum);
-                const float* po = a.pre_o + (c * per_chunk + st) * D + 4 * lh;
-#pragma unroll
-                for (int cc = 0; cc < D / 32; ++cc)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const f32x4 x = *(const f32x4*)(po + 32 * cc + 8 * q);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) ow[cc][4 * q + e] = fmaf(w, x[e], ow[cc][4 * q + e]);
-                    }
-            }
-        }
-        const float inv = lsum > 0.f ? (FP8 ? a.c.kv_scale : 1.f) / lsum : 0.f;  // FP8: V / kv_scale in the cache
-        __bf16* dst = (__bf16*)a.out + ((int64_t)(q0 + row) * H + h) * D + 4 * lh;
-#pragma unroll
-        for (int c = 0; c < D / 32; ++c)
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                *(u32x2*)(dst + 32 * c + 8 * q) = u32x2{pack_bf16x2(ow[c][4 * q] * inv, ow[c][4 * q + 1] * inv),
-                                                       pack_bf16x2(ow[c][4 * q + 2] * inv, ow[c][4 * q + 3] * inv)};
-        return;
     }
     if constexpr (PREFIX) {  // the chunk's state of each (row, head): O, running max, sum
 #pragma unroll
