@@ -224,7 +224,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves, kPrefillWavesPerSimd) void pref
     const bool has_lo = W > 0 || kstart > 0;
 
     const int tid = threadIdx.x;
-    const int nwaves = blockDim.x >> 6;
+    constexpr int nwaves = kPrefillWaves;  // the launch is always 64 * kPrefillWaves threads
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: copy setup stays scalar
     const int lane = tid & 63;
     const int col = lane & 15;
@@ -328,7 +328,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves, kPrefillWavesPerSimd) void pref
     constexpr int IPG = 16 / RPI;          // copy instructions per 16-key group
     const int crow = lane / CPR;           // row within the instruction's rows
     const int cslot = lane % CPR;          // LDS chunk slot within the row
-    const int nsub = nwaves / NGA;         // waves per group
+    constexpr int nsub = nwaves / NGA;     // waves per group
     const bool copier = wave < NGA * nsub;
     const int cga = wave % NGA;            // the group this wave copies
     const int csub = wave / NGA;
