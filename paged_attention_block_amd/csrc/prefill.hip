@@ -31,6 +31,8 @@
 // (never through an unread block-table entry) and then overwritten with zeros in LDS by
 // the wave that copied them, so cache slots outside every row's window may hold anything.
 // Tiles crossing the causal diagonal or the window edge get an element mask.
+// The bf16 output of a wave (32 rows x D) goes through an LDS buffer no wave reads any more,
+// so that each global store writes whole 256-byte rows rather than 8-byte pieces of 32 rows.
 //
 // Workgroups are numbered so that each XCD (work dispatched round-robin over 8) runs the
 // q-tiles of one (sequence, KV head) back to back: those share K/V through that XCD's L2.
