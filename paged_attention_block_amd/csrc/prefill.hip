@@ -44,13 +44,15 @@
 
 namespace pa {
 
-// Tile copies and their synchronisation are written as inline assembly on purpose.  The
-// compiler tracks its own HBM->LDS copies (global_load_lds) and, unable to tell that a
-// later LDS read targets a different buffer than a copy still in flight, waits for every
-// copy (vmcnt 0) before the read: that exposed the full copy latency in every other step.
-// Copies it cannot see never make its own waits unsafe (vmcnt counts complete in order,
-// extra outstanding operations only make a wait stricter), so the kernel waits for its
-// copies itself: wait_vmcnt before a tile is used, then lds_barrier.
+// Tile copies and their waits are inline assembly.  A copy's rows are visible to the other
+// waves of the workgroup only once the copying wave has waited for its copies and the
+// workgroup has then passed a barrier, so each wave waits for its own copies (wait_vmcnt)
+// right before the barrier: a wait the compiler places itself comes at the first read of the
+// tile, after the barrier.  Copies the compiler cannot see never make its own waits unsafe
+// (vmcnt counts complete in order; extra outstanding operations only make a wait stricter).
+// The compiler's LDS-copy builtin, which it tracks per LDS buffer, measured no faster issued
+// where these copies are; spread between the S^T MFMAs it cost the copies lead time, which
+// the workloads whose K/V comes from HBM need (the mixed step 6% slower).
 
 // one 16-byte-per-lane copy HBM -> LDS: lane l's 16 bytes at base + voff (base wave-uniform,
 // voff the lane's 32-bit offset) land at LDS byte address lds + 16*l (lds wave-uniform)
@@ -58,6 +60,33 @@ __device__ __forceinline__ void copy_to_lds16(const void* base, uint32_t voff, u
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                  :
                  : "v"(voff), "s"(base), "s"(lds)
+                 : "memory", "m0");
+}
+
+// Four (two) such copies under one M0 write: copy j takes lane offset voff[j] and lands at LDS
+// byte lds + S*j + 16*l.  The instruction's immediate offset is added to both the global and
+// the LDS address, so copy j carries S*j there and voff[j] is the lane's offset less S*j.
+template <int S>
+__device__ __forceinline__ void copy4_to_lds16(const void* base, const uint32_t (&voff)[4], uint32_t lds) {
+    static_assert(3 * S < 4096, "immediate offsets are 12 bits");
+    asm volatile("s_mov_b32 m0, %5\n\ts_nop 0\n\t"
+                 "global_load_lds_dwordx4 %0, %4\n\t"
+                 "global_load_lds_dwordx4 %1, %4 offset:%6\n\t"
+                 "global_load_lds_dwordx4 %2, %4 offset:%7\n\t"
+                 "global_load_lds_dwordx4 %3, %4 offset:%8"
+                 :
+                 : "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]), "s"(base), "s"(lds), "i"(S), "i"(2 * S),
+                   "i"(3 * S)
+                 : "memory", "m0");
+}
+template <int S>
+__device__ __forceinline__ void copy2_to_lds16(const void* base, const uint32_t (&voff)[2], uint32_t lds) {
+    static_assert(S < 4096, "immediate offsets are 12 bits");
+    asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\t"
+                 "global_load_lds_dwordx4 %0, %2\n\t"
+                 "global_load_lds_dwordx4 %1, %2 offset:%4"
+                 :
+                 : "v"(voff[0]), "v"(voff[1]), "s"(base), "s"(lds), "i"(S)
                  : "memory", "m0");
 }
 
@@ -88,6 +117,11 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
 // workgroup barrier after this wave's LDS writes completed; no wait for copies in flight
 __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+// the same barrier, holding `ready` (a scalar load issued before it) as an input, so that the
+// load is issued ahead of the barrier and its latency runs under the barrier's wait
+__device__ __forceinline__ void lds_barrier_after(int ready) {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::"s"(ready) : "memory");
 }
 
 // Waves per workgroup (W): the workgroup's waves share each K/V tile staged in LDS.  Four
@@ -334,6 +368,10 @@ __global__ __launch_bounds__(64 * kPrefillWaves, kPrefillWavesPerSimd) void pref
     const bool copier = wave < NGA * nsub;
     const int cga = wave % NGA;            // the group this wave copies
     const int csub = wave / NGA;
+    // batched: a plane's copies of the group go out under one M0 write (bf16, one wave per
+    // group), copy jj at immediate offset 1024*jj; cgk/cgv then hold the lane offsets less that
+    // (cg_at adds it back where a copy is issued on its own)
+    constexpr bool batched = !FP8 && nsub == 1 && (IPG == 4 || IPG == 2);
     uint32_t cgk[IPG], cgv[IPG];
     int my_copies = 0;                     // copy instructions this wave issues per tile
 #pragma unroll
@@ -342,10 +380,12 @@ __global__ __launch_bounds__(64 * kPrefillWaves, kPrefillWavesPerSimd) void pref
         const int row = RPI * ig + crow;   // token row within the group (0..15)
         const int ck = cslot ^ (row & KSW);
         const int cv = cslot ^ vswz(row);
-        cgk[jj] = (uint32_t)(((row * Hkv + g) * D + ck * 8) * ELT);
-        cgv[jj] = (uint32_t)(((row * Hkv + g) * D + cv * 8) * ELT);
+        const uint32_t imm = batched ? 1024u * jj : 0u;
+        cgk[jj] = (uint32_t)(((row * Hkv + g) * D + ck * 8) * ELT) - imm;
+        cgv[jj] = (uint32_t)(((row * Hkv + g) * D + cv * 8) * ELT) - imm;
         my_copies += (copier && ig < IPG) ? 2 : 0;
     }
+    auto cg_at = [&](const uint32_t (&cg)[IPG], int jj) -> uint32_t { return cg[jj] + (batched ? 1024u * jj : 0u); };
 
     // Source of this wave's 16-key group of the tile at k0 (wave-uniform).  A group with no
     // live key takes the rows of the tile's first live group instead, so no block-table entry
@@ -366,16 +406,30 @@ __global__ __launch_bounds__(64 * kPrefillWaves, kPrefillWavesPerSimd) void pref
         int j0;          // first key of the group copied
         bool mixed;
     };
-    auto group_src = [&](int k0) -> GroupSrc {
-        GroupSrc r;
+    // the group's first key and its block-table entry (looked up apart from forming the
+    // addresses, so that the lookup can be issued early)
+    struct GroupKey {
+        int j0;
+        int blk;
+        bool mixed;
+    };
+    auto group_key = [&](int k0) -> GroupKey {
+        GroupKey r;
         const int j0 = k0 + 16 * cga;
         const bool live = (j0 <= wg_hi) && (j0 + 15 >= wg_lo);
         r.j0 = live ? j0 : (max(k0, wg_lo) & ~15);
         r.mixed = fused && r.j0 + 15 >= off && (r.j0 < off || r.j0 + 15 > sk - 1);
+        r.blk = (!fused || r.j0 < off) ? table[r.j0 >> shift] : 0;
+        return r;
+    };
+    auto group_src_of = [&](const GroupKey& gk) -> GroupSrc {
+        GroupSrc r;
+        r.j0 = gk.j0;
+        r.mixed = gk.mixed;
         r.gb = 0;
         if (!fused || r.j0 < off) {
-            const int blk = table[r.j0 >> shift];
-            r.gb = ((int64_t)blk * BS + (r.j0 & (BS - 1))) * RB;
+            // the token's index in the cache fits 32 bits (below num_blocks * block_size)
+            r.gb = (int64_t)((uint64_t)(uint32_t)(gk.blk * BS + (r.j0 & (BS - 1))) * (uint32_t)RB);
             r.k = kplane + r.gb;
             r.v = kplane + vdelta + r.gb;
         } else {
@@ -385,6 +439,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves, kPrefillWavesPerSimd) void pref
         }
         return r;
     };
+    auto group_src = [&](int k0) -> GroupSrc { return group_src_of(group_key(k0)); };
     // FP8: the codes of the tile in flight, staged until land() widens them into LDS
     u32x2 stg_k[IPG], stg_v[IPG];
     // copy this wave's share of one plane of a tile into LDS buffer dst
@@ -395,17 +450,23 @@ __global__ __launch_bounds__(64 * kPrefillWaves, kPrefillWavesPerSimd) void pref
 #pragma unroll
             for (int jj = 0; jj < IPG; ++jj) {
                 const int ig = csub + nsub * jj;
-                if (ig < IPG) (vplane_ ? stg_v : stg_k)[jj] = *(const u32x2*)(src + cg[jj]);
+                if (ig < IPG) (vplane_ ? stg_v : stg_k)[jj] = *(const u32x2*)(src + cg_at(cg, jj));
             }
             return;
         }
         const uint32_t lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)dst;
         if (!gs.mixed) {
             const char* src = vplane_ ? gs.v : gs.k;
+            if constexpr (batched && IPG == 4) {
+                copy4_to_lds16<1024>(src, cg, lds + 1024u * (uint32_t)(IPG * cga));
+            } else if constexpr (batched && IPG == 2) {
+                copy2_to_lds16<1024>(src, cg, lds + 1024u * (uint32_t)(IPG * cga));
+            } else {
 #pragma unroll
-            for (int jj = 0; jj < IPG; ++jj) {
-                const int ig = csub + nsub * jj;
-                if (ig < IPG) copy_to_lds16(src, cg[jj], lds + 1024u * (uint32_t)(IPG * cga + ig));
+                for (int jj = 0; jj < IPG; ++jj) {
+                    const int ig = csub + nsub * jj;
+                    if (ig < IPG) copy_to_lds16(src, cg[jj], lds + 1024u * (uint32_t)(IPG * cga + ig));
+                }
             }
         } else {
 #pragma unroll
@@ -416,10 +477,10 @@ __global__ __launch_bounds__(64 * kPrefillWaves, kPrefillWavesPerSimd) void pref
                     const int key = gs.j0 + row;
                     const char* p;
                     if (key < off) {
-                        p = kplane + (vplane_ ? vdelta : 0) + gs.gb + cg[jj];
+                        p = kplane + (vplane_ ? vdelta : 0) + gs.gb + cg_at(cg, jj);
                     } else {
                         const int64_t rn = (int64_t)q0 + min(key, sk - 1) - off;
-                        p = (vplane_ ? vnew : knew) + rn * RB + (cg[jj] - (uint32_t)row * (uint32_t)RB);
+                        p = (vplane_ ? vnew : knew) + rn * RB + (cg_at(cg, jj) - (uint32_t)row * (uint32_t)RB);
                     }
                     copy_to_lds16_lane(p, lds + 1024u * (uint32_t)(IPG * cga + ig));
                 }
@@ -766,6 +827,10 @@ __global__ __launch_bounds__(64 * kPrefillWaves, kPrefillWavesPerSimd) void pref
         char* kc = kbuf(J);
         char* vc = vbuf(J);
         const int k0 = kt * BN;
+        // the group this step copies (tile kt + NBUF - 1; tile kt's own when there is none, a
+        // lookup already made), its block-table entry loaded before the waits below
+        const bool has_next = kt + NBUF - 1 < kt_end;
+        const GroupKey gk = group_key((has_next ? kt + NBUF - 1 : kt) * BN);
         // this wave's copies of tile kt have landed once at most those of the tiles after
         // it (up to NBUF - 2 of them) are still in flight
         if constexpr (FP8) {
@@ -780,9 +845,9 @@ __global__ __launch_bounds__(64 * kPrefillWaves, kPrefillWavesPerSimd) void pref
         }
         // all copies of tile kt visible; buffer jn (tile kt - 1) is free.  Not a fenced
         // barrier: that would also wait for the copies of the later tiles
-        lds_barrier();
-        if (kt + NBUF - 1 < kt_end) {
-            const GroupSrc gs = group_src(k0 + (NBUF - 1) * BN);
+        lds_barrier_after(gk.blk);
+        if (has_next) {
+            const GroupSrc gs = group_src_of(gk);
             issue(gs, false, cgk, kbuf(std::integral_constant<int, jn>{}));
             issue(gs, true, cgv, vbuf(std::integral_constant<int, jn>{}));
         }
