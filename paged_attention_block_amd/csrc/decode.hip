@@ -169,37 +169,41 @@ __device__ __forceinline__ void load_step_new(int k0, int kb, int ke, const int3
     }
 }
 
-// FP8 step registers widened to the bf16 layout the MFMAs take.
-template <int D>
-__device__ __forceinline__ void widen_step(const u32x2 (&k8)[2][D / 32], const typename VRow8<D>::T (&v8)[8],
-                                           u32x4 (&kr)[2][D / 32], typename VRow<D>::T (&vr)[8]) {
-#pragma unroll
-    for (int ga = 0; ga < 2; ++ga)
-#pragma unroll
-        for (int t = 0; t < D / 32; ++t)
-            kr[ga][t] = u32x4{e4m3x2_lo(k8[ga][t][0]), e4m3x2_hi(k8[ga][t][0]), e4m3x2_lo(k8[ga][t][1]),
-                              e4m3x2_hi(k8[ga][t][1])};
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        if constexpr (D == 128)
-            vr[j] = u32x4{e4m3x2_lo(v8[j][0]), e4m3x2_hi(v8[j][0]), e4m3x2_lo(v8[j][1]), e4m3x2_hi(v8[j][1])};
-        else
-            vr[j] = u32x2{e4m3x2_lo(v8[j]), e4m3x2_hi(v8[j])};
+// An FP8 step's registers are widened to the bf16 operands of its MFMAs as they are used
+// (every E4M3 value is a bf16 value, so the widening is exact): a K operand right before its
+// S^T MFMA, a V word right before the byte permutes that take it, so no widened copy of the
+// whole step is live at once.
+template <int D, bool FP8>
+__device__ __forceinline__ bf16x8 k_operand(const typename StepT<D, FP8>::K& x) {
+    if constexpr (FP8)
+        return __builtin_bit_cast(bf16x8, u32x4{e4m3x2_lo(x[0]), e4m3x2_hi(x[0]), e4m3x2_lo(x[1]), e4m3x2_hi(x[1])});
+    else
+        return __builtin_bit_cast(bf16x8, x);
+}
+// 32-bit word w (two bf16 dims) of a V row as the PV operand takes it
+template <int D, bool FP8>
+__device__ __forceinline__ uint32_t v_word(const typename StepT<D, FP8>::V& x, int w) {
+    if constexpr (!FP8) {
+        return x[w];
+    } else if constexpr (D == 128) {
+        return (w & 1) ? e4m3x2_hi(x[w >> 1]) : e4m3x2_lo(x[w >> 1]);
+    } else {
+        return (w & 1) ? e4m3x2_hi(x) : e4m3x2_lo(x);
     }
 }
 
 // Online-softmax update of one 32-key step (scores by MFMA, P packed to bf16, PV by MFMA).
 // With ALiBi, sl2 = this lane's head slope in log2 units and pos the query's position: the
 // score of key j gets sl2 * (j - pos) added after the scale.
-template <int D, bool ALIBI>
-__device__ __forceinline__ void compute_core(int k0, int kb, int ke, int grp, float c_log2,
-                                             float sl2, int pos,
-                                             const bf16x8 (&qf)[D / 32], u32x4 (&kr)[2][D / 32],
-                                             typename VRow<D>::T (&vr)[8], f32x4 (&oacc)[D / 16],
-                                             float& m_run, float& l_run) {
+template <int D, bool ALIBI, bool FP8>
+__device__ __forceinline__ void compute_step(int k0, int kb, int ke, int grp, float c_log2, float sl2, int pos,
+                                             const bf16x8 (&qf)[D / 32],
+                                             typename StepT<D, FP8>::K (&kr)[2][D / 32],
+                                             typename StepT<D, FP8>::V (&vr)[8],
+                                             f32x4 (&oacc)[D / 16], float& m_run, float& l_run) {
     constexpr int KS = D / 32;
     constexpr int DPL = D / 16;
-    typedef typename VRow<D>::T VT;
+    typedef typename StepT<D, FP8>::V VT;
     const bool edge = (k0 < kb) || (k0 + 32 > ke);
     f32x4 sacc[2];
 #pragma unroll
@@ -207,8 +211,7 @@ __device__ __forceinline__ void compute_core(int k0, int kb, int ke, int grp, fl
         sacc[ga] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int t = 0; t < KS; ++t)
-            sacc[ga] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[ga][t]),
-                                                               qf[t], sacc[ga], 0, 0, 0);
+            sacc[ga] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand<D, FP8>(kr[ga][t]), qf[t], sacc[ga], 0, 0, 0);
     }
     float sc[8];
 #pragma unroll
@@ -257,29 +260,12 @@ __device__ __forceinline__ void compute_core(int k0, int kb, int ke, int grp, fl
     for (int t = 0; t < DPL; ++t) {
         const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
         u32x4 w;
-        w[0] = __builtin_amdgcn_perm(vr[1][t >> 1], vr[0][t >> 1], sel);
-        w[1] = __builtin_amdgcn_perm(vr[3][t >> 1], vr[2][t >> 1], sel);
-        w[2] = __builtin_amdgcn_perm(vr[5][t >> 1], vr[4][t >> 1], sel);
-        w[3] = __builtin_amdgcn_perm(vr[7][t >> 1], vr[6][t >> 1], sel);
+        w[0] = __builtin_amdgcn_perm(v_word<D, FP8>(vr[1], t >> 1), v_word<D, FP8>(vr[0], t >> 1), sel);
+        w[1] = __builtin_amdgcn_perm(v_word<D, FP8>(vr[3], t >> 1), v_word<D, FP8>(vr[2], t >> 1), sel);
+        w[2] = __builtin_amdgcn_perm(v_word<D, FP8>(vr[5], t >> 1), v_word<D, FP8>(vr[4], t >> 1), sel);
+        w[3] = __builtin_amdgcn_perm(v_word<D, FP8>(vr[7], t >> 1), v_word<D, FP8>(vr[6], t >> 1), sel);
         oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w), pb, oacc[t],
                                                           0, 0, 0);
-    }
-}
-
-// One 32-key step from its loaded registers (FP8 rows widened first).
-template <int D, bool ALIBI, bool FP8>
-__device__ __forceinline__ void compute_step(int k0, int kb, int ke, int grp, float c_log2, float sl2, int pos,
-                                             const bf16x8 (&qf)[D / 32],
-                                             typename StepT<D, FP8>::K (&kr)[2][D / 32],
-                                             typename StepT<D, FP8>::V (&vr)[8],
-                                             f32x4 (&oacc)[D / 16], float& m_run, float& l_run) {
-    if constexpr (FP8) {
-        u32x4 kw[2][D / 32];
-        typename VRow<D>::T vw[8];
-        widen_step<D>(kr, vr, kw, vw);
-        compute_core<D, ALIBI>(k0, kb, ke, grp, c_log2, sl2, pos, qf, kw, vw, oacc, m_run, l_run);
-    } else {
-        compute_core<D, ALIBI>(k0, kb, ke, grp, c_log2, sl2, pos, qf, kr, vr, oacc, m_run, l_run);
     }
 }
 
@@ -366,6 +352,9 @@ __device__ __forceinline__ void fold_prefix(const DecodeArgs& a, int s, int head
 // CASCADE: shared-prefix decode.  Every sequence's steps then start at key_start, the first
 // piece of a sequence folds the prefix's state into its own, and a sequence with no own key
 // writes the prefix's result.
+// 32-key steps per register set of an FP8 decode (1: as bf16; 2: the bytes of one bf16 step)
+constexpr int kDecodeFp8StepsPerSet = 1;
+
 template <int D, bool ALIBI, bool CASCADE, bool FP8, bool FUSED>
 __global__ __launch_bounds__(512) void decode_bf16_kernel(const DecodeArgs a) {
     static_assert(!FUSED || (!FP8 && !CASCADE), "the fused store serves the plain bf16 decode");
@@ -491,8 +480,13 @@ __global__ __launch_bounds__(512) void decode_bf16_kernel(const DecodeArgs a) {
             // of the step's whole rows missed the L2 often enough to add ~4% to the traffic).  A workgroup barrier per two steps keeps the 8 waves, which
             // read adjacent 256-byte pieces of the same 2 KB token rows, close together in
             // the key walk (measured: 3% more bandwidth than free-running waves).
-            typename StepT<D, FP8>::K kA[2][KS], kB[2][KS];
-            typename StepT<D, FP8>::V vA[8], vB[8];
+            // An FP8 register set holds SPS = 2 consecutive steps (the bytes of one bf16 step), so
+            // a wave keeps as many bytes in flight with either cache; a step of a set past the
+            // segment's end is loaded as a dummy and not computed.
+            constexpr int SPS = FP8 ? kDecodeFp8StepsPerSet : 1;
+            constexpr int SK = 32 * SPS;
+            typename StepT<D, FP8>::K kA[SPS][2][KS], kB[SPS][2][KS];
+            typename StepT<D, FP8>::V vA[SPS][8], vB[SPS][8];
             int k0 = step_begin;
             auto ld = [&](int k, auto& kr, auto& vr, bool dummy) {
                 if constexpr (FUSED) {
@@ -505,18 +499,33 @@ __global__ __launch_bounds__(512) void decode_bf16_kernel(const DecodeArgs a) {
                 load_step<D, FP8>(k, kb, ke, table, shift, BS, row_elems, g, kplane, vplane, dummy ? 0u : k_off,
                                   dummy ? 0u : v_off, row_bytes, kr, vr);
             };
-            ld(k0, kA, vA, false);
+            // the SPS steps of the set at k (k < ke), or dummies at k
+            auto ld_set = [&](int k, auto& kr, auto& vr, bool dummy) {
+#pragma unroll
+                for (int u = 0; u < SPS; ++u) {
+                    const bool past = dummy || k + 32 * u >= ke;
+                    ld(past ? k : k + 32 * u, kr[u], vr[u], past);
+                }
+            };
+            auto compute_set = [&](int k, auto& kr, auto& vr) {
+#pragma unroll
+                for (int u = 0; u < SPS; ++u)
+                    if (u == 0 || k + 32 * u < ke)
+                        compute_step<D, ALIBI, FP8>(k + 32 * u, kb, ke, grp, c_log2, sl2, n - 1, qf, kr[u], vr[u], oacc,
+                                                    m_run, l_run);
+            };
+            ld_set(k0, kA, vA, false);
             while (true) {
                 __syncthreads();
-                const bool more1 = k0 + 32 < ke;
-                ld(more1 ? k0 + 32 : k0, kB, vB, !more1);
-                compute_step<D, ALIBI, FP8>(k0, kb, ke, grp, c_log2, sl2, n - 1, qf, kA, vA, oacc, m_run, l_run);
-                k0 += 32;
+                const bool more1 = k0 + SK < ke;
+                ld_set(more1 ? k0 + SK : k0, kB, vB, !more1);
+                compute_set(k0, kA, vA);
+                k0 += SK;
                 if (k0 >= ke) break;
-                const bool more2 = k0 + 32 < ke;
-                ld(more2 ? k0 + 32 : k0, kA, vA, !more2);
-                compute_step<D, ALIBI, FP8>(k0, kb, ke, grp, c_log2, sl2, n - 1, qf, kB, vB, oacc, m_run, l_run);
-                k0 += 32;
+                const bool more2 = k0 + SK < ke;
+                ld_set(more2 ? k0 + SK : k0, kA, vA, !more2);
+                compute_set(k0, kB, vB);
+                k0 += SK;
                 if (k0 >= ke) break;
             }
 
