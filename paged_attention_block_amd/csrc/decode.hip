@@ -349,12 +349,13 @@ __device__ __forceinline__ void fold_prefix(const DecodeArgs& a, int s, int head
     l_run = l;
 }
 
+// 32-key steps per register set of an FP8 decode (1: as bf16; 2: the bytes of one bf16 step,
+// measured slower)
+constexpr int kDecodeFp8StepsPerSet = 1;
+
 // CASCADE: shared-prefix decode.  Every sequence's steps then start at key_start, the first
 // piece of a sequence folds the prefix's state into its own, and a sequence with no own key
 // writes the prefix's result.
-// 32-key steps per register set of an FP8 decode (1: as bf16; 2: the bytes of one bf16 step)
-constexpr int kDecodeFp8StepsPerSet = 1;
-
 template <int D, bool ALIBI, bool CASCADE, bool FP8, bool FUSED>
 __global__ __launch_bounds__(512) void decode_bf16_kernel(const DecodeArgs a) {
     static_assert(!FUSED || (!FP8 && !CASCADE), "the fused store serves the plain bf16 decode");
@@ -477,12 +478,13 @@ __global__ __launch_bounds__(512) void decode_bf16_kernel(const DecodeArgs a) {
             // The prefetch is unconditional so that every iteration issues the same number of
             // loads and the waits stay exact: after the last step it is a dummy in which every
             // lane reads the same few 16-byte pieces of rows the step already read (a re-read
-            // of the step's whole rows missed the L2 often enough to add ~4% to the traffic).  A workgroup barrier per two steps keeps the 8 waves, which
-            // read adjacent 256-byte pieces of the same 2 KB token rows, close together in
-            // the key walk (measured: 3% more bandwidth than free-running waves).
-            // An FP8 register set holds SPS = 2 consecutive steps (the bytes of one bf16 step), so
-            // a wave keeps as many bytes in flight with either cache; a step of a set past the
-            // segment's end is loaded as a dummy and not computed.
+            // of the step's whole rows missed the L2 often enough to add ~4% to the traffic).  A
+            // workgroup barrier per two steps keeps the 8 waves, which read adjacent 256-byte
+            // pieces of the same 2 KB token rows, close together in the key walk (measured: 3%
+            // more bandwidth than free-running waves).
+            // A register set holds SPS consecutive steps (an FP8 set may hold two, the bytes of one
+            // bf16 step); a step of a set past the segment's end is loaded as a dummy and not
+            // computed.
             constexpr int SPS = FP8 ? kDecodeFp8StepsPerSet : 1;
             constexpr int SK = 32 * SPS;
             typename StepT<D, FP8>::K kA[SPS][2][KS], kB[SPS][2][KS];
