@@ -178,6 +178,9 @@ DECODE_CASES = {
     "g16_d128": (16, 1, 128, 32, 0, torch.bfloat16, [3, 70, 400]),
     "g1_d64": (4, 4, 64, 16, 7, torch.bfloat16, [1, 6, 7, 8, 200]),
     "f32_d64": (4, 2, 64, 16, 0, torch.float32, [0, 5, 17, 40]),
+    # more than 8 KV heads: several head groups per chunk (the second one of 12 half idle)
+    "g2_d64_hkv12": (24, 12, 64, 16, 0, torch.bfloat16, [5, 64, 300]),
+    "g1_d128_hkv32": (32, 32, 128, 16, 0, torch.bfloat16, [0, 33, 200, 700]),
 }
 
 

@@ -62,7 +62,7 @@ def draw_case(seed: int) -> dict:
     else:
         top = 20000 if rng.random() < 0.15 else 2500  # a few long contexts: many chunks per sequence
         seqs = [(int(rng.integers(0, top)), 1) for _ in range(B)]
-    return {
+    c = {
         "seed": seed, "dtype": dtype, "fp8": fp8_cache, "D": D, "Hkv": Hkv, "H": Hkv * G, "BS": BS,
         "window": window, "kind": kind, "seqs": seqs,
         "alibi": bool(rng.random() < 0.3),
@@ -70,6 +70,18 @@ def draw_case(seed: int) -> dict:
         "kv_scale": float(rng.choice([1.0, 0.5, 2.0, 0.3])) if fp8_cache else 1.0,
         "part": int(rng.choice([0, 0, 32, 64, 256])) if kind == "decode" else 0,
     }
+    _widen_heads(rng, c, G)
+    return c
+
+
+def _widen_heads(rng, c, G):
+    """Now and then more than 8 KV heads (the decode kernel then runs several head groups per
+    chunk, the last one partly idle); drawn after everything else, so the rest of a case is the
+    same as without this draw."""
+    if rng.random() < 0.12:
+        wide = int(rng.choice([12, 16]))
+        if wide * G <= 64:
+            c["Hkv"], c["H"] = wide, wide * G
 
 
 def test_sweep_draws_cover_the_options():
@@ -78,6 +90,7 @@ def test_sweep_draws_cover_the_options():
         assert any(c[key] for c in cases) and not all(c[key] for c in cases), key
     assert {c["kind"] for c in cases} == {"prefill", "decode"}
     assert any(c["window"] for c in cases)
+    assert any(c["Hkv"] > 8 and c["kind"] == "decode" for c in cases)
     assert any(c["dtype"] == torch.float32 for c in cases)
     assert len({c["H"] // c["Hkv"] for c in cases}) >= 5
     assert len({c["BS"] for c in cases}) >= 5
@@ -149,10 +162,12 @@ def draw_cascade(seed: int) -> dict:
     big = bool(rng.random() < 0.35)
     B = -(-512 // G) + int(rng.integers(0, 24)) if big else int(rng.integers(1, 12))
     own = [0 if rng.random() < 0.15 else int(rng.integers(1, 300 if big else 1500)) for _ in range(B)]
-    return {"seed": seed, "fp8": fp8_cache, "D": D, "Hkv": Hkv, "H": Hkv * G, "BS": BS, "prefix": prefix,
-            "ctx": [prefix + o for o in own],
-            "kv_scale": float(rng.choice([1.0, 0.5, 2.0])) if fp8_cache else 1.0,
-            "part": int(rng.choice([0, 0, 64, 256]))}
+    c = {"seed": seed, "fp8": fp8_cache, "D": D, "Hkv": Hkv, "H": Hkv * G, "BS": BS, "prefix": prefix,
+         "ctx": [prefix + o for o in own],
+         "kv_scale": float(rng.choice([1.0, 0.5, 2.0])) if fp8_cache else 1.0,
+         "part": int(rng.choice([0, 0, 64, 256]))}
+    _widen_heads(rng, c, G)
+    return c
 
 
 def test_cascade_draws_reach_both_prefix_passes():
