@@ -127,7 +127,7 @@ int pa_copy_blocks(const pa_cache_desc* cache, const int32_t* block_pairs, int32
  *                 key range are never read and may be -1)
  *   cu_seqlens_q, cu_seqlens_k  [num_seqs + 1] int32, non-decreasing, starting at 0
  *   max_seqlen_q  >= every seqlen_q (sizes the grid); max_seqlen_k >= every seqlen_k
- *   scale         final multiplier of q.K^T (e.g. 1/sqrt(head_size)), >= 0
+ *   scale         final multiplier of q.K^T (e.g. 1/sqrt(head_size)), finite and > 0
  *   alibi_slopes  NULL, or [num_heads] float32 ALiBi slopes: the score of query head h at
  *                 position p for key j gets alibi_slopes[h] * (j - p) added after the scale
  *                 (vllm-npu 0.4.2 diff, torch_sdpa.py / xformers.py, _make_alibi_bias)

@@ -271,7 +271,10 @@ static int prefill_args(const pa_cache_desc* cache, void* out, const void* query
     if (max_blocks_per_seq < 1) return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq must be >= 1");
     if ((int64_t)max_seqlen_k > (int64_t)max_blocks_per_seq * a.c.block_size)
         return fail(PA_ERR_INVALID_ARG, "max_seqlen_k %d exceeds max_blocks_per_seq * block_size", max_seqlen_k);
-    if (!(scale >= 0.f)) return fail(PA_ERR_INVALID_ARG, "scale must be >= 0 (got %g)", (double)scale);
+    // > 0 and finite: the kernels fold the scale into the exponent, where a masked score (-inf)
+    // times a zero or infinite scale would give NaN instead of a zero weight
+    if (!(scale > 0.f && scale <= 3.4e38f))
+        return fail(PA_ERR_INVALID_ARG, "scale must be finite and > 0 (got %g)", (double)scale);
     if (a.c.dtype == PA_F32 && (int64_t)num_seqs * max_seqlen_q >= (int64_t(1) << 31))
         return fail(PA_ERR_INVALID_ARG, "num_seqs * max_seqlen_q too large");
     if ((int64_t)num_seqs * num_heads * ((max_seqlen_q + 31) / 32) >= (int64_t(1) << 30))
@@ -398,7 +401,10 @@ static int decode_args(const pa_cache_desc* cache, void* out, const void* query,
         return fail(PA_ERR_INVALID_ARG, "max_seq_len %d exceeds max_blocks_per_seq * block_size", max_seq_len);
     if (partition_size < 0 || partition_size % 32 != 0)
         return fail(PA_ERR_INVALID_ARG, "partition_size must be 0 or a positive multiple of 32 (got %d)", partition_size);
-    if (!(scale >= 0.f)) return fail(PA_ERR_INVALID_ARG, "scale must be >= 0 (got %g)", (double)scale);
+    // > 0 and finite: the kernels fold the scale into the exponent, where a masked score (-inf)
+    // times a zero or infinite scale would give NaN instead of a zero weight
+    if (!(scale > 0.f && scale <= 3.4e38f))
+        return fail(PA_ERR_INVALID_ARG, "scale must be finite and > 0 (got %g)", (double)scale);
     const int32_t win = sliding_window > 0 ? sliding_window : 0;
     if ((int64_t)num_seqs * ((max_keys_of(max_seq_len, win, key_start) + 31) / 32 + 1) > 0x7fffffff)
         return fail(PA_ERR_INVALID_ARG, "num_seqs * max_seq_len too large");

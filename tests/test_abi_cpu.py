@@ -92,8 +92,9 @@ def test_prefill_argument_checks(lib):
     assert call(out=None) == 1
     assert call(mb=0) == 1
     assert call(msk=65) == 1 and b"max_blocks_per_seq" in lib.pa_last_error()
-    assert call(scale=float("nan")) == 1
-    assert call(scale=-0.5) == 1 and b"scale" in lib.pa_last_error()   # the kernels assume scale >= 0
+    # the kernels need a finite scale > 0 (a masked score times a zero or infinite scale is NaN)
+    for bad in (float("nan"), -0.5, 0.0, float("inf")):
+        assert call(scale=bad) == 1 and b"scale" in lib.pa_last_error(), bad
     assert call(d=desc(bs=8)) == 2                                      # bf16 needs block_size >= 16
     assert call(b=-1) == 1
 
@@ -108,6 +109,9 @@ def test_decode_argument_and_workspace_checks(lib):
     assert lib.pa_decode(d, FAKE, FAKE, FAKE, 300, FAKE, 64, 4097, 32, 0.1, 0, None, 128, FAKE, need - 1, None) == 3
     assert lib.pa_decode(d, FAKE, FAKE, FAKE, 300, FAKE, 64, 4097, 32, 0.1, 0, None, 128, None, need, None) == 3
     assert lib.pa_decode(d, FAKE, FAKE, FAKE, 300, FAKE, 64, 4097, 32, 0.1, 0, None, 48, FAKE, need, None) == 1
+    for bad in (0.0, -1.0, float("inf"), float("nan")):
+        assert lib.pa_decode(d, FAKE, FAKE, FAKE, 300, FAKE, 64, 4097, 32, bad, 0, None, 128, FAKE, need, None) == 1
+        assert b"scale" in lib.pa_last_error()
     assert lib.pa_decode(d, FAKE, FAKE, FAKE, 300, FAKE, 64, 4097, 32, 0.1, 0, None, -32, FAKE, need, None) == 1
     assert lib.pa_decode(d, FAKE, FAKE, FAKE, 200, FAKE, 64, 4097, 32, 0.1, 0, None, 128, FAKE, need, None) == 1
     assert lib.pa_decode(d, None, FAKE, FAKE, 300, FAKE, 64, 4097, 32, 0.1, 0, None, 128, FAKE, need, None) == 1
