@@ -289,6 +289,9 @@ __global__ __launch_bounds__(64 * kPrefillWaves, kPrefillWavesPerSimd) void pref
     // ALiBi slope of this wave's head in log2 units (the bias slope * (j - p) is added to the
     // scaled score before the softmax)
     const float sl2 = ALIBI && wave_ok ? a.alibi[h] * 1.4426950408889634f : 0.f;
+    // the same slope in raw-score units (the scale is > 0): the 32x32x16 form seeds the S^T
+    // accumulators with the bias, so the softmax needs no separate bias pass
+    const float sl2r = ALIBI ? sl2 / c_log2 : 0.f;
     const int BS = a.c.block_size;
     const int shift = a.c.block_shift;
     const char* __restrict__ kplane = (const char*)a.c.kv;
@@ -652,9 +655,18 @@ __global__ __launch_bounds__(64 * kPrefillWaves, kPrefillWavesPerSimd) void pref
     uint32_t kw[D / 16];
 #pragma unroll
     for (int t = 0; t < D / 16; ++t) kw[t] = (uint32_t)(lrow * D * 2 + (((2 * t + lh) ^ (lrow & KSW)) * 16));
-    auto qk_w = [&](const char* kt, f32x16 (&sw)[NB32]) {
+    auto qk_w = [&](const char* kt, f32x16 (&sw)[NB32], int k0) {
+        if constexpr (ALIBI) {
+            // bias of key k0 + 32b + 8(i/4) + 4(l/32) + i%4 for this lane's row, over the scale
+            const float base = sl2r * (float)(k0 + 4 * lh - prw);
 #pragma unroll
-        for (int b = 0; b < NB32; ++b) sw[b] = (f32x16)(0.f);
+            for (int b = 0; b < NB32; ++b)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) sw[b][i] = fmaf(sl2r, (float)(32 * b + 8 * (i >> 2) + (i & 3)), base);
+        } else {
+#pragma unroll
+            for (int b = 0; b < NB32; ++b) sw[b] = (f32x16)(0.f);
+        }
 #pragma unroll
         for (int t = 0; t < D / 16; ++t)
 #pragma unroll
@@ -686,16 +698,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves, kPrefillWavesPerSimd) void pref
                     sw[b][i] = (key > prw || key < plw) ? -INFINITY : sw[b][i];
                 }
         }
-        float cs = c_log2;
-        if constexpr (ALIBI) {
-            const float base = sl2 * (float)(k0 + 4 * lh - prw);
-#pragma unroll
-            for (int b = 0; b < NB32; ++b)
-#pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    sw[b][i] = fmaf(sw[b][i], c_log2, fmaf(sl2, (float)(32 * b + 8 * (i >> 2) + (i & 3)), base));
-            cs = 1.f;
-        }
+        const float cs = c_log2;  // (ALiBi: the bias is already in the accumulators)
         float mx = fmaxf(sw[0][0], sw[0][1]);
 #pragma unroll
         for (int x = 2; x < 16 * NB32; x += 2) mx = fmaxf(fmaxf(mx, sw[x >> 4][x & 15]), sw[x >> 4][(x & 15) + 1]);
@@ -859,7 +862,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves, kPrefillWavesPerSimd) void pref
                     f32x16 sw[NB32];
                     u32x4 pw[NB32][2];
                     float alpha;
-                    qk_w(kc + hb * CB * D * 2, sw);
+                    qk_w(kc + hb * CB * D * 2, sw, k0 + hb * CB);
                     softmax_w(k0 + hb * CB, sw, pw, alpha, inner);
                     pv_w(vc + hb * CB * D * 2, pw, alpha);
                 }
