@@ -9,6 +9,10 @@
  *   pa_prefill_varlen_with_store, pa_decode_with_store
  *                      the store of the new tokens and the attention in one call
  *   pa_cascade_decode  decode of a batch that shares a prefix of cached blocks
+ *   pa_cascade_prefill_varlen
+ *                      prefill of query chunks that share a prefix of cached blocks
+ *   pa_decode_no_alloc pa_decode with its scratch in the library (no workspace argument)
+ *   pa_*_workspace_size, pa_status_string, pa_last_error
  * Options: ALiBi slopes (alibi_slopes arguments) and an FP8 (E4M3) cache with a kv_scale
  * (pa_cache_desc.dtype / kv_scale).
  *
