@@ -83,6 +83,14 @@ __device__ inline void lane_offsets(int col, int grp, uint32_t row_bytes, uint32
 template <bool FP8>
 __device__ inline int q_slice(int t, int grp) { return FP8 ? 8 * (t >> 1) + 2 * grp + (t & 1) : 4 * t + grp; }
 
+// Block-table rows are read through the constant address space.  The table is never written
+// during a call, but the compiler cannot prove that of a plain pointer once the kernel stores
+// its outputs, and then reads it with vector loads: a step's table lookup then waits for every
+// load in flight (the wait counts are in order), including the other register set's, which
+// leaves one step loading at a time.  Read as constant memory, the lookups are scalar loads,
+// counted apart from the vector loads.
+typedef const __attribute__((address_space(4))) int32_t* const_table_t;
+
 // Loads of the 32-key step at k0 into registers: K rows (2 groups of 16 keys x KS slices,
 // MFMA A-operand layout) and the V rows one lane needs for the PV MFMAs (8 keys x DPL
 // dims).  Both 16-key groups of a step lie in one physical block each (block_size >= 16,
@@ -90,7 +98,7 @@ __device__ inline int q_slice(int t, int grp) { return FP8 ? 8 * (t >> 1) + 2 * 
 // group's rows instead, so every load is in bounds and unconditional.  Keys outside
 // [kb, ke) are masked after the load.
 template <int D, bool FP8>
-__device__ __forceinline__ void load_step(int k0, int kb, int ke, const int32_t* __restrict__ table,
+__device__ __forceinline__ void load_step(int k0, int kb, int ke, const_table_t table,
                                           int shift, int BS, int64_t row_elems, int g,
                                           const char* __restrict__ kplane,
                                           const char* __restrict__ vplane, uint32_t k_off,
@@ -136,7 +144,7 @@ __device__ __forceinline__ void load_step(int k0, int kb, int ke, const int32_t*
 // lanes whose K or V row is that key read it from the caller's row (knew_row / vnew_row: KV head
 // g's D elements) instead of the cache slot, which the store has not written yet.  bf16 only.
 template <int D>
-__device__ __forceinline__ void load_step_new(int k0, int kb, int ke, const int32_t* __restrict__ table,
+__device__ __forceinline__ void load_step_new(int k0, int kb, int ke, const_table_t table,
                                               int shift, int BS, int64_t row_elems, int g,
                                               const char* __restrict__ kplane,
                                               const char* __restrict__ vplane, uint32_t k_off,
@@ -450,7 +458,7 @@ __global__ __launch_bounds__(512) void decode_bf16_kernel(const DecodeArgs a) {
             const int step_begin = base + 32 * ls;             // multiple of 32
             const int kb = step_begin > lo ? step_begin : lo;  // first live key of the segment
             const int ke = min(n, base + 32 * le);             // one past the last
-            const int32_t* __restrict__ table = a.table + (int64_t)s * a.max_blocks;
+            const const_table_t table = (const_table_t)(a.table + (int64_t)s * a.max_blocks);
             // fused store: this workgroup holds the sequence's last step (the new token's key)
             const bool new_here = FUSED && le == steps;
             const int k_last = base + 32 * (steps - 1);
@@ -643,15 +651,15 @@ __global__ __launch_bounds__(512) void cascade_prefix_kernel(const DecodeArgs a,
         typename StepT<D, FP8>::K kA[2][KS], kB[2][KS];
             typename StepT<D, FP8>::V vA[8], vB[8];
         int k0 = kb;
-        load_step<D, FP8>(k0, kb, ke, a.table, shift, BS, row_elems, g, kplane, vplane, k_off, v_off, row_bytes, kA, vA);
+        load_step<D, FP8>(k0, kb, ke, (const_table_t)a.table, shift, BS, row_elems, g, kplane, vplane, k_off, v_off, row_bytes, kA, vA);
         while (true) {
             const int n1 = k0 + 32 < ke ? k0 + 32 : k0;
-            load_step<D, FP8>(n1, kb, ke, a.table, shift, BS, row_elems, g, kplane, vplane, k_off, v_off, row_bytes, kB, vB);
+            load_step<D, FP8>(n1, kb, ke, (const_table_t)a.table, shift, BS, row_elems, g, kplane, vplane, k_off, v_off, row_bytes, kB, vB);
             compute_step<D, false, FP8>(k0, kb, ke, grp, c_log2, 0.f, 0, qf, kA, vA, oacc, m_run, l_run);
             k0 += 32;
             if (k0 >= ke) break;
             const int n2 = k0 + 32 < ke ? k0 + 32 : k0;
-            load_step<D, FP8>(n2, kb, ke, a.table, shift, BS, row_elems, g, kplane, vplane, k_off, v_off, row_bytes, kA, vA);
+            load_step<D, FP8>(n2, kb, ke, (const_table_t)a.table, shift, BS, row_elems, g, kplane, vplane, k_off, v_off, row_bytes, kA, vA);
             compute_step<D, false, FP8>(k0, kb, ke, grp, c_log2, 0.f, 0, qf, kB, vB, oacc, m_run, l_run);
             k0 += 32;
             if (k0 >= ke) break;
