@@ -1,4 +1,5 @@
-"""Code-generation checks of the decode partition kernel (CPU only: hipcc cross-compiles).
+"""Code-generation checks of the decode and prefill kernels' inner loops (CPU only: hipcc
+cross-compiles).
 
 The decode kernel keeps two 32-key steps in registers: the next step's K/V loads are meant to
 be in flight while the current step computes.  Vector-memory waits count in issue order, so a
@@ -9,7 +10,9 @@ its outputs): every lookup's use waited for every load in flight, and the decode
 chunked prefill (8 sequences x 4096 keys) ran 7% slower, with every output still correct.  These
 tests compile ``decode.hip`` for gfx950 and check the step loop of the head-size-128 kernels that
 the benchmarks time: no full wait, the block-table lookups are scalar loads, and no single-dword
-vector load (the K/V loads are 8 or 16 bytes wide).
+vector load (the K/V loads are 8 or 16 bytes wide).  The prefill kernel's tile loop reads the block
+table the same way (its full waits are its own, for each wave's tile copies before the barrier):
+there the checks are the scalar lookups and the absence of single-dword vector loads.
 """
 
 import os
@@ -38,16 +41,25 @@ def _hipcc():
         return None
 
 
-@pytest.fixture(scope="module")
-def decode_asm(tmp_path_factory):
+def _device_asm(tmp_path_factory, source):
     cc = _hipcc()
     if cc is None:
         pytest.skip("hipcc not available")
-    out = str(tmp_path_factory.mktemp("asm") / "decode.s")
-    cmd = [cc, *pa_build.FLAGS, "--cuda-device-only", "-S", os.path.join(CSRC, "decode.hip"), "-o", out]
+    out = str(tmp_path_factory.mktemp("asm") / (source + ".s"))
+    cmd = [cc, *pa_build.FLAGS, "--cuda-device-only", "-S", os.path.join(CSRC, source), "-o", out]
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-2000:]
     return open(out).read()
+
+
+@pytest.fixture(scope="module")
+def decode_asm(tmp_path_factory):
+    return _device_asm(tmp_path_factory, "decode.hip")
+
+
+@pytest.fixture(scope="module")
+def prefill_asm(tmp_path_factory):
+    return _device_asm(tmp_path_factory, "prefill.hip")
 
 
 def _functions(asm):
@@ -60,10 +72,10 @@ def _functions(asm):
     return out
 
 
-def _innermost_loops(body):
-    """{header: [instructions]} for the depth-3 loops of a function, from the compiler's loop
-    comments (a header block is marked 'Inner Loop Header: Depth=3', the other blocks of the
-    loop 'in Loop: Header=<header> Depth=3')."""
+def _loops(body, depth):
+    """{header: [instructions]} for the loops of a function at one nesting depth, from the
+    compiler's loop comments (a header block is marked 'Loop Header: Depth=<depth>', the other
+    blocks of the loop 'in Loop: Header=<header> Depth=<depth>')."""
     blocks, cur = [], None
     for line in body.split("\n"):
         m = re.match(r"\.(LBB\d+_\d+):(.*)", line)
@@ -75,9 +87,9 @@ def _innermost_loops(body):
                 cur[1] += line
             elif line.strip():
                 cur[2].append(line.strip())
-    loops = {b[0]: list(b[2]) for b in blocks if "Inner Loop Header: Depth=3" in b[1]}
+    loops = {b[0]: list(b[2]) for b in blocks if f"Loop Header: Depth={depth}" in b[1]}
     for b in blocks:
-        m = re.search(r"in Loop: Header=(BB\d+_\d+) Depth=3", b[1])
+        m = re.search(rf"in Loop: Header=(BB\d+_\d+) Depth={depth}\b", b[1])
         if m and m.group(1) in loops:
             loops[m.group(1)].extend(b[2])
     return loops
@@ -86,7 +98,7 @@ def _innermost_loops(body):
 def _step_loop(asm, symbol):
     fns = _functions(asm)
     assert symbol in fns, f"{symbol} not in the listing"
-    loops = _innermost_loops(fns[symbol])
+    loops = _loops(fns[symbol], 3)
     assert loops, f"no innermost loop found in {symbol}"
     # the step loop is the innermost loop that issues the K/V loads
     return max(loops.values(), key=lambda ins: sum(i.startswith("global_load_dwordx") for i in ins))
@@ -102,3 +114,16 @@ def test_step_loop_keeps_loads_in_flight(decode_asm, kind):
     assert any(i.startswith("s_load_dword") for i in ins), f"{kind}: the block-table lookups are not scalar loads"
     dword = [i for i in ins if re.match(r"global_load_dword\s", i)]
     assert not dword, f"{kind}: single-dword vector loads in the step loop (table lookups?): {dword}"
+
+
+def test_prefill_tile_loop_reads_the_table_with_scalar_loads(prefill_asm):
+    fns = {k: v for k, v in _functions(prefill_asm).items() if "prefill_bf16_kernelILi128" in k}
+    assert fns, "no head-size-128 prefill kernel in the listing"
+    for symbol, body in fns.items():
+        loops = [ins for d in (1, 2, 3) for ins in _loops(body, d).values()]
+        tile = [ins for ins in loops if any(i.startswith("v_mfma") for i in ins)]
+        assert tile, f"{symbol}: no loop with MFMAs"
+        ins = max(tile, key=lambda x: sum(i.startswith("v_mfma") for i in x))
+        assert any(i.startswith("s_load_dword") for i in ins), f"{symbol}: the block-table lookups are not scalar loads"
+        dword = [i for i in ins if re.match(r"global_load_dword\s", i)]
+        assert not dword, f"{symbol}: single-dword vector loads in the tile loop: {dword}"
